@@ -1,0 +1,109 @@
+"""The fp64 oracle against what the pages and the mathematics fix (CPU only)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ce_oracle
+
+from oracle_pins import ALL_PINS, GOLDEN
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(ce_oracle)
+
+
+def test_naive_fp32_collapses_where_the_pages_say():
+    """Negative control for the pages' claim (torchtitan #5661, loss docstring):
+    the naive fp32 loss logsumexp(z) - z_t rounds to exactly 0 past a margin of
+    about 16.6, and the target gradient p_t - 1 with it, while the oracle keeps
+    both nonzero."""
+    with open(os.path.join(GOLDEN, "pages_fp32_collapse_margin.json")) as f:
+        g = json.load(f)
+    def naive(m):
+        # the max-shifted fp32 form: shift by the row max, sum the exps, take
+        # the log; gradient softmax - onehot
+        z = torch.tensor([0.0, m], dtype=torch.float32)
+        shifted = z - z.max()
+        sumexp = torch.exp(shifted).sum()
+        loss = torch.log(sumexp) - shifted[1]
+        grad = torch.exp(shifted) / sumexp
+        grad[1] -= 1.0
+        return float(loss), float(grad[1]), float(grad.sum())
+    lo, hi = naive(g["probe_below"]), naive(g["probe_above"])
+    assert lo[0] > 0 and lo[1] < 0
+    assert hi[0] == 0.0 and hi[1] == 0.0
+    # margin-20 example: naive NLL 0, target grad 0, non-target still ~2e-9
+    with open(os.path.join(GOLDEN, "pages_margin20.json")) as f:
+        m20 = json.load(f)
+    n20 = naive(20.0)
+    assert n20[0] == m20["naive_fp32"]["nll"] and n20[1] == m20["naive_fp32"]["target_grad"]
+    assert abs(n20[2] - m20["naive_fp32"]["nontarget_grad_sum_approx"]) < 0.1e-9
+    for m in (g["probe_above"], 20.0, 40.0):
+        out = ce_oracle(np.array([[0.0, m]]), np.array([1]))
+        assert out["loss"][0] > 0 and out["grad"][0, 1] < 0
+
+
+# Planted mistakes: each mutant of the oracle must fail at least one pin.
+MUTANTS = [
+    ("target kept in the non-target sum",
+     "z_nt[np.arange(rows.size), tl] = _NEG_INF", "pass"),
+    ("softplus argument sign flipped", "x = lse_nt - z_t", "x = z_t - lse_nt"),
+    ("log1p term dropped from lse",
+     "lse = np.maximum(lse_nt, z_t) + np.log1p(np.exp(-np.abs(x)))",
+     "lse = np.maximum(lse_nt, z_t)"),
+    ("z-loss dropped from the loss",
+     "loss[rows] = nll + z_alpha * lse * lse", "loss[rows] = nll"),
+    ("z-loss not squared", "loss[rows] = nll + z_alpha * lse * lse",
+     "loss[rows] = nll + z_alpha * lse"),
+    ("z-loss factor on non-targets halved",
+     "(1.0 + 2.0 * z_alpha * lse)", "(1.0 + z_alpha * lse)"),
+    ("z-loss gradient on the target loses p_t",
+     "-p_nt + 2.0 * z_alpha * lse * p_t", "-p_nt + 2.0 * z_alpha * lse"),
+    ("target gradient sign flipped",
+     "-p_nt + 2.0 * z_alpha * lse * p_t", "p_nt + 2.0 * z_alpha * lse * p_t"),
+    ("target gradient uses p_t instead of -p_nt",
+     "-p_nt + 2.0 * z_alpha * lse * p_t", "-p_t + 2.0 * z_alpha * lse * p_t"),
+    ("gradient not scaled", "sc = scale[rows]", "sc = np.ones(rows.size)"),
+    ("mask array ignored", "valid &= np.asarray(mask).reshape(T) != 0", "pass"),
+    ("segment scale multiplies by the length",
+     "scale = float(grad_scale) / lens[seg].astype(np.float64)",
+     "scale = float(grad_scale) * lens[seg].astype(np.float64)"),
+    ("segment sums take the loss, not the NLL",
+     "np.add.at(seg_nll, seg[valid], nll[valid])", "np.add.at(seg_nll, seg[valid], loss[valid])"),
+    ("segment sums include ignored rows' neighbours (index shifted)",
+     "np.add.at(seg_nll, seg[valid], nll[valid])",
+     "np.add.at(seg_nll, np.roll(seg, 1)[valid], nll[valid])"),
+    ("non-target probability uses the non-target lse",
+     "p = np.exp(z_nt - lse[:, None])", "p = np.exp(z_nt - lse_nt[:, None])"),
+    ("out-of-range targets not poisoned", "loss[bad] = np.nan", "pass"),
+]
+
+
+def _load_mutant(old, new):
+    src_path = os.path.join(os.path.dirname(oracle.__file__), "ce_oracle.py")
+    with open(src_path) as f:
+        src = f.read()
+    assert old in src, f"mutation anchor not found: {old!r}"
+    mod = {}
+    exec(compile(src.replace(old, new, 1), "<mutant>", "exec"), mod)
+    return mod["ce_oracle"]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new):
+    fn = _load_mutant(old, new)
+    failures = []
+    for pin in ALL_PINS:
+        try:
+            pin(fn)
+        except Exception as e:  # AssertionError, or a shape error the mistake causes
+            failures.append((pin.__name__, type(e).__name__))
+    assert failures, f"mutant {name!r} passed every pin"
