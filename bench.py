@@ -1,0 +1,209 @@
+"""Benchmark of the fused vocabulary CE forward + backward on one MI355X.
+
+One step = one ce_fused_fwd_bwd call over one batch of synthetic input (the
+whole hot path: row statistics, per-row loss, gradient, segment sums). Inputs
+are resident in HBM before timing starts. Each step uses the next of
+``--rotate`` input/output buffer sets, so a step never finds its logits in
+the 256 MB last-level cache from the previous use of the same buffers.
+
+Prints ONE JSON line with the metric, the roofline object for the row kernel
+(algorithmic bytes / measured kernel time, against 8 TB/s HBM), and the fp64
+CPU reference timed on a sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "cez_bf16_T8192_V32000_collapse"
+HBM_PEAK_GBPS = 8000.0
+METRIC = "fused CE fwd+bwd logit elems/sec + achieved HBM GB/s (% of peak)"
+
+
+def kernel_source_sha():
+    with open(os.path.join(ROOT, "loss_vocab_amd", "csrc", "ce_fused.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None
+    when none exists or the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, rows, threads):
+    """Time the fp64 oracle on ``rows`` rows of the workload recipe (generated
+    on the host), split in 256-row blocks over a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import ce_oracle
+    from workloads import make_inputs
+
+    sample = wl.scaled(T=rows) if rows != wl.T else wl
+    inp = make_inputs(sample, device="cpu")
+    z = inp["logits"]
+    t = inp["targets"].numpy()
+    seg = inp["segment_ids"].numpy() if inp["segment_ids"] is not None else None
+    blocks = [(r0, min(rows, r0 + 256)) for r0 in range(0, rows, 256)]
+
+    def work(b):
+        r0, r1 = b
+        zb = z[r0:r1].double().numpy()
+        return ce_oracle(zb, t[r0:r1], z_alpha=inp["z_alpha"], grad_scale=inp["grad_scale"],
+                         segment_ids=None if seg is None else seg[r0:r1],
+                         num_segments=inp["num_segments"],
+                         segment_mean=False)["loss"].sum()
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        tot = sum(ex.map(work, blocks))
+    dt = time.perf_counter() - t0
+    assert np.isfinite(tot)
+    return {"value": rows * wl.V / dt, "unit": "logit elems/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{rows} rows x V={wl.V} of the same recipe generated on the host; "
+                      f"fp64 numpy loss+gradient in 256-row blocks on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--cpu-rows", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange beyond a token count; "
+              "see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import WORKLOADS, alg_bytes
+
+    wl = WORKLOADS[args.workload]
+
+    # CPU reference first, before the GPU is touched.
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        rows = args.cpu_rows or min(wl.T, max(256, int(3e8 // wl.V) // 256 * 256))
+        cpu = cpu_baseline(wl, rows, threads)
+
+    import torch
+
+    import loss_vocab_amd as L
+    from workloads import make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    sets = []
+    for i in range(args.rotate):
+        inp = make_inputs(wl, device=dev, seed_offset=i)
+        in_place = wl.grad == "inplace"
+        loss = torch.empty(wl.T, dtype=torch.float32, device=dev)
+        grad = inp["logits"] if in_place else torch.empty((wl.T, wl.V), dtype=wl.grad_torch_dtype,
+                                                          device=dev)
+        seg = (torch.empty(wl.num_segments, dtype=torch.float32, device=dev)
+               if wl.num_segments else None)
+        ws_n = L.workspace_bytes(inp["logits"], num_segments=wl.num_segments)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+        sets.append((inp, loss, grad, seg, ws))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        inp, loss, grad, seg, ws = sets[i % len(sets)]
+        L.ce_fused_fwd_bwd(inp["logits"], inp["targets"], None, inp["segment_ids"],
+                           inp["z_alpha"], inp["grad_scale"], loss, seg, grad,
+                           num_segments=wl.num_segments, segment_mean=inp["segment_mean"],
+                           workspace=ws, stream=stream.cuda_stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps bracketed by synchronisation; per-step events on
+    # the launch stream give the kernels' own time.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per_call_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_call_ms = sum(per_call_ms) / len(per_call_ms)
+    ms_per_step = total_ms / args.steps
+
+    elems = wl.T * wl.V
+    nbytes = alg_bytes(wl)
+    achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": elems / (ms_per_step * 1e-3),
+        "unit": "logit elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "T": wl.T, "V": wl.V, "logits_dtype": wl.dtype,
+            "grad_dtype": "bf16" if wl.grad_torch_dtype == torch.bfloat16 else "f32",
+            "in_place": wl.grad == "inplace", "z_alpha": wl.z_alpha,
+            "ignored_rows": wl.n_masked, "segments": wl.num_segments,
+            "rotating_buffer_sets": args.rotate, "alg_bytes_per_step": nbytes,
+        },
+        "alg_GBps": nbytes / (ms_per_step * 1e-3) / 1e9,
+        "pct_of_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "kernel_ms_avg": avg_call_ms, "kernel_ms_median": per_call_ms[len(per_call_ms) // 2],
+        },
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,88 @@
+"""ctypes view of the C ABI declared in include/ce_fused.h.
+
+Loading never touches the GPU. There is no fallback: if the built library is
+absent, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libce_fused.so")
+
+CE_DTYPE_F32 = 0
+CE_DTYPE_BF16 = 1
+
+CE_OK = 0
+CE_ERR_INVALID_ARG = 1
+CE_ERR_UNSUPPORTED = 2
+CE_ERR_ALIAS = 3
+CE_ERR_WORKSPACE = 4
+CE_ERR_HIP = 5
+
+CE_FLAG_SEGMENT_MEAN = 0x1
+
+# Every symbol include/ce_fused.h declares.
+EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_status_string")
+
+
+class CeProblem(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("ld_logits", ctypes.c_int64),
+        ("ld_grad", ctypes.c_int64),
+        ("logits_dtype", ctypes.c_int32),
+        ("grad_dtype", ctypes.c_int32),
+        ("ignore_index", ctypes.c_int64),
+        ("num_segments", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+    ]
+
+
+class CeError(RuntimeError):
+    def __init__(self, status, where="ce_fused_fwd_bwd"):
+        self.status = status
+        super().__init__(f"{where} failed: {status_string(status)} ({status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m loss_vocab_amd.build` "
+            "(the fused CE has no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.ce_workspace_bytes.argtypes = [ctypes.POINTER(CeProblem)]
+    lib.ce_workspace_bytes.restype = ctypes.c_size_t
+    lib.ce_fused_fwd_bwd.argtypes = [
+        ctypes.POINTER(CeProblem), vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+        vp, vp, vp, vp, ctypes.c_size_t, vp,
+    ]
+    lib.ce_fused_fwd_bwd.restype = ctypes.c_int
+    lib.ce_status_string.argtypes = [ctypes.c_int]
+    lib.ce_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status):
+    return LIB.ce_status_string(int(status)).decode()
+
+
+def workspace_bytes(problem):
+    return int(LIB.ce_workspace_bytes(ctypes.byref(problem)))
+
+
+def call_raw(problem, logits, targets, mask, segment_ids, z_alpha, grad_scale,
+             loss_out, seg_loss_out, grad_out, workspace, workspace_bytes_, stream):
+    """Call ce_fused_fwd_bwd with integer addresses (0 = NULL); returns the status."""
+    return int(LIB.ce_fused_fwd_bwd(
+        ctypes.byref(problem), logits or None, targets or None, mask or None,
+        segment_ids or None, float(z_alpha), float(grad_scale), loss_out or None,
+        seg_loss_out or None, grad_out or None, workspace or None,
+        int(workspace_bytes_), stream or None))

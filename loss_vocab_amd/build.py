@@ -1,0 +1,51 @@
+"""Build the in-tree HIP library ``libce_fused.so`` for gfx950.
+
+Run ``python -m loss_vocab_amd.build`` (or ``__graft_entry__.build()``). The
+library is compiled by hipcc straight from ``csrc/ce_fused.hip``; it needs no
+GPU to build.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "ce_fused.hip")
+INC = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libce_fused.so")
+ARCH = "gfx950"
+
+# Packed-FP32 VALU forms are switched off for all device code.
+HIP_FLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc():
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the library)")
+
+
+def build(verbose=False, extra=()):
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", INC, SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

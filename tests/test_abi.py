@@ -1,0 +1,162 @@
+"""The C ABI on the CPU: the library loads, exports what the header declares,
+its struct layout matches the binding, and every host validation error comes
+back as a status code before any HIP call (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ce_fused.h")
+
+
+def _lib():
+    from loss_vocab_amd import _lib
+    return _lib
+
+
+def _declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ce_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert _declared_functions() == sorted(_lib().EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib().LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib().LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """Compile a C probe with gcc against the header and compare offsets."""
+    L = _lib()
+    fields = [f[0] for f in L.CeProblem._fields_]
+    src = tmp_path / "probe.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ce_fused.h"', 'int main(void){',
+             'printf("%zu\\n", sizeof(ce_problem));']
+    lines += [f'printf("%zu\\n", offsetof(ce_problem, {f}));' for f in fields]
+    lines += ["return 0;}"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(L.CeProblem)
+    for f, off in zip(fields, vals[1:]):
+        assert getattr(L.CeProblem, f).offset == off, f
+
+
+def test_status_strings():
+    L = _lib()
+    for code, name in [(0, "CE_OK"), (1, "CE_ERR_INVALID_ARG"), (2, "CE_ERR_UNSUPPORTED"),
+                       (3, "CE_ERR_ALIAS"), (4, "CE_ERR_WORKSPACE"), (5, "CE_ERR_HIP")]:
+        assert L.status_string(code) == name
+    assert L.status_string(99) == "CE_ERR_UNKNOWN"
+
+
+def _problem(T=8, V=100, ld=None, ldg=None, dt=0, gdt=0, S=0, flags=0):
+    L = _lib()
+    p = L.CeProblem()
+    p.T, p.V = T, V
+    p.ld_logits = V if ld is None else ld
+    p.ld_grad = V if ldg is None else ldg
+    p.logits_dtype, p.grad_dtype = dt, gdt
+    p.ignore_index = -100
+    p.num_segments = S
+    p.flags = flags
+    return p
+
+
+def test_workspace_bytes():
+    L = _lib()
+    assert L.workspace_bytes(_problem()) == 0
+    # [T] floats and [S+1] int32 offsets, each rounded up to 256 bytes
+    assert L.workspace_bytes(_problem(T=1000, S=7)) == 4096 + 256
+    assert L.workspace_bytes(_problem(T=65536, S=512)) == 262144 + 2304
+    assert L.LIB.ce_workspace_bytes(None) == 0
+
+
+# Fake device addresses: validation compares them, never dereferences them.
+A_LOGITS = 0x10000000
+A_TGT = 0x20000000
+A_LOSS = 0x30000000
+A_GRAD = 0x40000000
+A_SEG = 0x50000000
+A_WS = 0x60000000
+
+
+def _call(p, logits=A_LOGITS, targets=A_TGT, mask=0, seg=0, za=0.0, gs=1.0, loss=A_LOSS,
+          seg_out=0, grad=A_GRAD, ws=0, ws_bytes=0):
+    return _lib().call_raw(p, logits, targets, mask, seg, za, gs, loss, seg_out, grad, ws,
+                           ws_bytes, 0)
+
+
+@pytest.mark.parametrize("case,kwargs,pkw,expect", [
+    ("null problem", {}, None, 1),
+    ("T < 0", {}, dict(T=-1), 1),
+    ("V < 1", {}, dict(V=0), 1),
+    ("ld_logits < V", {}, dict(ld=99), 1),
+    ("ld_grad < V", {}, dict(ldg=50), 1),
+    ("bad logits dtype", {}, dict(dt=7), 1),
+    ("bad grad dtype", {}, dict(gdt=-1), 1),
+    ("unknown flag", {}, dict(flags=0x8), 1),
+    ("null logits", dict(logits=0), {}, 1),
+    ("null targets", dict(targets=0), {}, 1),
+    ("null loss_out", dict(loss=0), {}, 1),
+    ("segments without ids", {}, dict(S=4), 1),
+    ("ids without segments", dict(seg=A_SEG), {}, 1),
+    ("negative segments", {}, dict(S=-2), 1),
+    ("seg_loss_out without ids", dict(seg_out=A_LOSS + 4096), {}, 1),
+    ("segment mean without ids", {}, dict(flags=1), 1),
+    ("non-finite z_alpha", dict(za=float("nan")), {}, 1),
+    ("non-finite grad_scale", dict(gs=float("inf")), {}, 1),
+    ("grad overlaps logits (shifted)", dict(grad=A_LOGITS + 64), {}, 3),
+    ("in place with another dtype", dict(grad=A_LOGITS), dict(gdt=1), 3),
+    ("in place with another stride", dict(grad=A_LOGITS), dict(ldg=128, ld=100), 3),
+    ("workspace missing", dict(seg=A_SEG), dict(S=4), 4),
+    ("workspace too small", dict(seg=A_SEG, ws=A_WS, ws_bytes=100), dict(S=4), 4),
+])
+def test_validation_errors(case, kwargs, pkw, expect):
+    p = None if pkw is None else _problem(**pkw)
+    if p is None:
+        st = _lib().LIB.ce_fused_fwd_bwd(None, None, None, None, None, 0.0, 1.0, None, None,
+                                         None, None, 0, None)
+    else:
+        st = _call(p, **kwargs)
+    assert st == expect, (case, _lib().status_string(st))
+
+
+def test_product_path_has_no_fallback(monkeypatch, tmp_path):
+    """Without the built library, importing the binding fails loudly."""
+    import importlib
+    import loss_vocab_amd._lib as lib_mod
+    monkeypatch.setattr(os.path, "exists", lambda p: False if p.endswith("libce_fused.so") else True)
+    with pytest.raises(ImportError):
+        importlib.reload(lib_mod)
+    monkeypatch.undo()
+    importlib.reload(lib_mod)
+
+
+def test_package_does_not_import_the_oracle():
+    """The product package never references the oracle."""
+    pkg = os.path.join(ROOT, "loss_vocab_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    text = f.read()
+                assert "oracle" not in text, fn

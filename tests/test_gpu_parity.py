@@ -1,0 +1,381 @@
+"""HIP path vs the fp64 oracle, element by element, on seeded inputs.
+
+Small cases span several chunks per thread, the register-resident and the
+streamed kernel variants, and ragged tails (V not a multiple of the 16-byte
+width). Edge cases cover empty/degenerate shapes, strides, masks, infinities,
+in-place and forward-only calls, segments and determinism. Full-size cases run
+the five workload shapes in the benchmark's launch configuration and compare
+sampled rows (and sampled segments) with the oracle, plus properties that hold
+for every row.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from parity_utils import (check_grad, check_loss, check_zero_rows, run_hip, run_oracle,
+                          to_np64)
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+W = WORKLOADS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    import loss_vocab_amd  # noqa: F401  (raises if the HIP library is missing)
+    yield
+    torch.cuda.empty_cache()
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def compare_all(inp, *, grad_dtype=None, in_place=False, mask=None, want_grad=True, what=""):
+    logits = inp["logits"]
+    z64 = to_np64(logits)
+    gdt = grad_dtype or logits.dtype
+    loss, grad, seg = run_hip(inp, grad_dtype=gdt, in_place=in_place, want_grad=want_grad,
+                              mask=mask)
+    torch.cuda.synchronize()
+    ref = run_oracle(z64, _np(inp["targets"]), mask=_np(mask), segment_ids=_np(inp.get("segment_ids")),
+                     num_segments=inp.get("num_segments", 0), z_alpha=inp["z_alpha"],
+                     grad_scale=inp["grad_scale"], segment_mean=inp.get("segment_mean", False),
+                     want_grad=want_grad)
+    check_loss(_np(loss), ref["loss"], what + " loss")
+    inv = torch.as_tensor(~ref["valid"], device=DEV)
+    check_zero_rows(loss[inv], grad[inv] if grad is not None else None)
+    if want_grad:
+        check_grad(to_np64(grad), ref["grad"], gdt, what + " grad")
+    if seg is not None:
+        check_loss(_np(seg), ref["seg_nll"], what + " seg")
+        empty = ref["seg_nll"] == 0
+        assert np.all(_np(seg)[empty] == 0.0)
+    return loss, grad, seg, ref
+
+
+# ---------------------------------------------------------------------------
+# The five workload recipes at sizes the oracle finishes in seconds
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    ("f32_mask10_T256_V4096", W["ce_f32_T256_V4096_mask10"], {}),
+    ("bf16_collapse_zloss_ragged", W["cez_bf16_T8192_V32000_collapse"].scaled(T=300, V=3001), {}),
+    ("bf16_collapse_zloss_V32000", W["cez_bf16_T8192_V32000_collapse"].scaled(T=48), {}),
+    ("bf16_zipf_inplace_streamed", W["ce_bf16_T16384_V128256_zipf_inplace"].scaled(T=200, V=10007),
+     {"in_place": True}),
+    ("f32_peaked_zloss_streamed", W["cez_f32_T32768_V151936_peaked"].scaled(T=128, V=5003), {}),
+    ("bf16_segments", W["cezseg_bf16_T65536_V201088_seg512"].scaled(T=2000, V=515, num_segments=37),
+     {}),
+]
+
+
+@pytest.mark.parametrize("name,wl,opt", SMALL, ids=[s[0] for s in SMALL])
+def test_small_workloads(name, wl, opt):
+    print(f"[parity] {name} T={wl.T} V={wl.V}", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    compare_all(inp, in_place=opt.get("in_place", False), what=name)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+def _inp(z, t, alpha=0.0, gamma=1.0, seg=None, S=0, seg_mean=False):
+    return {"logits": z, "targets": t, "z_alpha": alpha, "grad_scale": gamma,
+            "segment_ids": seg, "num_segments": S, "segment_mean": seg_mean}
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 63, 64, 65, 4095, 4097, 8193])
+def test_vocab_sizes(dtype, V):
+    print(f"[parity] vocab V={V} {dtype}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V)
+    T = 5
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[1] = -100
+    compare_all(_inp(z, t, alpha=1e-3, gamma=0.25), what=f"V={V}")
+
+
+@pytest.mark.parametrize("T", [1, 3, 257])
+def test_row_counts(T):
+    g = torch.Generator(device=DEV).manual_seed(T)
+    z = torch.randn(T, 777, generator=g, device=DEV).to(torch.bfloat16)
+    t = torch.randint(0, 777, (T,), generator=g, device=DEV)
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / T), what=f"T={T}")
+
+
+def test_zero_rows():
+    import loss_vocab_amd as L
+    z = torch.empty(0, 100, device=DEV)
+    t = torch.empty(0, dtype=torch.int64, device=DEV)
+    loss, grad, _ = L.ce_fused(z, t)
+    torch.cuda.synchronize()
+    assert loss.numel() == 0 and grad.numel() == 0
+    # T = 0 with segments still writes zero segment sums
+    seg = torch.empty(0, dtype=torch.int32, device=DEV)
+    out = torch.full((4,), 7.0, device=DEV)
+    L.ce_fused_fwd_bwd(z, t, None, seg, 0.0, 1.0, torch.empty(0, device=DEV), out, None,
+                       num_segments=4)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+@pytest.mark.parametrize("dtype,pad", [(torch.float32, 13), (torch.bfloat16, 13),
+                                       (torch.float32, 64), (torch.bfloat16, 64)])
+def test_row_stride_larger_than_V(dtype, pad):
+    """pad 13 makes rows misaligned (scalar path); pad 64 keeps 16-byte rows."""
+    g = torch.Generator(device=DEV).manual_seed(pad)
+    T, V = 33, 1001
+    big = (torch.randn(T, V + pad, generator=g, device=DEV) * 2).to(dtype)
+    z = big[:, :V]
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[4] = -100
+    gbig = torch.full((T, V + 7), 5.0, dtype=torch.float32, device=DEV)
+    gout = gbig[:, :V]
+    import loss_vocab_amd as L
+    loss = torch.empty(T, device=DEV)
+    L.ce_fused_fwd_bwd(z, t, None, None, 1e-4, 0.5, loss, None, gout)
+    torch.cuda.synchronize()
+    ref = run_oracle(to_np64(z), _np(t), z_alpha=1e-4, grad_scale=0.5)
+    check_loss(_np(loss), ref["loss"])
+    check_grad(to_np64(gout), ref["grad"], torch.float32)
+    assert torch.all(gbig[:, V:] == 5.0), "padding columns of the gradient were written"
+    # the padding of the logits is never part of the result
+    big[:, V:] = float("nan")
+    loss2 = torch.empty(T, device=DEV)
+    L.ce_fused_fwd_bwd(z, t, None, None, 1e-4, 0.5, loss2, None, None)
+    torch.cuda.synchronize()
+    assert torch.equal(loss, loss2)
+
+
+def test_mask_array_and_ignore_index():
+    g = torch.Generator(device=DEV).manual_seed(3)
+    T, V = 64, 2050
+    z = torch.randn(T, V, generator=g, device=DEV).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[[0, 9]] = -100
+    mask = torch.ones(T, dtype=torch.uint8, device=DEV)
+    mask[[1, 9, 40]] = 0
+    z[1] = float("nan")            # an ignored row is never read
+    z[40] = float("-inf")
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1 / 59), mask=mask, what="mask")
+
+
+@pytest.mark.parametrize("all_masked", [True, False])
+def test_all_or_none_masked(all_masked):
+    g = torch.Generator(device=DEV).manual_seed(4)
+    T, V = 40, 3000
+    z = torch.randn(T, V, generator=g, device=DEV)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    if all_masked:
+        t[:] = -100
+    loss, grad, _, _ = compare_all(_inp(z, t, alpha=1e-4), grad_dtype=torch.bfloat16,
+                                   what="all/none")
+    if all_masked:
+        check_zero_rows(loss, grad)
+
+
+def test_infinite_logits():
+    T, V = 6, 300
+    z = torch.randn(T, V, device=DEV, generator=torch.Generator(device=DEV).manual_seed(6))
+    t = torch.tensor([5, 17, 299, 0, 150, 3], device=DEV)
+    z[0, :100] = float("-inf")           # many -inf non-targets
+    z[1, 17] = float("-inf")             # -inf target: NLL = +inf, target grad = -gamma
+    z[2, :299] = float("-inf")           # every non-target -inf (acts as V = 1)
+    z[3, 1::2] = float("-inf")
+    compare_all(_inp(z, t, alpha=1e-2, gamma=0.5), what="inf")
+
+
+def test_margin20_example_on_gpu():
+    """The pages' worked example (torchtitan #5661, second review)."""
+    z = torch.tensor([[0.0, 20.0]], device=DEV)
+    t = torch.tensor([1], device=DEV)
+    loss, grad, _, ref = compare_all(_inp(z, t), what="margin20")
+    assert abs(float(loss[0]) - 2.06e-9) < 0.005e-9
+    assert abs(float(grad[0, 1]) + 2.06e-9) < 0.005e-9
+    assert abs(float(grad[0].double().sum())) < 1e-15
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_collapse_regime_nll(dtype):
+    """Planted margins 17..45 (past the fp32 collapse point) without z-loss,
+    so the stored loss is the tiny NLL itself and is checked to rel 1e-5."""
+    g = torch.Generator(device=DEV).manual_seed(11)
+    T, V = 64, 9000
+    z = torch.randn(T, V, generator=g, device=DEV) * 2
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    margin = torch.linspace(17, 45, T, device=DEV)
+    z[torch.arange(T, device=DEV), t] = z.amax(dim=1) + margin
+    z = z.to(dtype)
+    loss, grad, _, ref = compare_all(_inp(z, t, gamma=1 / T), what="collapse")
+    assert torch.all(loss > 0)
+    assert torch.all(grad[torch.arange(T, device=DEV), t] < 0)
+
+
+@pytest.mark.parametrize("src,dst", [(torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)])
+def test_mixed_dtypes(src, dst):
+    g = torch.Generator(device=DEV).manual_seed(8)
+    z = torch.randn(70, 4099, generator=g, device=DEV).to(src)
+    t = torch.randint(0, 4099, (70,), generator=g, device=DEV)
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1 / 70), grad_dtype=dst, what="mixed")
+
+
+@pytest.mark.parametrize("V", [4096, 50001])
+def test_in_place_equals_out_of_place_and_forward_only(V):
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(V)
+    z = (torch.randn(77, V, generator=g, device=DEV) * 3).to(torch.bfloat16)
+    t = torch.randint(0, V, (77,), generator=g, device=DEV)
+    t[5] = -100
+    loss_a, grad_a, _ = L.ce_fused(z, t, z_alpha=1e-4, grad_scale=1 / 76)
+    loss_f, none, _ = L.ce_fused(z, t, z_alpha=1e-4, grad_scale=1 / 76, want_grad=False)
+    zc = z.clone()
+    loss_b, grad_b, _ = L.ce_fused(zc, t, z_alpha=1e-4, grad_scale=1 / 76, in_place=True)
+    torch.cuda.synchronize()
+    assert none is None
+    assert grad_b.data_ptr() == zc.data_ptr()
+    assert torch.equal(loss_a, loss_b) and torch.equal(loss_a, loss_f)
+    assert torch.equal(grad_a.view(torch.int16), grad_b.view(torch.int16))
+
+
+def test_z_alpha_zero_loss_is_nll():
+    g = torch.Generator(device=DEV).manual_seed(12)
+    z = torch.randn(50, 1234, generator=g, device=DEV)
+    t = torch.randint(0, 1234, (50,), generator=g, device=DEV)
+    seg = torch.zeros(50, dtype=torch.int32, device=DEV)
+    seg[25:] = 1
+    import loss_vocab_amd as L
+    loss, _, segsum = L.ce_fused(z, t, segment_ids=seg, num_segments=2, z_alpha=0.0)
+    torch.cuda.synchronize()
+    ref = run_oracle(to_np64(z), _np(t), z_alpha=0.0)
+    check_loss(_np(loss), ref["nll"])
+    check_loss(_np(segsum), [ref["nll"][:25].sum(), ref["nll"][25:].sum()])
+
+
+def test_out_of_range_targets_are_nan():
+    z = torch.randn(4, 100, device=DEV)
+    t = torch.tensor([100, -3, 7, 1000], device=DEV)
+    compare_all(_inp(z, t), what="oob")
+
+
+@pytest.mark.parametrize("layout", ["one", "singletons", "masked_segment", "empty_segments"])
+def test_segment_layouts(layout):
+    g = torch.Generator(device=DEV).manual_seed(21)
+    T, V = 96, 700
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    if layout == "one":
+        seg, S = torch.zeros(T, dtype=torch.int32), 1
+    elif layout == "singletons":
+        seg, S = torch.arange(T, dtype=torch.int32), T
+    elif layout == "masked_segment":
+        seg, S = torch.arange(T, dtype=torch.int32) // 12, 8
+        t[24:36] = -100                 # segment 2 fully ignored
+    else:
+        seg, S = torch.arange(T, dtype=torch.int32) // 12 * 2, 20   # odd ids and 16..19 empty
+    inp = _inp(z, t, alpha=1e-4, gamma=1.0, seg=seg.to(DEV), S=S, seg_mean=True)
+    _, _, segsum, ref = compare_all(inp, what=layout)
+    if layout == "masked_segment":
+        assert float(segsum[2]) == 0.0
+
+
+def test_deterministic():
+    inp = make_inputs(W["cez_bf16_T8192_V32000_collapse"].scaled(T=512), device=DEV)
+    a = run_hip(inp)
+    b = run_hip(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0])
+    assert torch.equal(a[1].view(torch.int16), b[1].view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# Full sizes, as the benchmark launches them: sampled rows vs the oracle
+# ---------------------------------------------------------------------------
+
+def _sample_rows(inp, T, k=24):
+    rng = np.random.default_rng(T)
+    t = _np(inp["targets"])
+    valid = np.nonzero(t != -100)[0]
+    masked = np.nonzero(t == -100)[0]
+    planted = np.nonzero(inp["planted"].numpy())[0]
+    rows = {0, 1, T - 1, T - 2}
+    rows |= set(rng.choice(valid, size=min(k, valid.size), replace=False).tolist())
+    if masked.size:
+        rows |= set(rng.choice(masked, size=min(6, masked.size), replace=False).tolist())
+    if planted.size:
+        rows |= set(rng.choice(planted, size=min(8, planted.size), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+FULL = ["ce_f32_T256_V4096_mask10", "cez_bf16_T8192_V32000_collapse",
+        "ce_bf16_T16384_V128256_zipf_inplace", "cez_f32_T32768_V151936_peaked",
+        "cezseg_bf16_T65536_V201088_seg512"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size(name):
+    import loss_vocab_amd as L
+    wl = W[name]
+    print(f"[parity] full {name}", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    T, V = wl.T, wl.V
+    rows = _sample_rows(inp, T)
+    ri = torch.as_tensor(rows, device=DEV)
+    z_rows = to_np64(inp["logits"][ri])
+    seg_ids = inp["segment_ids"]
+    # whole segments to check the sums on: first, last and two in between
+    seg_check = []
+    if seg_ids is not None:
+        ids = _np(seg_ids)
+        for s in (0, wl.num_segments // 3, 2 * wl.num_segments // 3, wl.num_segments - 1):
+            r = np.nonzero(ids == s)[0]
+            seg_check.append((s, r, to_np64(inp["logits"][torch.as_tensor(r, device=DEV)])))
+    in_place = wl.grad == "inplace"
+    loss, grad, seg = L.ce_fused(inp["logits"], inp["targets"], segment_ids=seg_ids,
+                                 num_segments=wl.num_segments, z_alpha=inp["z_alpha"],
+                                 grad_scale=inp["grad_scale"], segment_mean=inp["segment_mean"],
+                                 grad_dtype=wl.grad_torch_dtype, in_place=in_place)
+    torch.cuda.synchronize()
+    t_all = _np(inp["targets"])
+    # per-row scale: the segment length of each sampled row counts all rows of its id
+    scale = np.full(rows.size, inp["grad_scale"])
+    if inp["segment_mean"]:
+        lens = np.bincount(_np(seg_ids), minlength=wl.num_segments)
+        scale = inp["grad_scale"] / lens[_np(seg_ids)[rows]]
+    ref = run_oracle(z_rows, t_all[rows], z_alpha=inp["z_alpha"], grad_scale=1.0)
+    check_loss(_np(loss)[rows], ref["loss"], f"{name} sampled loss")
+    # the oracle ran with scale 1; apply each row's scale (exact in fp64 for
+    # the power-of-two-free factors up to rounding far below the tolerance)
+    g_ref = ref["grad"] * scale[:, None]
+    check_grad(to_np64(grad[ri]), g_ref, wl.grad_torch_dtype, f"{name} sampled grad")
+    # every ignored row is +0.0, every valid loss finite
+    inv = torch.as_tensor(t_all == -100, device=DEV)
+    check_zero_rows(loss[inv], grad[inv])
+    assert bool(torch.isfinite(loss[~inv]).all())
+    # without z-loss every valid gradient row sums to zero (torchtitan #5661,
+    # second review), up to the rounding of the stored values
+    if inp["z_alpha"] == 0.0:
+        eps = 2.0 ** -8 if wl.grad_torch_dtype == torch.bfloat16 else 1e-6
+        vrows = torch.nonzero(~inv).flatten()
+        for c0 in range(0, vrows.numel(), 1024):
+            gb = grad[vrows[c0:c0 + 1024]].double()
+            sums, absg = gb.sum(dim=1), gb.abs().sum(dim=1)
+            assert bool((sums.abs() <= eps * absg + 1e-12).all())
+            del gb
+    if seg is not None:
+        for s, r, zr in seg_check:
+            o = run_oracle(zr, t_all[r], z_alpha=inp["z_alpha"], grad_scale=1.0, want_grad=False)
+            ref_s = math.fsum(o["nll"][o["valid"]])
+            check_loss([float(seg[s])], [ref_s], f"{name} segment {s}")
+    del inp, loss, grad, seg
+    torch.cuda.empty_cache()
