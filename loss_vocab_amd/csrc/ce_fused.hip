@@ -12,15 +12,19 @@
 //
 // Device design (bandwidth-bound, no matrix cores):
 //  * one workgroup owns one row at a time (persistent grid-stride loop);
-//  * 16-byte loads/stores of bf16 or fp32, each thread owning the 16-byte
-//    chunks tid, tid + BLOCK, ...;
-//  * the first NRES chunks of each thread stay in registers as exps between
-//    the two passes, so they are read from HBM once; the rest of the row is
-//    streamed in pass 1 (online max / sum of exps) and streamed again in
-//    pass 2;
+//  * rows are read through a per-row buffer descriptor in 16-byte chunks:
+//    lane tid of slot i owns chunk i * BLOCK + tid, so one VGPR offset per
+//    lane plus a constant SGPR offset per slot address everything;
+//  * the first slots of each thread stay on chip between the two passes --
+//    as fp32 exps (NRES), as raw input in VGPRs (NRAW) or as raw input in LDS
+//    filled straight from HBM (NLDS) -- so they are read from HBM once; any
+//    remaining slots are streamed in pass 1 and read again in pass 2;
 //  * statistics are kept in the log2 domain: every exponential is one
-//    v_exp_f32 of an FMA, and a thread's partial is (shift, sum) with the
-//    shift a float that the merge uses exactly;
+//    v_exp_f32 of an FMA, and a partial is (shift, sum) with the shift a
+//    float that the merges use exactly;
+//  * the target column is set to -inf in the raw registers of the one lane
+//    that holds it, so no per-element test remains in the hot loops; its
+//    gradient is written by that lane after the row's chunk stores;
 //  * wave reduction by lane shuffles, then one LDS slot per wave;
 //  * the per-row epilogue (softplus, logaddexp, sigmoids, z-loss) in fp64;
 //  * per-segment NLL sums by a second kernel that walks each segment's rows
@@ -39,6 +43,8 @@ namespace {
 
 constexpr float kL2E = 1.44269504088896340736f;  // log2(e), rounded to float
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kNT = 2;                           // cache policy bits: non-temporal
+constexpr int kBufWord3 = 0x00020000;            // buffer descriptor word 3 (gfx9 raw buffer)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -56,8 +62,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
-// Element access. A "chunk" is W consecutive elements of a row; W is the
-// 16-byte width of the element type, or 1 for the unaligned fallback.
+// Element types
 // ---------------------------------------------------------------------------
 
 template <typename T>
@@ -66,12 +71,19 @@ struct Elem;
 template <>
 struct Elem<float> {
   static constexpr int BYTES = 4;
-  static constexpr int VEC = 4;
-  __device__ static float load1(const void* row, int64_t i) {
-    return static_cast<const float*>(row)[i];
+  static constexpr int VEC = 4;                  // elements per 16 bytes
+  static constexpr uint32_t NEG_INF_WORD = 0xff800000u;
+  __device__ static float load1(const void* row, uint32_t i) {
+    return *reinterpret_cast<const float*>(static_cast<const char*>(row) + i * 4u);
   }
-  __device__ static void store1(void* row, int64_t i, float v) {
-    __builtin_nontemporal_store(v, static_cast<float*>(row) + i);
+  __device__ static void store1(void* row, uint32_t i, float v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<float*>(static_cast<char*>(row) + i * 4u));
+  }
+  __device__ static void unpack(const u32x4 u, float (&x)[4]) {
+    x[0] = __uint_as_float(u.x);
+    x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z);
+    x[3] = __uint_as_float(u.w);
   }
 };
 
@@ -79,73 +91,29 @@ template <>
 struct Elem<bf16_t> {
   static constexpr int BYTES = 2;
   static constexpr int VEC = 8;
-  __device__ static float load1(const void* row, int64_t i) {
-    const uint32_t u = static_cast<const uint16_t*>(row)[i];
+  static constexpr uint32_t NEG_INF_WORD = 0xff80ff80u;
+  __device__ static float load1(const void* row, uint32_t i) {
+    const uint32_t u = *reinterpret_cast<const uint16_t*>(static_cast<const char*>(row) + i * 2u);
     return __uint_as_float(u << 16);
   }
-  __device__ static void store1(void* row, int64_t i, float v) {
+  __device__ static void store1(void* row, uint32_t i, float v) {
     const uint16_t h = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
-    __builtin_nontemporal_store(h, static_cast<uint16_t*>(row) + i);
+    __builtin_nontemporal_store(h, reinterpret_cast<uint16_t*>(static_cast<char*>(row) + i * 2u));
   }
-};
-
-// Raw storage of one chunk of W elements of type T.
-template <typename T, int W>
-struct Chunk {
-  static constexpr int NB = W * Elem<T>::BYTES;
-  static_assert(NB == 16 || W == 1, "a chunk is 16 bytes or one element");
-  u32x4 v;  // W == VEC: the 16 bytes; W == 1: the element's bits in v.x
-
-  __device__ void load(const void* row, int64_t c, bool nt) {
-    if constexpr (W == 1) {
-      v.x = __float_as_uint(Elem<T>::load1(row, c));
-    } else {
-      const u32x4* p = static_cast<const u32x4*>(row) + c;
-      v = nt ? __builtin_nontemporal_load(p) : *p;
-    }
-  }
-  __device__ void unpack(float (&x)[W]) const {
-    if constexpr (W == 1) {
-      x[0] = __uint_as_float(v.x);
-    } else if constexpr (Elem<T>::BYTES == 4) {
-      x[0] = __uint_as_float(v.x);
-      x[1] = __uint_as_float(v.y);
-      x[2] = __uint_as_float(v.z);
-      x[3] = __uint_as_float(v.w);
-    } else {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  __device__ static void unpack(const u32x4 u, float (&x)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[2 * k] = __uint_as_float(w[k] << 16);
-        x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-      }
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
     }
   }
 };
 
-// Store W consecutive gradient values (chunk index c of a row whose chunks
-// are W elements wide) as type TO, non-temporally.
-template <typename TO, int W>
-__device__ __forceinline__ void store_chunk(void* row, int64_t c, const float (&g)[W]) {
-  if constexpr (W == 1) {
-    Elem<TO>::store1(row, c, g[0]);
-  } else if constexpr (Elem<TO>::BYTES == 4) {
-    // W floats: 16 bytes per 4 elements.
-#pragma unroll
-    for (int q = 0; q < W / 4; ++q) {
-      u32x4 o = {__float_as_uint(g[4 * q]), __float_as_uint(g[4 * q + 1]),
-                 __float_as_uint(g[4 * q + 2]), __float_as_uint(g[4 * q + 3])};
-      __builtin_nontemporal_store(o, static_cast<u32x4*>(row) + c * (W / 4) + q);
-    }
-  } else if constexpr (W == 8) {
-    u32x4 o = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
-               pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
-    __builtin_nontemporal_store(o, static_cast<u32x4*>(row) + c);
-  } else {  // W == 4 bf16 outputs: 8 bytes
-    u32x2 o = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-    __builtin_nontemporal_store(o, static_cast<u32x2*>(row) + c);
-  }
-}
+// The empty asm marks the registers as rewritten (no instruction is emitted):
+// floats widened from them before it cannot be reused after it, so a resident
+// chunk costs 4 registers between passes instead of up to 8 live floats.
+__device__ __forceinline__ void touch(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Merge partial (m, s) -- s = sum 2^(y - m) over a set, m a float shift in
 // log2 units -- with (m2, s2). An empty partial is (-inf, 0).
@@ -154,6 +122,21 @@ __device__ __forceinline__ void merge(float& m, float& s, float m2, float s2) {
   const float sh = (mn == kNegInf) ? 0.f : mn;
   s = s * fexp2(m - sh) + s2 * fexp2(m2 - sh);
   m = mn;
+}
+
+// Online update of (mL, s) with G values (-inf = absent).
+template <int G>
+__device__ __forceinline__ void online_group(float& mL, float& s, const float* x) {
+  float gmax = kNegInf;
+#pragma unroll
+  for (int k = 0; k < G; ++k) gmax = fmaxf(gmax, x[k]);
+  const float mn = fmaxf(mL, gmax * kL2E);
+  const float sh = (mn == kNegInf) ? 0.f : mn;
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < G; ++k) acc += fexp2(__builtin_fmaf(x[k], kL2E, -sh));
+  s = s * fexp2(mL - sh) + acc;
+  mL = mn;
 }
 
 __device__ __forceinline__ double sigmoid_d(double x) {
@@ -177,86 +160,292 @@ struct RowParams {
   float z_alpha, grad_scale;
 };
 
-// ---------------------------------------------------------------------------
-// Row kernel.
-//   TI/TO  : logits / gradient element types
-//   W      : elements per chunk (16-byte width, or 1 for the unaligned path)
-//   BLOCK  : threads per workgroup
-//   NRES   : chunks per thread kept in registers between the passes
-//   U      : chunks per thread in flight in the streamed loops
-//   WRITE  : write the gradient (false = forward only)
-// ---------------------------------------------------------------------------
-template <typename TI, typename TO, int W, int BLOCK, int NRES, int U, bool WRITE>
-__global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
-  constexpr int NWAVE = BLOCK / 64;
-  static_assert(BLOCK % 64 == 0, "whole waves");
-  __shared__ float red_m[2][NWAVE];
-  __shared__ float red_s[2][NWAVE];
+// Per-row results of the epilogue that pass 2 needs.
+struct RowOut {
+  float g_t;     // gradient of the target column
+  float cnt;     // scale * (1 + 2 alpha lse): factor of every non-target softmax value
+  float kl;      // lse in log2 units
+  double cnt_d;
+  double lse_l2; // lse in log2 units, fp64
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int64_t V = p.V;
-  const int64_t nchunk = V / W;
-  const int tail = static_cast<int>(V - nchunk * W);
+// Block-reduced (M, S) of the non-target columns -> loss, NLL, gradient
+// factors, all in fp64 (the NLL of a confident row is ~e^-40 and keeps its
+// relative accuracy only if LSE_nt - z_t is formed in fp64).
+__device__ __forceinline__ RowOut row_epilogue(const RowParams& p, int64_t r, float M, float S,
+                                               float zt, bool write_loss) {
+  const double l2e = static_cast<double>(kL2E);
+  const double lse_nt = (M == kNegInf) ? -HUGE_VAL
+                                       : static_cast<double>(M) / l2e + log(static_cast<double>(S));
+  const double zt_d = static_cast<double>(zt);
+  const double xx = lse_nt - zt_d;                           // LSE_nt - z_t
+  const double l1p = log1p(exp(-fabs(xx)));
+  const double nll = (xx > 0.0 ? xx : 0.0) + l1p;            // softplus
+  const double lse = (lse_nt > zt_d ? lse_nt : zt_d) + l1p;  // logaddexp
+  const double p_nt = sigmoid_d(xx);
+  const double p_t = sigmoid_d(-xx);
+  double scale = static_cast<double>(p.grad_scale);
+  if (p.seg_mean) {
+    int32_t sid = p.seg_ids[r];
+    sid = sid < 0 ? 0 : (sid >= p.num_segments ? p.num_segments - 1 : sid);
+    const int32_t len = p.seg_start[sid + 1] - p.seg_start[sid];
+    scale /= static_cast<double>(len > 0 ? len : 1);
+  }
+  const double alpha = static_cast<double>(p.z_alpha);
+  const double zfac = (alpha == 0.0) ? 0.0 : 2.0 * alpha * lse;
+  if (write_loss) {
+    const double loss = nll + ((alpha == 0.0) ? 0.0 : alpha * lse * lse);
+    p.loss_out[r] = static_cast<float>(loss);
+    if (p.nll_ws) p.nll_ws[r] = static_cast<float>(nll);
+  }
+  RowOut o;
+  o.cnt_d = scale * (1.0 + zfac);
+  o.g_t = static_cast<float>(scale * (-p_nt + zfac * p_t));
+  o.cnt = static_cast<float>(o.cnt_d);
+  o.lse_l2 = l2e * lse;
+  o.kl = static_cast<float>(o.lse_l2);
+  return o;
+}
+
+// Workgroup reduction of per-lane (mL, s); every thread gets the result.
+template <int BLOCK>
+__device__ __forceinline__ void block_reduce(float& mL, float& s, float (&red_m)[2][BLOCK / 64],
+                                             float (&red_s)[2][BLOCK / 64], int par,
+                                             uint32_t lane, uint32_t wid) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(mL, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    merge(mL, s, m2, s2);
+  }
+  if (lane == 0) {
+    red_m[par][wid] = mL;
+    red_s[par][wid] = s;
+  }
+  __syncthreads();
+  float M = red_m[par][0], S = red_s[par][0];
+#pragma unroll
+  for (int w = 1; w < BLOCK / 64; ++w) merge(M, S, red_m[par][w], red_s[par][w]);
+  mL = M;
+  s = S;
+}
+
+// Fill an ignored (0) or poisoned (NaN) gradient row and its loss.
+template <typename TO, int BLOCK>
+__device__ __forceinline__ void fill_row(const RowParams& p, int64_t r, void* grow, uint32_t V,
+                                         float fill, bool write) {
+  if (threadIdx.x == 0) {
+    p.loss_out[r] = fill;
+    if (p.nll_ws) p.nll_ws[r] = fill;
+  }
+  if (!write) return;
+  constexpr int VEC = Elem<TO>::VEC;
+  const bool vec = (reinterpret_cast<uintptr_t>(grow) % 16) == 0;
+  const uint32_t nvec = vec ? V / VEC : 0;
+  const uint32_t fw = Elem<TO>::BYTES == 4 ? __float_as_uint(fill) : (pack_bf16x2(fill, fill));
+  const u32x4 f4 = {fw, fw, fw, fw};
+  for (uint32_t c = threadIdx.x; c < nvec; c += BLOCK)
+    __builtin_nontemporal_store(f4, reinterpret_cast<u32x4*>(static_cast<char*>(grow) + c * 16u));
+  for (uint32_t j = nvec * VEC + threadIdx.x; j < V; j += BLOCK) Elem<TO>::store1(grow, j, fill);
+}
+
+// ---------------------------------------------------------------------------
+// One-element kernel: rows whose start or stride is not 16-byte aligned.
+// Two streamed passes, one element per lane and step.
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO, int BLOCK, bool WRITE>
+__global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
+  __shared__ float red_m[2][BLOCK / 64];
+  __shared__ float red_s[2][BLOCK / 64];
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
+  const uint32_t V = static_cast<uint32_t>(p.V);
   const size_t in_row_bytes = static_cast<size_t>(p.ld_in) * Elem<TI>::BYTES;
   const size_t out_row_bytes = static_cast<size_t>(p.ld_out) * Elem<TO>::BYTES;
+  int par = 0;
+  for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
+    const int64_t t64 = p.targets[r];
+    const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+    void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes : nullptr;
+    if (!valid || t64 < 0 || t64 >= static_cast<int64_t>(V)) {
+      fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
+      continue;
+    }
+    const uint32_t t = static_cast<uint32_t>(t64);
+    const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes;
+    const float zt = Elem<TI>::load1(zrow, t);
+    float mL = kNegInf, s = 0.f;
+    for (uint32_t b = 0; b < V; b += 4 * BLOCK) {
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t j = b + u * BLOCK + tid;
+        x[u] = (j < V && j != t) ? Elem<TI>::load1(zrow, j) : kNegInf;
+      }
+      online_group<4>(mL, s, x);
+    }
+    block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+    const RowOut o = row_epilogue(p, r, mL, s, zt, tid == 0);
+    if constexpr (WRITE) {
+      for (uint32_t j = tid; j < V; j += BLOCK) {
+        const float g = (j == t) ? o.g_t
+                                 : o.cnt * fexp2(__builtin_fmaf(Elem<TI>::load1(zrow, j), kL2E, -o.kl));
+        Elem<TO>::store1(grow, j, g);
+      }
+    }
+  }
+}
+
+// v[i] &= and_m, |= or_m for the one slot i == k (k uniform): a compare
+// chain on k, so only that slot's registers are touched.
+template <int N>
+__device__ __forceinline__ void mask_target_slot(u32x4 (&v)[N], uint32_t k, u32x4 and_m,
+                                                 u32x4 or_m) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (k == static_cast<uint32_t>(i)) {
+      v[i] = (v[i] & and_m) | or_m;
+      return;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Vector kernel (16-byte aligned rows).
+//   TI/TO  : logits / gradient element types
+//   BLOCK  : threads per workgroup
+//   NRES   : slots per thread kept in registers as fp32 exps between passes
+//   NRAW   : slots per thread kept in registers as raw input between passes
+//   NLDS   : slots per thread staged in LDS (loaded HBM -> LDS directly)
+//   U      : slots per thread per step of the streamed loops
+//   WRITE  : write the gradient (false = forward only)
+//   PF     : double-buffer the streamed loops (2 U slots in flight per lane)
+//   EPI1   : one wave runs the fp64 epilogue and shares it through LDS
+// Slot i of thread tid is chunk c = i * BLOCK + tid (a chunk is 16 bytes of
+// input). Slots [0, NRES) are exp-resident, then NRAW raw-resident, then NLDS
+// in LDS; later slots are streamed. Loads never branch per lane: a lane past
+// the row's last chunk loads the last chunk again (in bounds) and replaces it
+// by -inf; only stores are predicated, and only in the row's partial slot.
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
+          bool PF, bool EPI1>
+__global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
+  constexpr int W = Elem<TI>::VEC;                 // elements per chunk
+  constexpr uint32_t OB = W * Elem<TO>::BYTES;     // gradient bytes per chunk
+  constexpr int NON = NRES + NRAW + NLDS;          // on-chip slots per thread
+  static_assert(BLOCK % 64 == 0, "whole waves");
+  __shared__ float red_m[2][BLOCK / 64];
+  __shared__ float red_s[2][BLOCK / 64];
+  __shared__ u32x4 stage[NLDS > 0 ? NLDS : 1][NLDS > 0 ? BLOCK : 1];
+  __shared__ float epi[2][4];
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wid = tid >> 6;
+  // In-row offsets are 32-bit (the host bounds a row below 2 GiB).
+  const uint32_t V = static_cast<uint32_t>(p.V);
+  const uint32_t nchunk = V / W;
+  const uint32_t clast = nchunk > 0 ? nchunk - 1 : 0;
+  const uint32_t tail_begin = nchunk * W;
+  const uint32_t voff_in = tid * 16u;
+  const uint32_t voff_out = tid * OB;
+  const size_t in_row_bytes = static_cast<size_t>(p.ld_in) * Elem<TI>::BYTES;
+  const size_t out_row_bytes = static_cast<size_t>(p.ld_out) * Elem<TO>::BYTES;
+  const uint32_t neg_w = Elem<TI>::NEG_INF_WORD;
+  const u32x4 neg4 = {neg_w, neg_w, neg_w, neg_w};
 
   int par = 0;
   for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
-    const int64_t t = p.targets[r];
-    const bool valid = (t != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+    const int64_t t64 = p.targets[r];
+    const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
     void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes : nullptr;
-
-    if (!valid || t < 0 || t >= V) {
+    if (!valid || t64 < 0 || t64 >= static_cast<int64_t>(V)) {
       // Ignored row: +0.0 everywhere, logits never read. Valid row with an
       // out-of-range target: NaN loss and gradient row.
-      const float fill = valid ? __builtin_nanf("") : 0.f;
-      if (tid == 0) {
-        p.loss_out[r] = fill;
-        if (p.nll_ws) p.nll_ws[r] = fill;
-      }
-      if constexpr (WRITE) {
-        float f[W];
-#pragma unroll
-        for (int k = 0; k < W; ++k) f[k] = fill;
-        for (int64_t c = tid; c < nchunk; c += BLOCK) store_chunk<TO, W>(grow, c, f);
-        if (tid < tail) Elem<TO>::store1(grow, nchunk * W + tid, fill);
-      }
+      fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
       continue;
     }
 
+    const uint32_t t = static_cast<uint32_t>(t64);
     const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes;
     const float zt = Elem<TI>::load1(zrow, t);
-    const int64_t ct = t / W;              // chunk holding the target column
-    const int kt = static_cast<int>(t - ct * W);
+    const __amdgpu_buffer_rsrc_t rin =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(zrow), 0, nchunk * 16u, kBufWord3);
 
-    // ---- pass 1a: resident chunks -> exps kept in registers ---------------
+    // Where the target sits: chunk ct, element kt, slot st, lane `mine`.
+    const uint32_t ct = t / W;
+    const uint32_t kt = t - ct * W;
+    const uint32_t st = ct / BLOCK;
+    const bool in_chunks = t < tail_begin;
+    const bool mine = in_chunks && (ct - st * BLOCK) == tid;
+    // AND/OR word masks that set element kt of a raw chunk to -inf (uniform).
+    const uint32_t kq = (kt * Elem<TI>::BYTES) >> 2;             // word of the chunk
+    const uint32_t ksh = (kt * Elem<TI>::BYTES * 8u) & 31u;      // bit offset in the word
+    const uint32_t kmask = Elem<TI>::BYTES == 4 ? 0xffffffffu : (0xffffu << ksh);
+    const uint32_t kput = Elem<TI>::BYTES == 4 ? 0xff800000u : (0xff80u << ksh);
+    const u32x4 and_m = {kq == 0 ? ~kmask : ~0u, kq == 1 ? ~kmask : ~0u,
+                         kq == 2 ? ~kmask : ~0u, kq == 3 ? ~kmask : ~0u};
+    const u32x4 or_m = {kq == 0 ? kput : 0u, kq == 1 ? kput : 0u, kq == 2 ? kput : 0u,
+                        kq == 3 ? kput : 0u};
+
+    // Slot loads: lane offsets are clamped to the last chunk, so every load
+    // is in bounds and none branches; lanes past the row end are replaced by
+    // -inf afterwards. The target's element is set to -inf in the one lane
+    // that holds it.
+    // The lane offset is re-derived every row (the empty asm hides that it is
+    // row-invariant), so the per-slot offsets are formed next to their loads
+    // instead of being hoisted out of the row loop and kept live.
+    uint32_t vin = voff_in;
+    asm volatile("" : "+v"(vin));
+    const uint32_t c16_last = clast * 16u;
+    auto load_slot = [&](uint32_t base) -> u32x4 {
+      return __builtin_amdgcn_raw_buffer_load_b128(rin, min(vin + base * 16u, c16_last), 0, 0);
+    };
+    auto load_slot_last_use = [&](uint32_t base) -> u32x4 {
+      return __builtin_amdgcn_raw_buffer_load_b128(rin, min(vin + base * 16u, c16_last), 0, kNT);
+    };
+    // On-chip slots are read from memory exactly once: non-temporal.
+    auto fix_slot = [&](uint32_t base, u32x4& v) {
+      const bool out = base + tid >= nchunk;
+      v.x = out ? neg_w : v.x;
+      v.y = out ? neg_w : v.y;
+      v.z = out ? neg_w : v.z;
+      v.w = out ? neg_w : v.w;
+    };
+
+    // ---- issue every on-chip load first ------------------------------------
+    u32x4 rawe[NRES > 0 ? NRES : 1];
+    u32x4 rawv[NRAW > 0 ? NRAW : 1];
+    if (nchunk > 0) {
+#pragma unroll
+      for (int i = 0; i < NRES; ++i) rawe[i] = load_slot_last_use(i * BLOCK);
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) rawv[i] = load_slot_last_use((NRES + i) * BLOCK);
+      if constexpr (NLDS > 0) {
+        // HBM -> LDS without a register round trip: lane l of a wave lands
+        // at base + 16 l, so slot i of thread tid is stage[i][tid].
+#pragma unroll
+        for (int i = 0; i < NLDS; ++i) {
+          const uint32_t off = min(vin + (NRES + NRAW + i) * BLOCK * 16u, c16_last);
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)(static_cast<const char*>(zrow) + off),
+              (__attribute__((address_space(3))) void*)(&stage[i][tid & ~63u]), 16, 0, kNT);
+        }
+      }
+    }
+
+    float mL = kNegInf, s = 0.f;
+
+    // ---- pass 1a: exp-resident slots ---------------------------------------
     float e[NRES > 0 ? NRES : 1][W];
     float rsh = 0.f;          // shift of the resident exps (log2 units)
-    float mL = kNegInf, s = 0.f;
     if constexpr (NRES > 0) {
-      Chunk<TI, W> raw[NRES];
 #pragma unroll
-      for (int i = 0; i < NRES; ++i) {
-        const int64_t c = static_cast<int64_t>(i) * BLOCK + tid;
-        if (c < nchunk) raw[i].load(zrow, c, false);
-      }
+      for (int i = 0; i < NRES; ++i) fix_slot(i * BLOCK, rawe[i]);
+      if (mine && st < NRES) mask_target_slot<NRES>(rawe, st, and_m, or_m);
       float rmax = kNegInf;
 #pragma unroll
       for (int i = 0; i < NRES; ++i) {
-        const int64_t c = static_cast<int64_t>(i) * BLOCK + tid;
-        if (c < nchunk) {
-          raw[i].unpack(e[i]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < W; ++k) e[i][k] = kNegInf;
-        }
-        if (c == ct) {
-#pragma unroll
-          for (int k = 0; k < W; ++k)
-            if (k == kt) e[i][k] = kNegInf;   // the target is not summed
-        }
+        Elem<TI>::unpack(rawe[i], e[i]);
 #pragma unroll
         for (int k = 0; k < W; ++k) rmax = fmaxf(rmax, e[i][k]);
       }
@@ -277,156 +466,220 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       s = rs;
     }
 
-    // ---- pass 1b: streamed chunks, online (shift, sum) ---------------------
-    for (int64_t c0 = static_cast<int64_t>(NRES) * BLOCK + tid; c0 < nchunk;
-         c0 += static_cast<int64_t>(U) * BLOCK) {
-      Chunk<TI, W> raw[U];
+    // ---- pass 1b: raw register-resident slots (max, then sum) -------------
+    if constexpr (NRAW > 0) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + static_cast<int64_t>(u) * BLOCK;
-        if (c < nchunk) raw[u].load(zrow, c, false);
+      for (int i = 0; i < NRAW; ++i) fix_slot((NRES + i) * BLOCK, rawv[i]);
+      if (mine && st >= NRES && st < NRES + NRAW)
+        mask_target_slot<NRAW>(rawv, st - NRES, and_m, or_m);
+      float vmax = kNegInf;
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) {
+        float x[W];
+        Elem<TI>::unpack(rawv[i], x);
+#pragma unroll
+        for (int k = 0; k < W; ++k) vmax = fmaxf(vmax, x[k]);
       }
-      float x[U][W];
-      float gmax = kNegInf;
+      const float vml = vmax * kL2E;
+      const float vsh = (vml == kNegInf) ? 0.f : vml;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t c = c0 + static_cast<int64_t>(u) * BLOCK;
-        if (c < nchunk) {
-          raw[u].unpack(x[u]);
-        } else {
+      for (int i = 0; i < NRAW; ++i) touch(rawv[i]);
+      float vs = 0.f;
 #pragma unroll
-          for (int k = 0; k < W; ++k) x[u][k] = kNegInf;
-        }
-        if (c == ct) {
-#pragma unroll
-          for (int k = 0; k < W; ++k)
-            if (k == kt) x[u][k] = kNegInf;
-        }
-#pragma unroll
-        for (int k = 0; k < W; ++k) gmax = fmaxf(gmax, x[u][k]);
-      }
-      const float mn = fmaxf(mL, gmax * kL2E);
-      const float sh = (mn == kNegInf) ? 0.f : mn;
-      float acc = 0.f;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int i = 0; i < NRAW; ++i) {
+        float x[W];
+        Elem<TI>::unpack(rawv[i], x);
         float cs = 0.f;
 #pragma unroll
-        for (int k = 0; k < W; ++k) cs += fexp2(__builtin_fmaf(x[u][k], kL2E, -sh));
-        acc += cs;
+        for (int k = 0; k < W; ++k) cs += fexp2(__builtin_fmaf(x[k], kL2E, -vsh));
+        vs += cs;
       }
-      s = s * fexp2(mL - sh) + acc;
-      mL = mn;
+      merge(mL, s, vml, vs);
     }
-    // Elements past the last whole chunk: one per thread.
-    if (tid < tail) {
-      const int64_t j = nchunk * W + tid;
+
+    // ---- pass 1c: LDS-staged slots -----------------------------------------
+    if constexpr (NLDS > 0) {
+      constexpr int i0 = NRES + NRAW;
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's HBM -> LDS copies have landed
+#pragma unroll
+      for (int i = 0; i < NLDS; ++i) {
+        u32x4 v = stage[i][tid];
+        fix_slot((i0 + i) * BLOCK, v);
+        if (mine && i0 + i == static_cast<int>(st)) v = (v & and_m) | or_m;
+        float x[W];
+        Elem<TI>::unpack(v, x);
+        online_group<W>(mL, s, x);
+      }
+    }
+
+    // ---- pass 1d: streamed slots, online (shift, sum) ----------------------
+    auto stream1 = [&](u32x4 (&raw)[U], uint32_t b) {
+      float x[U * W];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        fix_slot(b + u * BLOCK, raw[u]);
+        if (mine && b + u * BLOCK == st * BLOCK) raw[u] = (raw[u] & and_m) | or_m;
+        float xu[W];
+        Elem<TI>::unpack(raw[u], xu);
+#pragma unroll
+        for (int k = 0; k < W; ++k) x[u * W + k] = xu[k];
+      }
+      online_group<U * W>(mL, s, x);
+    };
+    if constexpr (PF) {
+      // Two groups in flight: group B's loads run while group A is reduced.
+      // Loads past the row end are clamped to its last chunk (one broadcast
+      // line) and their lanes are -inf, so a trailing empty group is harmless.
+      if (NON * BLOCK < nchunk) {
+        u32x4 ra[U], rb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ra[u] = load_slot(NON * BLOCK + u * BLOCK);
+        for (uint32_t b = NON * BLOCK; b < nchunk; b += 2 * U * BLOCK) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) rb[u] = load_slot(b + (U + u) * BLOCK);
+          stream1(ra, b);
+#pragma unroll
+          for (int u = 0; u < U; ++u) ra[u] = load_slot(b + (2 * U + u) * BLOCK);
+          stream1(rb, b + U * BLOCK);
+        }
+      }
+    } else {
+      for (uint32_t b = NON * BLOCK; b < nchunk; b += U * BLOCK) {
+        u32x4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = load_slot(b + u * BLOCK);
+        stream1(raw, b);
+      }
+    }
+    // Elements past the last whole chunk: one per lane.
+    if (tid < V - tail_begin) {
+      const uint32_t j = tail_begin + tid;
       const float xv = (j == t) ? kNegInf : Elem<TI>::load1(zrow, j);
       merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
     }
 
-    // ---- workgroup reduction of (shift, sum) -------------------------------
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float m2 = __shfl_xor(mL, off, 64);
-      const float s2 = __shfl_xor(s, off, 64);
-      merge(mL, s, m2, s2);
-    }
-    if (lane == 0) {
-      red_m[par][wid] = mL;
-      red_s[par][wid] = s;
-    }
-    __syncthreads();
-    float M = red_m[par][0], S = red_s[par][0];
-#pragma unroll
-    for (int w = 1; w < NWAVE; ++w) merge(M, S, red_m[par][w], red_s[par][w]);
-
-    // ---- per-row epilogue in fp64 ------------------------------------------
-    const double l2e = static_cast<double>(kL2E);
-    const double lse_nt = (M == kNegInf) ? -HUGE_VAL
-                                         : static_cast<double>(M) / l2e + log(static_cast<double>(S));
-    const double zt_d = static_cast<double>(zt);
-    const double xx = lse_nt - zt_d;             // LSE_nt - z_t
-    const double l1p = log1p(exp(-fabs(xx)));
-    const double nll = (xx > 0.0 ? xx : 0.0) + l1p;              // softplus
-    const double lse = (lse_nt > zt_d ? lse_nt : zt_d) + l1p;    // logaddexp
-    const double p_nt = sigmoid_d(xx);
-    const double p_t = sigmoid_d(-xx);
-    double scale = static_cast<double>(p.grad_scale);
-    if (p.seg_mean) {
-      int32_t sid = p.seg_ids[r];
-      sid = sid < 0 ? 0 : (sid >= p.num_segments ? p.num_segments - 1 : sid);
-      const int32_t len = p.seg_start[sid + 1] - p.seg_start[sid];
-      scale /= static_cast<double>(len > 0 ? len : 1);
-    }
-    const double alpha = static_cast<double>(p.z_alpha);
-    const double zfac = (alpha == 0.0) ? 0.0 : 2.0 * alpha * lse;
-    if (tid == 0) {
-      const double loss = nll + ((alpha == 0.0) ? 0.0 : alpha * lse * lse);
-      p.loss_out[r] = static_cast<float>(loss);
-      if (p.nll_ws) p.nll_ws[r] = static_cast<float>(nll);
+    block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+    RowOut o;
+    if constexpr (EPI1) {
+      // Wave 0 alone runs the fp64 epilogue; the others wait at the barrier,
+      // leaving the SIMDs to other workgroups.
+      if (wid == 0) {
+        o = row_epilogue(p, r, mL, s, zt, tid == 0);
+        if (lane == 0) {
+          epi[par][0] = o.g_t;
+          epi[par][1] = o.cnt;
+          epi[par][2] = o.kl;
+        }
+      }
+      __syncthreads();
+      o.g_t = epi[par][0];
+      o.cnt = epi[par][1];
+      o.kl = epi[par][2];
+    } else {
+      o = row_epilogue(p, r, mL, s, zt, tid == 0);
     }
 
     // ---- pass 2: gradient ----------------------------------------------------
     if constexpr (WRITE) {
-      const double cnt = scale * (1.0 + zfac);               // non-target factor
-      const float g_t = static_cast<float>(scale * (-p_nt + zfac * p_t));
-      const float cnt_f = static_cast<float>(cnt);
-      const float kl = static_cast<float>(l2e * lse);        // lse in log2 units
+      const __amdgpu_buffer_rsrc_t rout =
+          __builtin_amdgcn_make_buffer_rsrc(grow, 0, nchunk * OB, kBufWord3);
+      uint32_t vout = voff_out;
+      asm volatile("" : "+v"(vout));
+      auto store_slot = [&](uint32_t base, const float (&g)[W]) {
+        if (base + BLOCK > nchunk && base + tid >= nchunk) return;
+        const uint32_t vo = vout + base * OB;
+        const uint32_t so = 0u;
+        if constexpr (Elem<TO>::BYTES == 2 && W == 8) {
+          const u32x4 q = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
+                           pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(q, rout, vo, so, kNT);
+        } else if constexpr (Elem<TO>::BYTES == 2) {   // 4 fp32 in -> 4 bf16 out
+          const u32x2 q = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+          __builtin_amdgcn_raw_buffer_store_b64(q, rout, vo, so, kNT);
+        } else {
+#pragma unroll
+          for (int h = 0; h < W / 4; ++h) {
+            const u32x4 q = {__float_as_uint(g[4 * h]), __float_as_uint(g[4 * h + 1]),
+                             __float_as_uint(g[4 * h + 2]), __float_as_uint(g[4 * h + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(q, rout, vo + 16u * h, so, kNT);
+          }
+        }
+      };
+      auto grad_of = [&](const u32x4 v, float (&g)[W]) {
+        float x[W];
+        Elem<TI>::unpack(v, x);
+#pragma unroll
+        for (int k = 0; k < W; ++k) g[k] = o.cnt * fexp2(__builtin_fmaf(x[k], kL2E, -o.kl));
+      };
       if constexpr (NRES > 0) {
-        const float f = static_cast<float>(cnt * exp2(static_cast<double>(rsh) - l2e * lse));
+        // Resident exps carry the lane's own shift rsh: rescale to lse.
+        const float f = o.cnt * fexp2(rsh - o.kl);
 #pragma unroll
         for (int i = 0; i < NRES; ++i) {
-          const int64_t c = static_cast<int64_t>(i) * BLOCK + tid;
-          if (c < nchunk) {
-            float g[W];
+          float g[W];
 #pragma unroll
-            for (int k = 0; k < W; ++k) g[k] = e[i][k] * f;
-            if (c == ct) {
-#pragma unroll
-              for (int k = 0; k < W; ++k)
-                if (k == kt) g[k] = g_t;
-            }
-            store_chunk<TO, W>(grow, c, g);
-          }
+          for (int k = 0; k < W; ++k) g[k] = e[i][k] * f;
+          store_slot(i * BLOCK, g);
         }
       }
-      for (int64_t c0 = static_cast<int64_t>(NRES) * BLOCK + tid; c0 < nchunk;
-           c0 += static_cast<int64_t>(U) * BLOCK) {
-        Chunk<TI, W> raw[U];
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) touch(rawv[i]);
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) {
+        float g[W];
+        grad_of(rawv[i], g);
+        store_slot((NRES + i) * BLOCK, g);
+      }
+#pragma unroll
+      for (int i = 0; i < NLDS; ++i) {
+        float g[W];
+        grad_of(stage[i][tid], g);
+        store_slot((NRES + NRAW + i) * BLOCK, g);
+      }
+      auto stream2 = [&](const u32x4 (&raw)[U], uint32_t b) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t c = c0 + static_cast<int64_t>(u) * BLOCK;
-          if (c < nchunk) raw[u].load(zrow, c, true);
+          float g[W];
+          grad_of(raw[u], g);
+          store_slot(b + u * BLOCK, g);
         }
+      };
+      if constexpr (PF) {
+        if (NON * BLOCK < nchunk) {
+          u32x4 ra[U], rb[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int64_t c = c0 + static_cast<int64_t>(u) * BLOCK;
-          if (c < nchunk) {
-            float x[W], g[W];
-            raw[u].unpack(x);
+          for (int u = 0; u < U; ++u) ra[u] = load_slot_last_use(NON * BLOCK + u * BLOCK);
+          for (uint32_t b = NON * BLOCK; b < nchunk; b += 2 * U * BLOCK) {
 #pragma unroll
-            for (int k = 0; k < W; ++k) g[k] = cnt_f * fexp2(__builtin_fmaf(x[k], kL2E, -kl));
-            if (c == ct) {
+            for (int u = 0; u < U; ++u) rb[u] = load_slot_last_use(b + (U + u) * BLOCK);
+            stream2(ra, b);
 #pragma unroll
-              for (int k = 0; k < W; ++k)
-                if (k == kt) g[k] = g_t;
-            }
-            store_chunk<TO, W>(grow, c, g);
+            for (int u = 0; u < U; ++u) ra[u] = load_slot_last_use(b + (2 * U + u) * BLOCK);
+            stream2(rb, b + U * BLOCK);
           }
         }
-      }
-      if (tid < tail) {
-        const int64_t j = nchunk * W + tid;
-        float g;
-        if (j == t) {
-          g = g_t;
-        } else {
-          const float xv = Elem<TI>::load1(zrow, j);
-          g = cnt_f * fexp2(__builtin_fmaf(xv, kL2E, -kl));
+      } else {
+        for (uint32_t b = NON * BLOCK; b < nchunk; b += U * BLOCK) {
+          u32x4 raw[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) raw[u] = load_slot_last_use(b + u * BLOCK);
+          stream2(raw, b);
         }
+      }
+      if (tid < V - tail_begin) {
+        const uint32_t j = tail_begin + tid;
+        const float g = (j == t) ? o.g_t
+                                 : o.cnt * fexp2(__builtin_fmaf(Elem<TI>::load1(zrow, j), kL2E, -o.kl));
         Elem<TO>::store1(grow, j, g);
       }
+      // The target column: written after its chunk by the same lane, so this
+      // store lands last (a lane's stores to one address stay in order).
+      if (mine) Elem<TO>::store1(grow, t, o.g_t);
+    }
+    if constexpr (NLDS > 0) {
+      // The next row's HBM -> LDS copies overwrite the staging slots: every
+      // read of them by this wave must have returned first.
+      __builtin_amdgcn_s_waitcnt(0);
     }
   }
 }
@@ -491,36 +744,60 @@ int device_cus() {
   return n;
 }
 
-template <typename TI, typename TO, int W, int BLOCK, int NRES, int U, bool WRITE>
-ce_status launch_rows(const RowParams& rp, hipStream_t stream) {
-  auto kern = ce_rows_kernel<TI, TO, W, BLOCK, NRES, U, WRITE>;
-  static std::atomic<int> occ{0};
+// Grid: `per_cu` workgroups per compute unit (0: as many as fit), each
+// looping over rows; never more workgroups than rows.
+template <typename Kern>
+ce_status launch_persistent(Kern kern, int block, std::atomic<int>& occ, const RowParams& rp,
+                            hipStream_t stream, int per_cu_cap = 0) {
   int per_cu = occ.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, BLOCK, 0) != hipSuccess || n <= 0)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, block, 0) != hipSuccess || n <= 0)
       return CE_ERR_HIP;
     occ.store(n, std::memory_order_relaxed);
     per_cu = n;
   }
   const int cus = device_cus();
   if (cus <= 0) return CE_ERR_HIP;
+  if (per_cu_cap > 0) per_cu = per_cu_cap;
   const int64_t want = static_cast<int64_t>(cus) * per_cu;
   const int64_t grid = rp.T < want ? rp.T : want;
   if (grid <= 0) return CE_OK;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(BLOCK), 0, stream, rp);
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(block), 0, stream, rp);
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 
+template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
+          bool PF = false, bool EPI1 = false>
+ce_status launch_rows(const RowParams& rp, hipStream_t stream, int per_cu_cap = 0) {
+  static std::atomic<int> occ{0};
+  return launch_persistent(ce_rows_kernel<TI, TO, BLOCK, NRES, NRAW, NLDS, U, WRITE, PF, EPI1>,
+                           BLOCK, occ, rp, stream, per_cu_cap);
+}
+
+template <typename TI, typename TO, bool WRITE>
+ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
+  static std::atomic<int> occ{0};
+  return launch_persistent(ce_rows_scalar_kernel<TI, TO, 256, WRITE>, 256, occ, rp, stream);
+}
+
 // Pick a kernel variant for (input type, output type, vector path or not).
+// Kernel shape by row length (chunks of 16 bytes), measured on MI355X:
+//  * short rows: 256 lanes, both passes streamed (the second read of a row
+//    hits the on-die caches), two load groups in flight per lane;
+//  * medium rows: 512 lanes, 8 slots per lane kept on chip (4 in VGPRs, 4
+//    in LDS), the rest streamed;
+//  * long rows: 1024 lanes, 13 slots per lane on chip (4 VGPR + 9 LDS:
+//    208 KiB of a row), the rest streamed.
+// All use one workgroup per row until the grid reaches 64 per compute unit.
 template <typename TI, typename TO, bool WRITE>
 ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
-  if (!vec) return launch_rows<TI, TO, 1, 256, 0, 8, WRITE>(rp, stream);
-  constexpr int W = Elem<TI>::VEC;
-  // Rows that fit in registers: keep them resident (read once from HBM).
-  const int64_t nchunk = rp.V / W;
-  if (nchunk <= 256 * 4) return launch_rows<TI, TO, W, 256, 4, 4, WRITE>(rp, stream);
-  return launch_rows<TI, TO, W, 256, 0, 4, WRITE>(rp, stream);
+  if (!vec) return launch_rows_scalar<TI, TO, WRITE>(rp, stream);
+  const int64_t nchunk = rp.V / Elem<TI>::VEC;
+  if (nchunk <= 8192) return launch_rows<TI, TO, 256, 0, 0, 0, 4, WRITE, true, true>(rp, stream, 64);
+  if (nchunk <= 16384)
+    return launch_rows<TI, TO, 512, 0, 4, 4, 2, WRITE, true, true>(rp, stream, 64);
+  return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true>(rp, stream, 64);
 }
 
 template <typename TI>
@@ -588,6 +865,7 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_
   if (seg_loss_out && p->num_segments == 0) return CE_ERR_INVALID_ARG;
   if ((p->flags & CE_FLAG_SEGMENT_MEAN) && p->num_segments == 0) return CE_ERR_INVALID_ARG;
   if (T > INT32_MAX) return CE_ERR_UNSUPPORTED;  // segment offsets are int32
+  if (V > (int64_t{1} << 28)) return CE_ERR_UNSUPPORTED;  // in-row byte offsets are 32-bit
   if (T > 0 && (!logits || !targets || !loss_out)) return CE_ERR_INVALID_ARG;
   if (!std::isfinite(z_alpha) || !std::isfinite(grad_scale)) return CE_ERR_INVALID_ARG;
 

@@ -299,6 +299,60 @@ def test_deterministic():
 
 
 # ---------------------------------------------------------------------------
+# Kernel tiers by row length in 16-byte chunks: up to 8192 chunks (256 lanes,
+# both passes streamed), up to 16384 (512 lanes, 4 VGPR + 4 LDS slots per
+# lane), beyond (1024 lanes, 4 VGPR + 9 LDS slots, rest streamed). Targets
+# are placed in each kind of slot: register, LDS, streamed, the row's partial
+# last slot and the tail past the last whole chunk.
+# ---------------------------------------------------------------------------
+
+TIER_CASES = [
+    (torch.bfloat16, 8192 * 8), (torch.bfloat16, 8192 * 8 + 8), (torch.bfloat16, 70001),
+    (torch.bfloat16, 16384 * 8), (torch.bfloat16, 16384 * 8 + 3), (torch.bfloat16, 150000),
+    (torch.float32, 8192 * 4 + 1), (torch.float32, 40000), (torch.float32, 70003),
+]
+
+
+def _tier_targets(V, W):
+    nchunk = V // W
+    lanes = 256 if nchunk <= 8192 else (512 if nchunk <= 16384 else 1024)
+    marks = [0, 1, lanes - 1, lanes, 4 * lanes - 1, 4 * lanes, 8 * lanes - 1, 8 * lanes,
+             13 * lanes - 1, 13 * lanes, 17 * lanes + 5, nchunk - 1]
+    elems = sorted({min(V - 1, c * W + (c % W)) for c in marks if c < max(nchunk, 1)})
+    return elems + [V - 1, V // 2]
+
+
+@pytest.mark.parametrize("dtype,V", TIER_CASES, ids=[f"{d}-{v}".replace("torch.", "") for d, v in TIER_CASES])
+def test_kernel_tiers(dtype, V):
+    W = 4 if dtype == torch.float32 else 8
+    tg = _tier_targets(V, W)
+    T = len(tg) + 2
+    print(f"[parity] tier V={V} {dtype} T={T}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V)
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2.5)
+    t = torch.tensor(tg + [-100, 3], device=DEV)
+    # half the rows confident (collapse regime), so a wrong exclusion of the
+    # target column shows in the NLL
+    for i in range(0, len(tg), 2):
+        z[i, tg[i]] = z[i].max() + 30.0
+    z = z.to(dtype)
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / (T - 1)), what=f"tier V={V}")
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / (T - 1)),
+                grad_dtype=torch.float32 if dtype == torch.bfloat16 else torch.bfloat16,
+                what=f"tier V={V} mixed")
+
+
+def test_many_rows_per_workgroup():
+    """More rows than workgroups: every workgroup loops over several rows."""
+    g = torch.Generator(device=DEV).manual_seed(99)
+    T, V = 40000, 77
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[::7] = -100
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / T), what="many rows")
+
+
+# ---------------------------------------------------------------------------
 # Full sizes, as the benchmark launches them: sampled rows vs the oracle
 # ---------------------------------------------------------------------------
 
