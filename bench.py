@@ -92,6 +92,8 @@ def main():
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=1024,
+                    help="size of the plain device copy timed after the run (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -168,6 +170,28 @@ def main():
     avg_call_ms = sum(per_call_ms) / len(per_call_ms)
     ms_per_step = total_ms / args.steps
 
+    # A plain device-to-device copy of known size, after the timed region:
+    # the same box's practical read+write ceiling, and the calibration kernel
+    # for the HBM byte counters.
+    copy_probe = None
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        c0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / reps
+        copy_probe = {"bytes_read": n, "bytes_written": n, "ms": cms, "GBps": 2 * n / (cms * 1e-3) / 1e9}
+        del src, dst
+
     elems = wl.T * wl.V
     nbytes = alg_bytes(wl)
     achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
@@ -200,6 +224,7 @@ def main():
             "kernel_ms_avg": avg_call_ms, "kernel_ms_median": per_call_ms[len(per_call_ms) // 2],
         },
         "cpu_baseline": cpu,
+        "copy_probe": copy_probe,
         "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)
