@@ -320,6 +320,7 @@ __device__ __forceinline__ void mask_target_slot(u32x4 (&v)[N], uint32_t k, u32x
 //   WRITE  : write the gradient (false = forward only)
 //   PF     : double-buffer the streamed loops (2 U slots in flight per lane)
 //   EPI1   : one wave runs the fp64 epilogue and shares it through LDS
+//   OG     : streamed slots per online (max, sum) update (divides U)
 // Slot i of thread tid is chunk c = i * BLOCK + tid (a chunk is 16 bytes of
 // input). Slots [0, NRES) are exp-resident, then NRAW raw-resident, then NLDS
 // in LDS; later slots are streamed. Loads never branch per lane: a lane past
@@ -327,8 +328,9 @@ __device__ __forceinline__ void mask_target_slot(u32x4 (&v)[N], uint32_t k, u32x
 // by -inf; only stores are predicated, and only in the row's partial slot.
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
-          bool PF, bool EPI1>
+          bool PF, bool EPI1, int OG = U>
 __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
+  static_assert(U % OG == 0, "online groups split the step evenly");
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
   constexpr uint32_t OB = W * Elem<TO>::BYTES;     // gradient bytes per chunk
   constexpr int NON = NRES + NRAW + NLDS;          // on-chip slots per thread
@@ -514,17 +516,20 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 
     // ---- pass 1d: streamed slots, online (shift, sum) ----------------------
     auto stream1 = [&](u32x4 (&raw)[U], uint32_t b) {
-      float x[U * W];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        fix_slot(b + u * BLOCK, raw[u]);
-        if (mine && b + u * BLOCK == st * BLOCK) raw[u] = (raw[u] & and_m) | or_m;
-        float xu[W];
-        Elem<TI>::unpack(raw[u], xu);
+      for (int g0 = 0; g0 < U; g0 += OG) {
+        float x[OG * W];
 #pragma unroll
-        for (int k = 0; k < W; ++k) x[u * W + k] = xu[k];
+        for (int u = g0; u < g0 + OG; ++u) {
+          fix_slot(b + u * BLOCK, raw[u]);
+          if (mine && b + u * BLOCK == st * BLOCK) raw[u] = (raw[u] & and_m) | or_m;
+          float xu[W];
+          Elem<TI>::unpack(raw[u], xu);
+#pragma unroll
+          for (int k = 0; k < W; ++k) x[(u - g0) * W + k] = xu[k];
+        }
+        online_group<OG * W>(mL, s, x);
       }
-      online_group<U * W>(mL, s, x);
     };
     if constexpr (PF) {
       // Two groups in flight: group B's loads run while group A is reduced.
@@ -768,10 +773,10 @@ ce_status launch_persistent(Kern kern, int block, std::atomic<int>& occ, const R
 }
 
 template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
-          bool PF = false, bool EPI1 = false>
+          bool PF = false, bool EPI1 = false, int OG = U>
 ce_status launch_rows(const RowParams& rp, hipStream_t stream, int per_cu_cap = 0) {
   static std::atomic<int> occ{0};
-  return launch_persistent(ce_rows_kernel<TI, TO, BLOCK, NRES, NRAW, NLDS, U, WRITE, PF, EPI1>,
+  return launch_persistent(ce_rows_kernel<TI, TO, BLOCK, NRES, NRAW, NLDS, U, WRITE, PF, EPI1, OG>,
                            BLOCK, occ, rp, stream, per_cu_cap);
 }
 
@@ -788,7 +793,7 @@ ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
 //  * medium rows: 512 lanes, 8 slots per lane kept on chip (4 in VGPRs, 4
 //    in LDS), the rest streamed;
 //  * long rows: 1024 lanes, 13 slots per lane on chip (4 VGPR + 9 LDS:
-//    208 KiB of a row), the rest streamed.
+//    208 KiB of a row), the rest streamed with one online update per slot.
 // All use one workgroup per row until the grid reaches 64 per compute unit.
 template <typename TI, typename TO, bool WRITE>
 ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
@@ -797,7 +802,7 @@ ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   if (nchunk <= 8192) return launch_rows<TI, TO, 256, 0, 0, 0, 4, WRITE, true, true>(rp, stream, 64);
   if (nchunk <= 16384)
     return launch_rows<TI, TO, 512, 0, 4, 4, 2, WRITE, true, true>(rp, stream, 64);
-  return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true>(rp, stream, 64);
+  return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
 }
 
 template <typename TI>
