@@ -94,6 +94,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of the plain device copy timed after the run (0: skip)")
+    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+                    help="fused: one ce_fused_fwd_bwd call per step; split: per-shard statistics, "
+                         "finish, per-shard gradient (the vocabulary-parallel form on one GPU)")
+    ap.add_argument("--shards", type=int, default=2)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -137,13 +141,38 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
+    bounds = L.shard_bounds(wl.V, args.shards, 8 if wl.dtype == "bf16" else 4)
+    split_bufs = []
+    if args.path == "split":
+        for inp, *_ in sets:
+            split_bufs.append((torch.empty((len(bounds), wl.T, 3), dtype=torch.float32, device=dev),
+                               torch.empty((wl.T, 4), dtype=torch.float32, device=dev)))
+    phase_ev = []   # split path: (stats, finish, grad) event triples per step
 
     def step(i):
         inp, loss, grad, seg, ws = sets[i % len(sets)]
-        L.ce_fused_fwd_bwd(inp["logits"], inp["targets"], None, inp["segment_ids"],
-                           inp["z_alpha"], inp["grad_scale"], loss, seg, grad,
-                           num_segments=wl.num_segments, segment_mean=inp["segment_mean"],
-                           workspace=ws, stream=stream.cuda_stream)
+        if args.path == "fused":
+            L.ce_fused_fwd_bwd(inp["logits"], inp["targets"], None, inp["segment_ids"],
+                               inp["z_alpha"], inp["grad_scale"], loss, seg, grad,
+                               num_segments=wl.num_segments, segment_mean=inp["segment_mean"],
+                               workspace=ws, stream=stream.cuda_stream)
+            return
+        stats, row_state = split_bufs[i % len(sets)]
+        z, t = inp["logits"], inp["targets"]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        for k, (a, b) in enumerate(bounds):
+            L.ce_shard_stats(z[:, a:b], t, None, stats[k], v0=a, stream=stream.cuda_stream)
+        ev[1].record(stream)
+        L.ce_rows_finish(len(bounds), stats, t, None, inp["segment_ids"], inp["z_alpha"], loss,
+                         seg, row_state, vocab=wl.V, num_segments=wl.num_segments,
+                         segment_mean=inp["segment_mean"], workspace=ws, stream=stream.cuda_stream)
+        ev[2].record(stream)
+        for a, b in bounds:
+            L.ce_shard_grad(z[:, a:b], t, row_state, inp["grad_scale"], grad[:, a:b], v0=a,
+                            stream=stream.cuda_stream)
+        ev[3].record(stream)
+        phase_ev.append(ev)
 
     for i in range(args.warmup):
         step(i)
@@ -196,6 +225,24 @@ def main():
     nbytes = alg_bytes(wl)
     achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(wl.name)
+    split_info = None
+    if args.path == "split":
+        # The split form reads each valid row twice (statistics, then
+        # gradient); its dominant kernels are the gradient passes.
+        timed = phase_ev[-args.steps:]
+        ms = [sum(e[j].elapsed_time(e[j + 1]) for e in timed) / len(timed) for j in range(3)]
+        b_in = 4 if wl.dtype == "f32" else 2
+        b_out = 4 if wl.grad_torch_dtype == torch.float32 else 2
+        read = wl.n_valid * wl.V * b_in
+        grad_bytes = read + wl.T * wl.V * b_out + 8 * wl.T + 16 * wl.T
+        stats_bytes = read + 8 * wl.T + 12 * wl.T * len(bounds)
+        split_info = {"shards": [list(b) for b in bounds], "stats_ms": ms[0], "finish_ms": ms[1],
+                      "grad_ms": ms[2], "stats_GBps": stats_bytes / (ms[0] * 1e-3) / 1e9,
+                      "grad_GBps": grad_bytes / (ms[2] * 1e-3) / 1e9,
+                      "split_alg_bytes_per_step": stats_bytes + grad_bytes}
+        achieved = grad_bytes / (ms[2] * 1e-3) / 1e9
+        avg_call_ms = ms[2]
+        traffic = None
     out = {
         "metric": METRIC,
         "value": elems / (ms_per_step * 1e-3),
@@ -215,6 +262,7 @@ def main():
             "in_place": wl.grad == "inplace", "z_alpha": wl.z_alpha,
             "ignored_rows": wl.n_masked, "segments": wl.num_segments,
             "rotating_buffer_sets": args.rotate, "alg_bytes_per_step": nbytes,
+            "path": args.path,
         },
         "alg_GBps": nbytes / (ms_per_step * 1e-3) / 1e9,
         "pct_of_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -225,6 +273,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "copy_probe": copy_probe,
+        "split": split_info,
         "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)

@@ -128,6 +128,78 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p,
                            size_t workspace_bytes,
                            void* stream);
 
+/*
+ * Split form: statistics over column shards, a per-row finish, and a
+ * gradient pass from saved per-row state.
+ *
+ * This is the vocabulary-parallel layout of torchtitan PR #5661 "fix softmax
+ * collapse with improved CE perf" (third review, inline diff: each rank
+ * reduces its [T, V_local] shard, the target logit comes from the rank that
+ * owns the target column, and the per-row statistics are combined across
+ * ranks) and its final recompute design (approving review, "What this PR
+ * does": forward saves the input logits and per-row statistics; backward
+ * rebuilds the softmax, puts the precomputed target gradient in the target
+ * slot and scales by the incoming gradient). Fast-LLM PR #552 (PR body,
+ * Approach) shares one softmax pass plus its tensor-parallel reduction the
+ * same way. With one shard it is a forward/backward split of
+ * ce_fused_fwd_bwd: ce_shard_stats + ce_rows_finish forward,
+ * ce_shard_grad backward.
+ */
+
+/* A column shard: columns [v0, v0 + V) of a vocabulary of V_total columns
+ * (V_total is the ce_problem V given to ce_rows_finish). */
+typedef struct ce_shard {
+  int64_t T;              /* rows (T >= 0) */
+  int64_t V;              /* columns held by this shard (V >= 1) */
+  int64_t v0;             /* global index of the shard's first column (>= 0) */
+  int64_t ld_logits;      /* elements between consecutive rows of the shard (>= V) */
+  int64_t ld_grad;        /* elements between consecutive gradient rows (>= V) */
+  int32_t logits_dtype;   /* ce_dtype */
+  int32_t grad_dtype;     /* ce_dtype (gradient pass only) */
+  int64_t ignore_index;
+} ce_shard;
+
+/*
+ * Pass 1 over a shard. For each row, stats[3 r .. 3 r + 2] =
+ *   (m, s, z): with the shard's non-target columns j (the target column is
+ *   excluded when the shard holds it), s = sum_j 2^(z_j log2(e) - m) for a
+ *   float shift m in log2 units (m = -inf, s = 0 when no column remains);
+ *   z = the target logit when the shard holds the target column, else -inf.
+ * Ignored rows (target == ignore_index, or mask byte 0) get (-inf, 0, -inf)
+ * and are not read. stats is a device [T, 3] float array.
+ */
+ce_status ce_shard_stats(const ce_shard* s, const void* logits, const int64_t* targets,
+                         const uint8_t* mask, float* stats, void* stream);
+
+/*
+ * Per-row finish over num_shards shards whose statistics are stored
+ * back to back in stats ([num_shards, T, 3], shard order). p gives T, the
+ * full vocabulary V, ignore_index, num_segments and flags (strides and
+ * dtypes are unused). Writes loss_out[T] and seg_loss_out[S] exactly as
+ * ce_fused_fwd_bwd does, and row_state[T, 4] = (lse log2(e),
+ * (1 + 2 z_alpha lse) * f_r, -sigmoid(LSE_nt - z_t) + 2 z_alpha lse sigmoid(z_t - LSE_nt)
+ * times f_r, kind), f_r = 1 or 1 / segment length under CE_FLAG_SEGMENT_MEAN,
+ * kind = 0 valid, 1 ignored, 2 poisoned (target outside [0, V): NaN loss).
+ * The merge runs in fp64 in shard order (deterministic). workspace as for
+ * ce_fused_fwd_bwd with the same p.
+ */
+ce_status ce_rows_finish(const ce_problem* p, int32_t num_shards, const float* stats,
+                         const int64_t* targets, const uint8_t* mask,
+                         const int32_t* segment_ids, float z_alpha, float* loss_out,
+                         float* seg_loss_out, float* row_state, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * Pass 2 over a shard: grad_out = grad_scale * (row_state factors applied to
+ * exp(z - lse)), the target column (when the shard holds it) set to
+ * grad_scale * the saved target gradient; ignored rows +0.0 and poisoned rows
+ * NaN without reading the logits. grad_out may equal logits (in place, same
+ * dtype and ld); any other overlap is CE_ERR_ALIAS.
+ */
+ce_status ce_shard_grad(const ce_shard* s, const void* logits, const int64_t* targets,
+                        const float* row_state, float grad_scale, void* grad_out,
+                        void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* ce_status_string(int status);
 

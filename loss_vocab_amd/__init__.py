@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     CE_OK,
     CeError,
     CeProblem,
+    CeShard,
     status_string,
 )
 
@@ -121,3 +122,113 @@ def ce_fused(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
                      num_segments=num_segments, segment_mean=segment_mean,
                      ignore_index=ignore_index)
     return loss, grad, seg
+
+
+# ---------------------------------------------------------------------------
+# Split form: per-shard statistics, per-row finish, per-shard gradient.
+# ---------------------------------------------------------------------------
+
+def _stream(t, stream):
+    return int(stream if stream is not None else torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_shard(logits, v0, grad_out=None, ignore_index=IGNORE_INDEX):
+    if logits.dtype not in _DTYPES:
+        raise TypeError(f"logits dtype {logits.dtype} is not float32/bfloat16")
+    T, V = logits.shape
+    s = CeShard()
+    s.T, s.V, s.v0 = T, V, int(v0)
+    s.ld_logits = _rows(logits, "logits")
+    s.logits_dtype = _DTYPES[logits.dtype]
+    if grad_out is not None:
+        if grad_out.dtype not in _DTYPES or tuple(grad_out.shape) != (T, V):
+            raise ValueError("grad_out must be float32/bfloat16 with the shard's shape")
+        s.ld_grad = _rows(grad_out, "grad_out")
+        s.grad_dtype = _DTYPES[grad_out.dtype]
+    else:
+        s.ld_grad, s.grad_dtype = s.ld_logits, s.logits_dtype
+    s.ignore_index = int(ignore_index)
+    return s
+
+
+def ce_shard_stats(logits, targets, mask, stats, *, v0, ignore_index=IGNORE_INDEX, stream=None):
+    """Pass 1 over the column shard ``logits`` = columns [v0, v0 + V) of the
+    vocabulary; writes ``stats`` [T, 3] f32 (shift, sum, target logit)."""
+    sh = make_shard(logits, v0, ignore_index=ignore_index)
+    st = _lib.shard_stats_raw(sh, _ptr(logits), _ptr(targets), _ptr(mask), _ptr(stats),
+                              _stream(logits, stream))
+    if st != CE_OK:
+        raise CeError(st, "ce_shard_stats")
+
+
+def ce_rows_finish(num_shards, stats, targets, mask, segment_ids, z_alpha, loss_out, seg_loss_out,
+                   row_state, *, vocab, num_segments=0, segment_mean=False,
+                   ignore_index=IGNORE_INDEX, workspace=None, stream=None):
+    """Merge ``stats`` [num_shards, T, 3] into loss_out [T], seg_loss_out [S]
+    and row_state [T, 4] for a vocabulary of ``vocab`` columns."""
+    p = CeProblem()
+    p.T, p.V = targets.shape[0], int(vocab)
+    p.ld_logits = p.ld_grad = p.V
+    p.ignore_index = int(ignore_index)
+    p.num_segments = int(num_segments)
+    p.flags = CE_FLAG_SEGMENT_MEAN if segment_mean else 0
+    need = _lib.workspace_bytes(p)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=targets.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.rows_finish_raw(p, num_shards, _ptr(stats), _ptr(targets), _ptr(mask),
+                              _ptr(segment_ids), z_alpha, _ptr(loss_out), _ptr(seg_loss_out),
+                              _ptr(row_state), _ptr(workspace), ws_bytes,
+                              _stream(targets, stream))
+    if st != CE_OK:
+        raise CeError(st, "ce_rows_finish")
+
+
+def ce_shard_grad(logits, targets, row_state, grad_scale, grad_out, *, v0,
+                  ignore_index=IGNORE_INDEX, stream=None):
+    """Pass 2 over a column shard from the saved ``row_state``."""
+    sh = make_shard(logits, v0, grad_out, ignore_index=ignore_index)
+    st = _lib.shard_grad_raw(sh, _ptr(logits), _ptr(targets), _ptr(row_state), grad_scale,
+                             _ptr(grad_out), _stream(logits, stream))
+    if st != CE_OK:
+        raise CeError(st, "ce_shard_grad")
+
+
+def shard_bounds(V, num_shards, align=8):
+    """Contiguous column ranges of ``num_shards`` shards, boundaries rounded to
+    ``align`` columns (so shards of a 16-byte aligned row stay aligned)."""
+    base = -(-V // num_shards)
+    base = -(-base // align) * align
+    out, v = [], 0
+    while v < V:
+        out.append((v, min(V, v + base)))
+        v += base
+    return out
+
+
+def ce_split(logits, targets, *, shards=2, mask=None, segment_ids=None, num_segments=0,
+             z_alpha=0.0, grad_scale=1.0, segment_mean=False, grad_dtype=None, in_place=False,
+             align=8, ignore_index=IGNORE_INDEX):
+    """The split form on one device: the columns of ``logits`` cut into shards,
+    statistics per shard, one finish, gradient per shard.
+
+    Returns ``(loss[T], grad[T, V], seg_loss[S] or None, row_state[T, 4])``.
+    """
+    T, V = logits.shape
+    dev = logits.device
+    bounds = shard_bounds(V, shards, align)
+    stats = torch.empty((len(bounds), T, 3), dtype=torch.float32, device=dev)
+    for k, (a, b) in enumerate(bounds):
+        ce_shard_stats(logits[:, a:b], targets, mask, stats[k], v0=a, ignore_index=ignore_index)
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    seg = (torch.empty(num_segments, dtype=torch.float32, device=dev)
+           if segment_ids is not None else None)
+    row_state = torch.empty((T, 4), dtype=torch.float32, device=dev)
+    ce_rows_finish(len(bounds), stats, targets, mask, segment_ids, z_alpha, loss, seg, row_state,
+                   vocab=V, num_segments=num_segments, segment_mean=segment_mean,
+                   ignore_index=ignore_index)
+    grad = logits if in_place else torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
+    for a, b in bounds:
+        ce_shard_grad(logits[:, a:b], targets, row_state, grad_scale, grad[:, a:b], v0=a,
+                      ignore_index=ignore_index)
+    return loss, grad, seg, row_state

@@ -25,7 +25,8 @@ CE_ERR_HIP = 5
 CE_FLAG_SEGMENT_MEAN = 0x1
 
 # Every symbol include/ce_fused.h declares.
-EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_status_string")
+EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_shard_stats", "ce_rows_finish",
+           "ce_shard_grad", "ce_status_string")
 
 
 class CeProblem(ctypes.Structure):
@@ -39,6 +40,19 @@ class CeProblem(ctypes.Structure):
         ("ignore_index", ctypes.c_int64),
         ("num_segments", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class CeShard(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("v0", ctypes.c_int64),
+        ("ld_logits", ctypes.c_int64),
+        ("ld_grad", ctypes.c_int64),
+        ("logits_dtype", ctypes.c_int32),
+        ("grad_dtype", ctypes.c_int32),
+        ("ignore_index", ctypes.c_int64),
     ]
 
 
@@ -62,6 +76,15 @@ def _load():
         vp, vp, vp, vp, ctypes.c_size_t, vp,
     ]
     lib.ce_fused_fwd_bwd.restype = ctypes.c_int
+    lib.ce_shard_stats.argtypes = [ctypes.POINTER(CeShard), vp, vp, vp, vp, vp]
+    lib.ce_shard_stats.restype = ctypes.c_int
+    lib.ce_rows_finish.argtypes = [
+        ctypes.POINTER(CeProblem), ctypes.c_int32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp,
+        vp, ctypes.c_size_t, vp,
+    ]
+    lib.ce_rows_finish.restype = ctypes.c_int
+    lib.ce_shard_grad.argtypes = [ctypes.POINTER(CeShard), vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.ce_shard_grad.restype = ctypes.c_int
     lib.ce_status_string.argtypes = [ctypes.c_int]
     lib.ce_status_string.restype = ctypes.c_char_p
     return lib
@@ -86,3 +109,22 @@ def call_raw(problem, logits, targets, mask, segment_ids, z_alpha, grad_scale,
         segment_ids or None, float(z_alpha), float(grad_scale), loss_out or None,
         seg_loss_out or None, grad_out or None, workspace or None,
         int(workspace_bytes_), stream or None))
+
+
+def shard_stats_raw(shard, logits, targets, mask, stats, stream):
+    return int(LIB.ce_shard_stats(ctypes.byref(shard), logits or None, targets or None,
+                                  mask or None, stats or None, stream or None))
+
+
+def rows_finish_raw(problem, num_shards, stats, targets, mask, segment_ids, z_alpha, loss_out,
+                    seg_loss_out, row_state, workspace, workspace_bytes_, stream):
+    return int(LIB.ce_rows_finish(
+        ctypes.byref(problem), int(num_shards), stats or None, targets or None, mask or None,
+        segment_ids or None, float(z_alpha), loss_out or None, seg_loss_out or None,
+        row_state or None, workspace or None, int(workspace_bytes_), stream or None))
+
+
+def shard_grad_raw(shard, logits, targets, row_state, grad_scale, grad_out, stream):
+    return int(LIB.ce_shard_grad(ctypes.byref(shard), logits or None, targets or None,
+                                 row_state or None, float(grad_scale), grad_out or None,
+                                 stream or None))

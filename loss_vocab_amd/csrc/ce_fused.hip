@@ -158,7 +158,20 @@ struct RowParams {
   int32_t num_segments;
   int32_t seg_mean;
   float z_alpha, grad_scale;
+  int64_t v0;                // global index of the first column of these rows
+  float* stats;              // statistics mode: [T, 3] (shift, sum, target logit)
+  const float* row_state;    // gradient mode: [T, 4] saved per-row state
 };
+
+// What a row-kernel launch does.
+enum RowMode : int {
+  kFused = 0,   // both passes, loss and gradient
+  kStats = 1,   // pass 1 only: per-row (shift, sum, target logit) of a shard
+  kGrad = 2     // pass 2 only, from a saved per-row state
+};
+
+// Row state kinds stored in the 4th float of a saved row state.
+constexpr float kRowValid = 0.f, kRowIgnored = 1.f, kRowPoisoned = 2.f;
 
 // Per-row results of the epilogue that pass 2 needs.
 struct RowOut {
@@ -172,25 +185,48 @@ struct RowOut {
 // Block-reduced (M, S) of the non-target columns -> loss, NLL, gradient
 // factors, all in fp64 (the NLL of a confident row is ~e^-40 and keeps its
 // relative accuracy only if LSE_nt - z_t is formed in fp64).
+// The per-row loss terms from the non-target logsumexp and the target logit.
+struct RowLoss {
+  double nll;   // softplus(LSE_nt - z_t)
+  double lse;   // logaddexp(LSE_nt, z_t)
+  double p_nt;  // sigmoid(LSE_nt - z_t): probability off the target
+  double p_t;   // sigmoid(z_t - LSE_nt): target probability
+};
+
+__device__ __forceinline__ RowLoss row_loss(double lse_nt, double zt_d) {
+  RowLoss o;
+  const double xx = lse_nt - zt_d;                       // LSE_nt - z_t
+  const double l1p = log1p(exp(-fabs(xx)));
+  o.nll = (xx > 0.0 ? xx : 0.0) + l1p;                   // softplus
+  o.lse = (lse_nt > zt_d ? lse_nt : zt_d) + l1p;         // logaddexp
+  o.p_nt = sigmoid_d(xx);
+  o.p_t = sigmoid_d(-xx);
+  return o;
+}
+
+// LSE_nt from a (shift, sum) partial in log2 units.
+__device__ __forceinline__ double lse_from_partial(double M, double S) {
+  return (M == -HUGE_VAL) ? -HUGE_VAL : M / static_cast<double>(kL2E) + log(S);
+}
+
+// 1 / (rows carrying row r's segment id), or 1.
+__device__ __forceinline__ double segment_factor(const int32_t* seg_ids, const int32_t* seg_start,
+                                                 int32_t num_segments, int64_t r) {
+  int32_t sid = seg_ids[r];
+  sid = sid < 0 ? 0 : (sid >= num_segments ? num_segments - 1 : sid);
+  const int32_t len = seg_start[sid + 1] - seg_start[sid];
+  return 1.0 / static_cast<double>(len > 0 ? len : 1);
+}
+
 __device__ __forceinline__ RowOut row_epilogue(const RowParams& p, int64_t r, float M, float S,
                                                float zt, bool write_loss) {
   const double l2e = static_cast<double>(kL2E);
-  const double lse_nt = (M == kNegInf) ? -HUGE_VAL
-                                       : static_cast<double>(M) / l2e + log(static_cast<double>(S));
-  const double zt_d = static_cast<double>(zt);
-  const double xx = lse_nt - zt_d;                           // LSE_nt - z_t
-  const double l1p = log1p(exp(-fabs(xx)));
-  const double nll = (xx > 0.0 ? xx : 0.0) + l1p;            // softplus
-  const double lse = (lse_nt > zt_d ? lse_nt : zt_d) + l1p;  // logaddexp
-  const double p_nt = sigmoid_d(xx);
-  const double p_t = sigmoid_d(-xx);
+  const RowLoss L = row_loss(lse_from_partial(M == kNegInf ? -HUGE_VAL : static_cast<double>(M),
+                                              static_cast<double>(S)),
+                             static_cast<double>(zt));
+  const double nll = L.nll, lse = L.lse, p_nt = L.p_nt, p_t = L.p_t;
   double scale = static_cast<double>(p.grad_scale);
-  if (p.seg_mean) {
-    int32_t sid = p.seg_ids[r];
-    sid = sid < 0 ? 0 : (sid >= p.num_segments ? p.num_segments - 1 : sid);
-    const int32_t len = p.seg_start[sid + 1] - p.seg_start[sid];
-    scale /= static_cast<double>(len > 0 ? len : 1);
-  }
+  if (p.seg_mean) scale *= segment_factor(p.seg_ids, p.seg_start, p.num_segments, r);
   const double alpha = static_cast<double>(p.z_alpha);
   const double zfac = (alpha == 0.0) ? 0.0 : 2.0 * alpha * lse;
   if (write_loss) {
@@ -233,8 +269,8 @@ __device__ __forceinline__ void block_reduce(float& mL, float& s, float (&red_m)
 // Fill an ignored (0) or poisoned (NaN) gradient row and its loss.
 template <typename TO, int BLOCK>
 __device__ __forceinline__ void fill_row(const RowParams& p, int64_t r, void* grow, uint32_t V,
-                                         float fill, bool write) {
-  if (threadIdx.x == 0) {
+                                         float fill, bool write, bool write_loss = true) {
+  if (write_loss && threadIdx.x == 0) {
     p.loss_out[r] = fill;
     if (p.nll_ws) p.nll_ws[r] = fill;
   }
@@ -253,7 +289,7 @@ __device__ __forceinline__ void fill_row(const RowParams& p, int64_t r, void* gr
 // One-element kernel: rows whose start or stride is not 16-byte aligned.
 // Two streamed passes, one element per lane and step.
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int BLOCK, bool WRITE>
+template <typename TI, typename TO, int BLOCK, bool WRITE, int MODE = kFused>
 __global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
   __shared__ float red_m[2][BLOCK / 64];
   __shared__ float red_s[2][BLOCK / 64];
@@ -264,27 +300,62 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
   int par = 0;
   for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
     const int64_t t64 = p.targets[r];
-    const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
     void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes : nullptr;
-    if (!valid || t64 < 0 || t64 >= static_cast<int64_t>(V)) {
-      fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
-      continue;
-    }
-    const uint32_t t = static_cast<uint32_t>(t64);
-    const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes;
-    const float zt = Elem<TI>::load1(zrow, t);
-    float mL = kNegInf, s = 0.f;
-    for (uint32_t b = 0; b < V; b += 4 * BLOCK) {
-      float x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t j = b + u * BLOCK + tid;
-        x[u] = (j < V && j != t) ? Elem<TI>::load1(zrow, j) : kNegInf;
+    const int64_t tl = t64 - p.v0;
+    const bool owned = tl >= 0 && tl < static_cast<int64_t>(V);
+    RowOut o{};
+    if constexpr (MODE == kGrad) {
+      const float* rs = p.row_state + 4 * r;
+      if (rs[3] != kRowValid) {
+        fill_row<TO, BLOCK>(p, r, grow, V, rs[3] == kRowIgnored ? 0.f : __builtin_nanf(""), true,
+                            false);
+        continue;
       }
-      online_group<4>(mL, s, x);
+      o.kl = rs[0];
+      o.cnt = p.grad_scale * rs[1];
+      o.g_t = p.grad_scale * rs[2];
+    } else {
+      const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+      if constexpr (MODE == kStats) {
+        if (!valid) {
+          if (tid == 0) {
+            p.stats[3 * r] = kNegInf;
+            p.stats[3 * r + 1] = 0.f;
+            p.stats[3 * r + 2] = kNegInf;
+          }
+          continue;
+        }
+      } else if (!valid || !owned) {
+        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
+        continue;
+      }
     }
-    block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
-    const RowOut o = row_epilogue(p, r, mL, s, zt, tid == 0);
+    const uint32_t t = owned ? static_cast<uint32_t>(tl) : V;
+    const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes;
+    if constexpr (MODE != kGrad) {
+      const float zt = owned ? Elem<TI>::load1(zrow, t) : kNegInf;
+      float mL = kNegInf, s = 0.f;
+      for (uint32_t b = 0; b < V; b += 4 * BLOCK) {
+        float x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t j = b + u * BLOCK + tid;
+          x[u] = (j < V && j != t) ? Elem<TI>::load1(zrow, j) : kNegInf;
+        }
+        online_group<4>(mL, s, x);
+      }
+      block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+      if constexpr (MODE == kStats) {
+        if (tid == 0) {
+          p.stats[3 * r] = mL;
+          p.stats[3 * r + 1] = s;
+          p.stats[3 * r + 2] = zt;
+        }
+        continue;
+      } else {
+        o = row_epilogue(p, r, mL, s, zt, tid == 0);
+      }
+    }
     if constexpr (WRITE) {
       for (uint32_t j = tid; j < V; j += BLOCK) {
         const float g = (j == t) ? o.g_t
@@ -328,9 +399,11 @@ __device__ __forceinline__ void mask_target_slot(u32x4 (&v)[N], uint32_t k, u32x
 // by -inf; only stores are predicated, and only in the row's partial slot.
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
-          bool PF, bool EPI1, int OG = U>
+          bool PF, bool EPI1, int OG = U, int MODE = kFused>
 __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   static_assert(U % OG == 0, "online groups split the step evenly");
+  static_assert(MODE != kGrad || (NRES + NRAW + NLDS == 0 && WRITE), "gradient mode streams");
+  static_assert(MODE != kStats || !WRITE, "statistics mode writes no gradient");
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
   constexpr uint32_t OB = W * Elem<TO>::BYTES;     // gradient bytes per chunk
   constexpr int NON = NRES + NRAW + NLDS;          // on-chip slots per thread
@@ -358,18 +431,46 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   int par = 0;
   for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
     const int64_t t64 = p.targets[r];
-    const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
     void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes : nullptr;
-    if (!valid || t64 < 0 || t64 >= static_cast<int64_t>(V)) {
-      // Ignored row: +0.0 everywhere, logits never read. Valid row with an
-      // out-of-range target: NaN loss and gradient row.
-      fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
-      continue;
+    // The target's column within these rows (t_local = V: not among them).
+    const int64_t tl = t64 - p.v0;
+    const bool owned = tl >= 0 && tl < static_cast<int64_t>(V);
+    RowOut saved{};
+    if constexpr (MODE == kGrad) {
+      // The saved state says whether the row is ignored (+0.0), poisoned
+      // (NaN) or carries gradient factors.
+      const float* rs = p.row_state + 4 * r;
+      const float kind = rs[3];
+      if (kind != kRowValid) {
+        fill_row<TO, BLOCK>(p, r, grow, V, kind == kRowIgnored ? 0.f : __builtin_nanf(""), true,
+                            false);
+        continue;
+      }
+      saved.kl = rs[0];
+      saved.cnt = p.grad_scale * rs[1];
+      saved.g_t = p.grad_scale * rs[2];
+    } else {
+      const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+      if constexpr (MODE == kStats) {
+        if (!valid) {
+          if (tid == 0) {
+            p.stats[3 * r] = kNegInf;
+            p.stats[3 * r + 1] = 0.f;
+            p.stats[3 * r + 2] = kNegInf;
+          }
+          continue;
+        }
+      } else if (!valid || !owned) {
+        // Ignored row: +0.0 everywhere, logits never read. Valid row with an
+        // out-of-range target: NaN loss and gradient row.
+        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
+        continue;
+      }
     }
 
-    const uint32_t t = static_cast<uint32_t>(t64);
+    const uint32_t t = owned ? static_cast<uint32_t>(tl) : V;
     const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes;
-    const float zt = Elem<TI>::load1(zrow, t);
+    const float zt = (MODE != kGrad && owned) ? Elem<TI>::load1(zrow, t) : kNegInf;
     const __amdgpu_buffer_rsrc_t rin =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(zrow), 0, nchunk * 16u, kBufWord3);
 
@@ -417,7 +518,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
     // ---- issue every on-chip load first ------------------------------------
     u32x4 rawe[NRES > 0 ? NRES : 1];
     u32x4 rawv[NRAW > 0 ? NRAW : 1];
-    if (nchunk > 0) {
+    if (MODE != kGrad && nchunk > 0) {
 #pragma unroll
       for (int i = 0; i < NRES; ++i) rawe[i] = load_slot_last_use(i * BLOCK);
 #pragma unroll
@@ -531,7 +632,9 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
         online_group<OG * W>(mL, s, x);
       }
     };
-    if constexpr (PF) {
+    if constexpr (MODE == kGrad) {
+      // no pass 1
+    } else if constexpr (PF) {
       // Two groups in flight: group B's loads run while group A is reduced.
       // Loads past the row end are clamped to its last chunk (one broadcast
       // line) and their lanes are -inf, so a trailing empty group is harmless.
@@ -557,15 +660,25 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       }
     }
     // Elements past the last whole chunk: one per lane.
-    if (tid < V - tail_begin) {
+    if (MODE != kGrad && tid < V - tail_begin) {
       const uint32_t j = tail_begin + tid;
       const float xv = (j == t) ? kNegInf : Elem<TI>::load1(zrow, j);
       merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
     }
 
-    block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+    if constexpr (MODE != kGrad) block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+    if constexpr (MODE == kStats) {
+      if (tid == 0) {
+        p.stats[3 * r] = mL;
+        p.stats[3 * r + 1] = s;
+        p.stats[3 * r + 2] = zt;
+      }
+      continue;
+    }
     RowOut o;
-    if constexpr (EPI1) {
+    if constexpr (MODE == kGrad) {
+      o = saved;
+    } else if constexpr (EPI1) {
       // Wave 0 alone runs the fp64 epilogue; the others wait at the barrier,
       // leaving the SIMDs to other workgroups.
       if (wid == 0) {
@@ -726,6 +839,68 @@ __global__ __launch_bounds__(256) void ce_seg_sum_kernel(const float* __restrict
   }
 }
 
+// Merge the (shift, sum, target logit) statistics of P column shards of each
+// row and finish the row: loss, NLL staging for segment sums, and the saved
+// state the gradient pass needs: (lse log2 e, non-target factor, target
+// gradient, kind), the factors already divided by the segment length under
+// the segment-mean flag and still to be multiplied by the upstream scale.
+struct FinishParams {
+  const float* stats;        // [P, T, 3]
+  const int64_t* targets;
+  const uint8_t* mask;
+  const int32_t* seg_ids;
+  const int32_t* seg_start;
+  float* loss_out;
+  float* nll_ws;
+  float* row_state;          // [T, 4]
+  int64_t T, V, ignore_index;
+  int32_t P, num_segments, seg_mean;
+  float z_alpha;
+};
+
+__global__ __launch_bounds__(256) void ce_finish_kernel(FinishParams f) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= f.T) return;
+  const int64_t t = f.targets[r];
+  const bool valid = (t != f.ignore_index) && (f.mask == nullptr || f.mask[r] != 0);
+  float* rs = f.row_state + 4 * r;
+  if (!valid || t < 0 || t >= f.V) {
+    const float fill = valid ? __builtin_nanf("") : 0.f;
+    f.loss_out[r] = fill;
+    if (f.nll_ws) f.nll_ws[r] = fill;
+    rs[0] = 0.f;
+    rs[1] = 0.f;
+    rs[2] = 0.f;
+    rs[3] = valid ? kRowPoisoned : kRowIgnored;
+    return;
+  }
+  // Merge in fp64 in shard order: max shift, rescaled sums, owner's logit.
+  double M = -HUGE_VAL;
+  float zt = kNegInf;
+  for (int k = 0; k < f.P; ++k) {
+    const float* st = f.stats + 3 * (static_cast<int64_t>(k) * f.T + r);
+    M = fmax(M, static_cast<double>(st[0]));
+    zt = fmaxf(zt, st[2]);
+  }
+  double S = 0.0;
+  if (M != -HUGE_VAL) {
+    for (int k = 0; k < f.P; ++k) {
+      const float* st = f.stats + 3 * (static_cast<int64_t>(k) * f.T + r);
+      if (st[0] != kNegInf) S += static_cast<double>(st[1]) * exp2(static_cast<double>(st[0]) - M);
+    }
+  }
+  const RowLoss L = row_loss(lse_from_partial(M, S), static_cast<double>(zt));
+  const double alpha = static_cast<double>(f.z_alpha);
+  const double zfac = (alpha == 0.0) ? 0.0 : 2.0 * alpha * L.lse;
+  const double seg = f.seg_mean ? segment_factor(f.seg_ids, f.seg_start, f.num_segments, r) : 1.0;
+  f.loss_out[r] = static_cast<float>(L.nll + ((alpha == 0.0) ? 0.0 : alpha * L.lse * L.lse));
+  if (f.nll_ws) f.nll_ws[r] = static_cast<float>(L.nll);
+  rs[0] = static_cast<float>(static_cast<double>(kL2E) * L.lse);
+  rs[1] = static_cast<float>(seg * (1.0 + zfac));
+  rs[2] = static_cast<float>(seg * (-L.p_nt + zfac * L.p_t));
+  rs[3] = kRowValid;
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -773,17 +948,18 @@ ce_status launch_persistent(Kern kern, int block, std::atomic<int>& occ, const R
 }
 
 template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
-          bool PF = false, bool EPI1 = false, int OG = U>
+          bool PF = false, bool EPI1 = false, int OG = U, int MODE = kFused>
 ce_status launch_rows(const RowParams& rp, hipStream_t stream, int per_cu_cap = 0) {
   static std::atomic<int> occ{0};
-  return launch_persistent(ce_rows_kernel<TI, TO, BLOCK, NRES, NRAW, NLDS, U, WRITE, PF, EPI1, OG>,
-                           BLOCK, occ, rp, stream, per_cu_cap);
+  return launch_persistent(
+      ce_rows_kernel<TI, TO, BLOCK, NRES, NRAW, NLDS, U, WRITE, PF, EPI1, OG, MODE>, BLOCK, occ,
+      rp, stream, per_cu_cap);
 }
 
-template <typename TI, typename TO, bool WRITE>
+template <typename TI, typename TO, bool WRITE, int MODE = kFused>
 ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
   static std::atomic<int> occ{0};
-  return launch_persistent(ce_rows_scalar_kernel<TI, TO, 256, WRITE>, 256, occ, rp, stream);
+  return launch_persistent(ce_rows_scalar_kernel<TI, TO, 256, WRITE, MODE>, 256, occ, rp, stream);
 }
 
 // Pick a kernel variant for (input type, output type, vector path or not).
@@ -813,6 +989,15 @@ ce_status dispatch_out(const RowParams& rp, int32_t grad_dtype, bool write, bool
   return dispatch_rows<TI, bf16_t, true>(rp, vec, stream);
 }
 
+// Statistics and gradient passes of a shard stream whole rows (nothing is
+// reused between the two calls), so they use the short-row streaming shape.
+template <typename TI, int MODE, typename TO = TI>
+ce_status dispatch_shard(const RowParams& rp, bool vec, hipStream_t stream) {
+  constexpr bool W = MODE == kGrad;
+  if (!vec) return launch_rows_scalar<TI, TO, W, MODE>(rp, stream);
+  return launch_rows<TI, TO, 256, 0, 0, 0, 4, W, true, true, 4, MODE>(rp, stream, 64);
+}
+
 bool ranges_overlap(uintptr_t a0, size_t an, uintptr_t b0, size_t bn) {
   return an && bn && a0 < b0 + bn && b0 < a0 + an;
 }
@@ -822,6 +1007,62 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a != 0 && b > INT64_MAX / a) return false;
   *out = a * b;
   return true;
+}
+
+// Bytes spanned by T rows of V elements at stride ld (false on overflow).
+bool span_bytes(int64_t T, int64_t V, int64_t ld, int bytes, size_t* out) {
+  if (T == 0) {
+    *out = 0;
+    return true;
+  }
+  int64_t tmp = 0;
+  if (!mul_ok(T - 1, ld, &tmp) || tmp > INT64_MAX - V) return false;
+  if (!mul_ok(tmp + V, bytes, &tmp)) return false;
+  *out = static_cast<size_t>(tmp);
+  return true;
+}
+
+bool valid_dtype(int32_t dt) { return dt == CE_DTYPE_F32 || dt == CE_DTYPE_BF16; }
+
+bool rows_vec(const void* ptr, int64_t ld, int bytes) {
+  return (reinterpret_cast<uintptr_t>(ptr) % 16 == 0) && ((ld * bytes) % 16 == 0);
+}
+
+// Launch the segment-offset search (segments present) into the workspace.
+ce_status launch_seg_bounds(const int32_t* segment_ids, int64_t T, int32_t S, void* workspace,
+                            float** nll_ws, int32_t** seg_start, hipStream_t stream) {
+  *nll_ws = static_cast<float*>(workspace);
+  *seg_start = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                          align_up(static_cast<size_t>(T) * sizeof(float)));
+  (void)hipGetLastError();
+  const unsigned nb = static_cast<unsigned>((static_cast<int64_t>(S) + 1 + 255) / 256);
+  hipLaunchKernelGGL(ce_seg_bounds_kernel, dim3(nb), dim3(256), 0, stream, segment_ids, T, S,
+                     *seg_start);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+// Shape checks shared by the shard entry points.
+ce_status check_shard(const ce_shard* s, size_t* in_bytes) {
+  if (s == nullptr) return CE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->V < 1 || s->v0 < 0 || s->ld_logits < s->V) return CE_ERR_INVALID_ARG;
+  if (!valid_dtype(s->logits_dtype)) return CE_ERR_INVALID_ARG;
+  if (s->T > INT32_MAX || s->V > (int64_t{1} << 28)) return CE_ERR_UNSUPPORTED;
+  if (!span_bytes(s->T, s->V, s->ld_logits, dtype_bytes(s->logits_dtype), in_bytes))
+    return CE_ERR_INVALID_ARG;
+  return CE_OK;
+}
+
+RowParams shard_params(const ce_shard* s, const void* logits, const int64_t* targets) {
+  RowParams rp{};
+  rp.logits = logits;
+  rp.targets = targets;
+  rp.T = s->T;
+  rp.V = s->V;
+  rp.ld_in = s->ld_logits;
+  rp.ld_out = s->ld_logits;
+  rp.ignore_index = s->ignore_index;
+  rp.v0 = s->v0;
+  return rp;
 }
 
 }  // namespace
@@ -916,7 +1157,7 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_
   }
 
   if (T > 0) {
-    RowParams rp;
+    RowParams rp{};
     rp.logits = logits;
     rp.grad = grad_out;
     rp.targets = targets;
@@ -953,6 +1194,113 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
   return CE_OK;
+}
+
+ce_status ce_shard_stats(const ce_shard* sh, const void* logits, const int64_t* targets,
+                         const uint8_t* mask, float* stats, void* stream_ptr) {
+  size_t in_bytes = 0;
+  const ce_status chk = check_shard(sh, &in_bytes);
+  if (chk != CE_OK) return chk;
+  if (sh->T == 0) return CE_OK;
+  if (!logits || !targets || !stats) return CE_ERR_INVALID_ARG;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  RowParams rp = shard_params(sh, logits, targets);
+  rp.mask = mask;
+  rp.stats = stats;
+  const bool vec = rows_vec(logits, sh->ld_logits, dtype_bytes(sh->logits_dtype));
+  (void)hipGetLastError();
+  return sh->logits_dtype == CE_DTYPE_F32 ? dispatch_shard<float, kStats>(rp, vec, stream)
+                                          : dispatch_shard<bf16_t, kStats>(rp, vec, stream);
+}
+
+ce_status ce_rows_finish(const ce_problem* p, int32_t num_shards, const float* stats,
+                         const int64_t* targets, const uint8_t* mask, const int32_t* segment_ids,
+                         float z_alpha, float* loss_out, float* seg_loss_out, float* row_state,
+                         void* workspace, size_t workspace_bytes, void* stream_ptr) {
+  if (p == nullptr) return CE_ERR_INVALID_ARG;
+  const int64_t T = p->T;
+  if (T < 0 || p->V < 1 || num_shards < 1) return CE_ERR_INVALID_ARG;
+  if ((p->flags & ~CE_FLAG_SEGMENT_MEAN) != 0 || p->num_segments < 0) return CE_ERR_INVALID_ARG;
+  if (T > 0 && (segment_ids != nullptr) != (p->num_segments > 0)) return CE_ERR_INVALID_ARG;
+  if (T == 0 && segment_ids != nullptr && p->num_segments == 0) return CE_ERR_INVALID_ARG;
+  if (seg_loss_out && p->num_segments == 0) return CE_ERR_INVALID_ARG;
+  if ((p->flags & CE_FLAG_SEGMENT_MEAN) && p->num_segments == 0) return CE_ERR_INVALID_ARG;
+  if (T > INT32_MAX) return CE_ERR_UNSUPPORTED;
+  if (T > 0 && (!stats || !targets || !loss_out || !row_state)) return CE_ERR_INVALID_ARG;
+  if (!std::isfinite(z_alpha)) return CE_ERR_INVALID_ARG;
+  const size_t need = ce_workspace_bytes(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CE_ERR_WORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0) return CE_ERR_WORKSPACE;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const int32_t S = p->num_segments;
+  float* nll_ws = nullptr;
+  int32_t* seg_start = nullptr;
+  if (S > 0) {
+    const ce_status st = launch_seg_bounds(segment_ids, T, S, workspace, &nll_ws, &seg_start, stream);
+    if (st != CE_OK) return st;
+  }
+  if (T > 0) {
+    FinishParams f{};
+    f.stats = stats;
+    f.targets = targets;
+    f.mask = mask;
+    f.seg_ids = segment_ids;
+    f.seg_start = seg_start;
+    f.loss_out = loss_out;
+    f.nll_ws = seg_loss_out ? nll_ws : nullptr;
+    f.row_state = row_state;
+    f.T = T;
+    f.V = p->V;
+    f.ignore_index = p->ignore_index;
+    f.P = num_shards;
+    f.num_segments = S;
+    f.seg_mean = (p->flags & CE_FLAG_SEGMENT_MEAN) ? 1 : 0;
+    f.z_alpha = z_alpha;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ce_finish_kernel, dim3(static_cast<unsigned>((T + 255) / 256)), dim3(256), 0,
+                       stream, f);
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  }
+  if (seg_loss_out) {
+    hipLaunchKernelGGL(ce_seg_sum_kernel, dim3(static_cast<unsigned>(S)), dim3(256), 0, stream,
+                       nll_ws, seg_start, S, seg_loss_out);
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  }
+  return CE_OK;
+}
+
+ce_status ce_shard_grad(const ce_shard* sh, const void* logits, const int64_t* targets,
+                        const float* row_state, float grad_scale, void* grad_out,
+                        void* stream_ptr) {
+  size_t in_bytes = 0, out_bytes = 0;
+  const ce_status chk = check_shard(sh, &in_bytes);
+  if (chk != CE_OK) return chk;
+  if (!valid_dtype(sh->grad_dtype) || sh->ld_grad < sh->V) return CE_ERR_INVALID_ARG;
+  if (!span_bytes(sh->T, sh->V, sh->ld_grad, dtype_bytes(sh->grad_dtype), &out_bytes))
+    return CE_ERR_INVALID_ARG;
+  if (!std::isfinite(grad_scale)) return CE_ERR_INVALID_ARG;
+  if (sh->T == 0) return CE_OK;
+  if (!logits || !targets || !row_state || !grad_out) return CE_ERR_INVALID_ARG;
+  const bool same = grad_out == logits && sh->grad_dtype == sh->logits_dtype &&
+                    sh->ld_grad == sh->ld_logits;
+  if (!same && ranges_overlap(reinterpret_cast<uintptr_t>(logits), in_bytes,
+                              reinterpret_cast<uintptr_t>(grad_out), out_bytes))
+    return CE_ERR_ALIAS;
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  RowParams rp = shard_params(sh, logits, targets);
+  rp.grad = grad_out;
+  rp.ld_out = sh->ld_grad;
+  rp.row_state = row_state;
+  rp.grad_scale = grad_scale;
+  const int bi = dtype_bytes(sh->logits_dtype), bo = dtype_bytes(sh->grad_dtype);
+  const bool vec = rows_vec(logits, sh->ld_logits, bi) && rows_vec(grad_out, sh->ld_grad, bo);
+  (void)hipGetLastError();
+  if (sh->logits_dtype == CE_DTYPE_F32)
+    return sh->grad_dtype == CE_DTYPE_F32 ? dispatch_shard<float, kGrad, float>(rp, vec, stream)
+                                          : dispatch_shard<float, kGrad, bf16_t>(rp, vec, stream);
+  return sh->grad_dtype == CE_DTYPE_F32 ? dispatch_shard<bf16_t, kGrad, float>(rp, vec, stream)
+                                        : dispatch_shard<bf16_t, kGrad, bf16_t>(rp, vec, stream);
 }
 
 }  // extern "C"

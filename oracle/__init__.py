@@ -16,6 +16,7 @@ from .ce_oracle import (  # noqa: F401
     IGNORE_INDEX,
     ce_oracle,
     segment_lengths,
+    shard_nontarget_lse,
     sigmoid,
     softplus,
 )

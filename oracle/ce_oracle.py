@@ -218,3 +218,36 @@ def ce_oracle(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
         "grad": grad, "seg_nll": seg_nll, "seg_loss": seg_loss,
         "mean": mean, "n_valid": n_valid,
     }
+
+
+def shard_nontarget_lse(z_shard, targets, v0, *, mask=None, ignore_index=IGNORE_INDEX):
+    """Per-row statistics of one column shard, in float64.
+
+    A shard holds columns [v0, v0 + V_k) of the vocabulary (torchtitan PR
+    #5661, third review, inline diff: each rank reduces over its own columns;
+    the rank that owns the target column supplies the target logit).
+    Returns ``(lse, zt)``: ``lse[r]`` = log sum of exp over the shard's
+    columns other than the row's target (-inf when none is left or the row is
+    ignored) and ``zt[r]`` = the target logit if the shard holds the target
+    column, else -inf.
+    """
+    z = np.asarray(z_shard, dtype=np.float64)
+    T, Vk = z.shape
+    t = np.asarray(targets, dtype=np.int64).reshape(T)
+    valid = t != ignore_index
+    if mask is not None:
+        valid &= np.asarray(mask).reshape(T) != 0
+    lse = np.full(T, _NEG_INF)
+    zt = np.full(T, _NEG_INF)
+    for r in range(T):
+        if not valid[r]:
+            continue
+        row = z[r].copy()
+        tl = t[r] - v0
+        if 0 <= tl < Vk:
+            zt[r] = row[tl]
+            row[tl] = _NEG_INF
+        m = row.max()
+        if np.isfinite(m) or m > 0:
+            lse[r] = m + np.log(np.exp(row - m).sum())
+    return lse, zt

@@ -289,6 +289,36 @@ def pin_segments(fn):
         _close(out["grad"][r], plain["grad"][r] * (gamma / n), 1e-15, 0, f"seg scale row {r}")
 
 
+def pin_shard_nontarget_lse(shard_fn):
+    """Per-shard non-target logsumexp against 120-digit brute force, and the
+    closed form of a uniform shard."""
+    mpmath.mp.dps = 120
+    rng = np.random.default_rng(8)
+    z = rng.normal(0, 3.0, size=(6, 7))
+    z[2, 3] = 60.0
+    z[4, :] = -np.inf
+    z[4, 5] = 1.0
+    t = np.array([10, 13, 13, 5, 15, -100])   # shard holds columns [10, 17)
+    lse, zt = shard_fn(z, t, 10)
+    for r in range(6):
+        if t[r] == -100:
+            assert lse[r] == -np.inf and zt[r] == -np.inf
+            continue
+        tl = t[r] - 10
+        cols = [j for j in range(7) if j != tl]
+        terms = [mpmath.exp(mpmath.mpf(float(z[r, j]))) for j in cols if np.isfinite(z[r, j])]
+        ref = float(mpmath.log(mpmath.fsum(terms))) if terms else -np.inf
+        _close(lse[r], ref, 1e-14, 0, f"shard lse row {r}")
+        if 0 <= tl < 7:
+            assert zt[r] == z[r, tl]
+        else:
+            assert zt[r] == -np.inf
+    # uniform shard of width 9 holding the target: lse = c + ln 8
+    lse, zt = shard_fn(np.full((1, 9), 2.5), np.array([4]), 0)
+    _close(lse[0], 2.5 + math.log(8.0), 1e-15, 0, "uniform shard")
+    assert zt[0] == 2.5
+
+
 ALL_PINS = [
     pin_margin20,
     pin_collapse_is_avoided,

@@ -40,14 +40,16 @@ def test_library_exports_every_declared_symbol():
         assert name in exported, name
 
 
-def test_struct_layout_matches_header(tmp_path):
+@pytest.mark.parametrize("ctype,pytype", [("ce_problem", "CeProblem"), ("ce_shard", "CeShard")])
+def test_struct_layout_matches_header(tmp_path, ctype, pytype):
     """Compile a C probe with gcc against the header and compare offsets."""
     L = _lib()
-    fields = [f[0] for f in L.CeProblem._fields_]
+    cls = getattr(L, pytype)
+    fields = [f[0] for f in cls._fields_]
     src = tmp_path / "probe.c"
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ce_fused.h"', 'int main(void){',
-             'printf("%zu\\n", sizeof(ce_problem));']
-    lines += [f'printf("%zu\\n", offsetof(ce_problem, {f}));' for f in fields]
+             f'printf("%zu\\n", sizeof({ctype}));']
+    lines += [f'printf("%zu\\n", offsetof({ctype}, {f}));' for f in fields]
     lines += ["return 0;}"]
     src.write_text("\n".join(lines))
     exe = tmp_path / "probe"
@@ -55,9 +57,9 @@ def test_struct_layout_matches_header(tmp_path):
                    check=True)
     vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
                                            check=True).stdout.split()]
-    assert vals[0] == ctypes.sizeof(L.CeProblem)
+    assert vals[0] == ctypes.sizeof(cls)
     for f, off in zip(fields, vals[1:]):
-        assert getattr(L.CeProblem, f).offset == off, f
+        assert getattr(cls, f).offset == off, f
 
 
 def test_status_strings():
@@ -160,3 +162,65 @@ def test_package_does_not_import_the_oracle():
                 with open(os.path.join(dirpath, fn)) as f:
                     text = f.read()
                 assert "oracle" not in text, fn
+
+
+def _shard(T=8, V=100, v0=0, ld=None, ldg=None, dt=0, gdt=0):
+    L = _lib()
+    s = L.CeShard()
+    s.T, s.V, s.v0 = T, V, v0
+    s.ld_logits = V if ld is None else ld
+    s.ld_grad = V if ldg is None else ldg
+    s.logits_dtype, s.grad_dtype = dt, gdt
+    s.ignore_index = -100
+    return s
+
+
+@pytest.mark.parametrize("case,kw,expect", [
+    ("V < 1", dict(V=0), 1),
+    ("negative v0", dict(v0=-1), 1),
+    ("ld < V", dict(ld=50), 1),
+    ("bad dtype", dict(dt=3), 1),
+    ("huge V", dict(V=1 << 29, ld=1 << 29), 2),
+])
+def test_shard_stats_validation(case, kw, expect):
+    st = _lib().shard_stats_raw(_shard(**kw), A_LOGITS, A_TGT, 0, A_LOSS, 0)
+    assert st == expect, case
+
+
+def test_shard_stats_null_pointers():
+    L = _lib()
+    assert L.shard_stats_raw(_shard(), 0, A_TGT, 0, A_LOSS, 0) == 1
+    assert L.shard_stats_raw(_shard(), A_LOGITS, 0, 0, A_LOSS, 0) == 1
+    assert L.shard_stats_raw(_shard(), A_LOGITS, A_TGT, 0, 0, 0) == 1
+    assert L.LIB.ce_shard_stats(None, None, None, None, None, None) == 1
+
+
+@pytest.mark.parametrize("case,kw,grad,expect", [
+    ("no grad", {}, 0, 1),
+    ("bad grad dtype", dict(gdt=5), A_GRAD, 1),
+    ("ld_grad < V", dict(ldg=10), A_GRAD, 1),
+    ("overlap", {}, A_LOGITS + 32, 3),
+    ("in place other dtype", dict(gdt=1), A_LOGITS, 3),
+])
+def test_shard_grad_validation(case, kw, grad, expect):
+    st = _lib().shard_grad_raw(_shard(**kw), A_LOGITS, A_TGT, A_WS, 1.0, grad, 0)
+    assert st == expect, case
+
+
+def test_shard_grad_nonfinite_scale():
+    assert _lib().shard_grad_raw(_shard(), A_LOGITS, A_TGT, A_WS, float("nan"), A_GRAD, 0) == 1
+
+
+@pytest.mark.parametrize("case,pkw,kw,expect", [
+    ("no shards", {}, dict(n=0), 1),
+    ("null stats", {}, dict(stats=0), 1),
+    ("null row state", {}, dict(rs=0), 1),
+    ("segments without ids", dict(S=3), {}, 1),
+    ("workspace missing", dict(S=3), dict(seg=A_SEG), 4),
+    ("bad flag", dict(flags=4), {}, 1),
+])
+def test_rows_finish_validation(case, pkw, kw, expect):
+    p = _problem(**pkw)
+    st = _lib().rows_finish_raw(p, kw.get("n", 2), kw.get("stats", A_LOGITS), A_TGT, 0,
+                                kw.get("seg", 0), 0.0, A_LOSS, 0, kw.get("rs", A_GRAD), 0, 0, 0)
+    assert st == expect, case

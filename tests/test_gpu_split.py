@@ -1,0 +1,171 @@
+"""The split form (per-shard statistics, per-row finish, per-shard gradient)
+against the fp64 oracle on the GPU.
+
+The unique part of a shard's statistics is its non-target logsumexp
+(shift / log2(e) + log(sum)) and the owner's target logit; the float shift
+itself is arbitrary, so only those are compared. The finished losses,
+segment sums and gradients are compared element by element.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import shard_nontarget_lse
+from parity_utils import check_grad, check_loss, check_zero_rows, run_oracle, to_np64
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+L2E_F = float(np.float32(1.4426950408889634))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import loss_vocab_amd  # noqa: F401
+    yield
+    torch.cuda.empty_cache()
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+CASES = [
+    # (dtype, T, V, shards, align, alpha, segments)
+    (torch.bfloat16, 40, 3001, 1, 8, 1e-4, 0),
+    (torch.bfloat16, 40, 3001, 2, 8, 1e-4, 0),
+    (torch.bfloat16, 33, 20011, 3, 8, 0.0, 5),
+    (torch.float32, 33, 9999, 4, 4, 1e-3, 0),
+    (torch.bfloat16, 25, 1003, 3, 1, 1e-4, 0),    # unaligned shard starts: one-element kernel
+    (torch.float32, 25, 777, 5, 1, 0.0, 4),
+    (torch.bfloat16, 12, 70001, 2, 8, 1e-4, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,T,V,shards,align,alpha,S", CASES,
+                         ids=[f"{c[0]}-T{c[1]}-V{c[2]}-P{c[3]}-a{c[4]}".replace("torch.", "") for c in CASES])
+def test_split_matches_oracle(dtype, T, V, shards, align, alpha, S):
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(V + shards)
+    z = torch.randn(T, V, generator=g, device=DEV) * 2.5
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    bounds = L.shard_bounds(V, shards, align)
+    # targets at shard edges, confident rows, ignored rows
+    for i, (a, b) in enumerate(bounds):
+        if 2 * i + 1 < T:
+            t[2 * i] = a
+            t[2 * i + 1] = b - 1
+    z[3, t[3]] = z[3].max() + 35.0
+    z[5, t[5]] = z[5].max() + 18.0
+    t[T - 1] = -100
+    z = z.to(dtype)
+    seg = None
+    if S:
+        seg = torch.sort(torch.randint(0, S, (T,), generator=g, device=DEV)).values.to(torch.int32)
+    gamma = 1.0 / (T - 1)
+    z64 = to_np64(z)
+    loss, grad, segsum, row_state = L.ce_split(z, t, shards=shards, segment_ids=seg, num_segments=S,
+                                               z_alpha=alpha, grad_scale=gamma,
+                                               segment_mean=S > 0, align=align)
+    torch.cuda.synchronize()
+    ref = run_oracle(z64, _np(t), segment_ids=_np(seg), num_segments=S, z_alpha=alpha,
+                     grad_scale=gamma, segment_mean=S > 0)
+    check_loss(_np(loss), ref["loss"], "split loss")
+    check_grad(to_np64(grad), ref["grad"], dtype, "split grad")
+    inv = torch.as_tensor(~ref["valid"], device=DEV)
+    check_zero_rows(loss[inv], grad[inv])
+    if S:
+        check_loss(_np(segsum), ref["seg_nll"], "split seg")
+    rs = _np(row_state)
+    assert np.all(rs[~ref["valid"], 3] == 1.0) and np.all(rs[ref["valid"], 3] == 0.0)
+
+
+@pytest.mark.parametrize("dtype,align", [(torch.bfloat16, 8), (torch.float32, 4), (torch.bfloat16, 1)])
+def test_shard_stats_unique_part(dtype, align):
+    """shift / log2(e) + log(sum) is the shard's non-target logsumexp; the
+    third value is the target logit in the owning shard and -inf elsewhere."""
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(17)
+    T, V = 30, 5003
+    z = (torch.randn(T, V, generator=g, device=DEV) * 3).to(dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[4] = -100
+    mask = torch.ones(T, dtype=torch.uint8, device=DEV)
+    mask[7] = 0
+    for a, b in L.shard_bounds(V, 3, align):
+        st = torch.empty(T, 3, device=DEV)
+        L.ce_shard_stats(z[:, a:b], t, mask, st, v0=a)
+        torch.cuda.synchronize()
+        st = st.double().cpu().numpy()
+        lse_ref, zt_ref = shard_nontarget_lse(to_np64(z[:, a:b]), _np(t), a, mask=_np(mask))
+        lse = np.where(st[:, 0] == -np.inf, -np.inf, st[:, 0] / L2E_F + np.log(np.maximum(st[:, 1], 1e-300)))
+        fin = np.isfinite(lse_ref)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.all(np.abs(lse[fin] - lse_ref[fin]) <= 2e-6 * np.maximum(1.0, np.abs(lse_ref[fin])))
+        assert np.array_equal(st[:, 2], zt_ref)
+
+
+def test_backward_scale_is_applied_at_gradient_time():
+    """One saved row state, two upstream scales: gradients scale exactly."""
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(5)
+    T, V = 20, 4001
+    z = torch.randn(T, V, generator=g, device=DEV)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    _, g1, _, rs = L.ce_split(z, t, shards=2, z_alpha=1e-3, grad_scale=0.25, align=4)
+    g2 = torch.empty_like(g1)
+    for a, b in L.shard_bounds(V, 2, 4):
+        L.ce_shard_grad(z[:, a:b], t, rs, 0.5, g2[:, a:b], v0=a)
+    torch.cuda.synchronize()
+    assert torch.equal(g2, 2 * g1)
+
+
+def test_split_in_place_and_forward_agrees_with_fused():
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(6)
+    T, V = 64, 32000
+    z = (torch.randn(T, V, generator=g, device=DEV) * 3).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[::9] = -100
+    loss_f, grad_f, _ = L.ce_fused(z, t, z_alpha=1e-4, grad_scale=1 / 57)
+    zc = z.clone()
+    loss_s, grad_s, _, _ = L.ce_split(zc, t, shards=2, z_alpha=1e-4, grad_scale=1 / 57, in_place=True)
+    torch.cuda.synchronize()
+    assert grad_s.data_ptr() == zc.data_ptr()
+    ref = run_oracle(to_np64(z), _np(t), z_alpha=1e-4, grad_scale=1 / 57)
+    check_loss(_np(loss_s), ref["loss"])
+    check_grad(to_np64(grad_s), ref["grad"], torch.bfloat16)
+    # the two forms agree closely (different summation orders)
+    assert torch.allclose(loss_s, loss_f, rtol=2e-6, atol=0)
+
+
+def test_split_pages_share_full_size():
+    """The pages' measured shape, T = 16384, V = 128256 bf16, in two shards of
+    64128 columns (one tensor-parallel rank's share each): sampled rows vs the
+    oracle, and ignored rows exactly zero."""
+    import loss_vocab_amd as L
+    wl = WORKLOADS["ce_bf16_T16384_V128256_zipf_inplace"]
+    print("[split] full size", flush=True)
+    inp = make_inputs(wl, device=DEV)
+    T, V = wl.T, wl.V
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(T, size=24, replace=False))
+    ri = torch.as_tensor(rows, device=DEV)
+    z_rows = to_np64(inp["logits"][ri])
+    loss, grad, _, _ = L.ce_split(inp["logits"], inp["targets"], shards=2, z_alpha=1e-4,
+                                  grad_scale=inp["grad_scale"], grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    t_np = _np(inp["targets"])
+    ref = run_oracle(z_rows, t_np[rows], z_alpha=1e-4, grad_scale=inp["grad_scale"])
+    check_loss(_np(loss)[rows], ref["loss"], "split full loss")
+    check_grad(to_np64(grad[ri]), ref["grad"], torch.bfloat16, "split full grad")
+    inv = torch.as_tensor(t_np == -100, device=DEV)
+    check_zero_rows(loss[inv], grad[inv])
+    del inp, grad
+    torch.cuda.empty_cache()

@@ -10,7 +10,7 @@ import torch
 import oracle
 from oracle import ce_oracle
 
-from oracle_pins import ALL_PINS, GOLDEN
+from oracle_pins import ALL_PINS, GOLDEN, pin_shard_nontarget_lse
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -18,6 +18,24 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
 def test_pin(pin):
     pin(ce_oracle)
+
+
+def test_pin_shard_nontarget_lse():
+    pin_shard_nontarget_lse(oracle.shard_nontarget_lse)
+
+
+def test_shard_lses_merge_to_the_row():
+    """Merging the shards' non-target logsumexps with the owner's target logit
+    (log-add) gives the full row's lse of the oracle."""
+    rng = np.random.default_rng(3)
+    z = rng.normal(0, 2.0, size=(5, 50))
+    t = rng.integers(0, 50, size=5)
+    full = ce_oracle(z, t)
+    parts = [oracle.shard_nontarget_lse(z[:, a:b], t, a) for a, b in [(0, 16), (16, 40), (40, 50)]]
+    lse_nt = np.logaddexp.reduce(np.stack([p[0] for p in parts]), axis=0)
+    zt = np.max(np.stack([p[1] for p in parts]), axis=0)
+    assert np.allclose(np.logaddexp(lse_nt, zt), full["lse"], rtol=1e-14, atol=0)
+    assert np.array_equal(zt, z[np.arange(5), t])
 
 
 def test_naive_fp32_collapses_where_the_pages_say():
