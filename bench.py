@@ -146,7 +146,7 @@ def main():
     if args.path == "split":
         for inp, *_ in sets:
             split_bufs.append((torch.empty((len(bounds), wl.T, 3), dtype=torch.float32, device=dev),
-                               torch.empty((wl.T, 4), dtype=torch.float32, device=dev)))
+                               torch.empty((wl.T, 8), dtype=torch.float32, device=dev)))
     phase_ev = []   # split path: (stats, finish, grad) event triples per step
 
     def step(i):

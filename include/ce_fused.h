@@ -176,10 +176,14 @@ ce_status ce_shard_stats(const ce_shard* s, const void* logits, const int64_t* t
  * back to back in stats ([num_shards, T, 3], shard order). p gives T, the
  * full vocabulary V, ignore_index, num_segments and flags (strides and
  * dtypes are unused). Writes loss_out[T] and seg_loss_out[S] exactly as
- * ce_fused_fwd_bwd does, and row_state[T, 4] = (lse log2(e),
- * (1 + 2 z_alpha lse) * f_r, -sigmoid(LSE_nt - z_t) + 2 z_alpha lse sigmoid(z_t - LSE_nt)
- * times f_r, kind), f_r = 1 or 1 / segment length under CE_FLAG_SEGMENT_MEAN,
- * kind = 0 valid, 1 ignored, 2 poisoned (target outside [0, V): NaN loss).
+ * ce_fused_fwd_bwd does, and the saved per-row state row_state[T, 8]:
+ *   [0] lse * log2(e)
+ *   [1] p_nt = sigmoid(LSE_nt - z_t)      (probability off the target)
+ *   [2] p_t  = sigmoid(z_t - LSE_nt)      (target probability)
+ *   [3] 2 z_alpha lse                    (z-loss gradient factor)
+ *   [4] f_r = 1 / segment length under CE_FLAG_SEGMENT_MEAN, else 1
+ *   [5] kind: 0 valid, 1 ignored, 2 poisoned (target outside [0, V): NaN loss)
+ *   [6..7] 0.
  * The merge runs in fp64 in shard order (deterministic). workspace as for
  * ce_fused_fwd_bwd with the same p.
  */
@@ -190,15 +194,24 @@ ce_status ce_rows_finish(const ce_problem* p, int32_t num_shards, const float* s
                          size_t workspace_bytes, void* stream);
 
 /*
- * Pass 2 over a shard: grad_out = grad_scale * (row_state factors applied to
- * exp(z - lse)), the target column (when the shard holds it) set to
- * grad_scale * the saved target gradient; ignored rows +0.0 and poisoned rows
- * NaN without reading the logits. grad_out may equal logits (in place, same
- * dtype and ld); any other overlap is CE_ERR_ALIAS.
+ * Pass 2 over a shard from the saved row state. With w_r the weight of row
+ * r's NLL term -- row_weight[r] when row_weight is given, else
+ * grad_scale * f_r -- and u_r = grad_scale * f_r the weight of its z-loss
+ * term, the gradient is
+ *   g_rj = (w_r + u_r 2 z_alpha lse) exp(z_rj - lse)          j != t
+ *   g_rt = -w_r p_nt + u_r 2 z_alpha lse p_t,
+ * so with row_weight == NULL it equals ce_fused_fwd_bwd's gradient.
+ * row_weight lets per-row weights chosen after the forward -- the seam of a
+ * GSPO/GRPO-style loss that shares this softmax, Fast-LLM PR #552 "Fuse GSPO
+ * into the monolithic compiled loss" (PR body, Approach: a deferred child
+ * whose backward runs after an eager per-segment step) -- scale the NLL
+ * gradient row by row. Ignored rows are +0.0 and poisoned rows NaN without
+ * reading the logits. grad_out may equal logits (in place, same dtype and
+ * ld); any other overlap is CE_ERR_ALIAS.
  */
 ce_status ce_shard_grad(const ce_shard* s, const void* logits, const int64_t* targets,
-                        const float* row_state, float grad_scale, void* grad_out,
-                        void* stream);
+                        const float* row_state, const float* row_weight, float grad_scale,
+                        void* grad_out, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* ce_status_string(int status);

@@ -165,7 +165,7 @@ def ce_rows_finish(num_shards, stats, targets, mask, segment_ids, z_alpha, loss_
                    row_state, *, vocab, num_segments=0, segment_mean=False,
                    ignore_index=IGNORE_INDEX, workspace=None, stream=None):
     """Merge ``stats`` [num_shards, T, 3] into loss_out [T], seg_loss_out [S]
-    and row_state [T, 4] for a vocabulary of ``vocab`` columns."""
+    and row_state [T, 8] for a vocabulary of ``vocab`` columns."""
     p = CeProblem()
     p.T, p.V = targets.shape[0], int(vocab)
     p.ld_logits = p.ld_grad = p.V
@@ -184,12 +184,13 @@ def ce_rows_finish(num_shards, stats, targets, mask, segment_ids, z_alpha, loss_
         raise CeError(st, "ce_rows_finish")
 
 
-def ce_shard_grad(logits, targets, row_state, grad_scale, grad_out, *, v0,
+def ce_shard_grad(logits, targets, row_state, grad_scale, grad_out, *, v0, row_weight=None,
                   ignore_index=IGNORE_INDEX, stream=None):
-    """Pass 2 over a column shard from the saved ``row_state``."""
+    """Pass 2 over a column shard from the saved ``row_state``; ``row_weight``
+    [T] f32 (optional) weights each row's NLL gradient."""
     sh = make_shard(logits, v0, grad_out, ignore_index=ignore_index)
-    st = _lib.shard_grad_raw(sh, _ptr(logits), _ptr(targets), _ptr(row_state), grad_scale,
-                             _ptr(grad_out), _stream(logits, stream))
+    st = _lib.shard_grad_raw(sh, _ptr(logits), _ptr(targets), _ptr(row_state), _ptr(row_weight),
+                             grad_scale, _ptr(grad_out), _stream(logits, stream))
     if st != CE_OK:
         raise CeError(st, "ce_shard_grad")
 
@@ -208,11 +209,11 @@ def shard_bounds(V, num_shards, align=8):
 
 def ce_split(logits, targets, *, shards=2, mask=None, segment_ids=None, num_segments=0,
              z_alpha=0.0, grad_scale=1.0, segment_mean=False, grad_dtype=None, in_place=False,
-             align=8, ignore_index=IGNORE_INDEX):
+             align=8, row_weight=None, ignore_index=IGNORE_INDEX):
     """The split form on one device: the columns of ``logits`` cut into shards,
     statistics per shard, one finish, gradient per shard.
 
-    Returns ``(loss[T], grad[T, V], seg_loss[S] or None, row_state[T, 4])``.
+    Returns ``(loss[T], grad[T, V], seg_loss[S] or None, row_state[T, 8])``.
     """
     T, V = logits.shape
     dev = logits.device
@@ -223,12 +224,12 @@ def ce_split(logits, targets, *, shards=2, mask=None, segment_ids=None, num_segm
     loss = torch.empty(T, dtype=torch.float32, device=dev)
     seg = (torch.empty(num_segments, dtype=torch.float32, device=dev)
            if segment_ids is not None else None)
-    row_state = torch.empty((T, 4), dtype=torch.float32, device=dev)
+    row_state = torch.empty((T, _lib.ROW_STATE), dtype=torch.float32, device=dev)
     ce_rows_finish(len(bounds), stats, targets, mask, segment_ids, z_alpha, loss, seg, row_state,
                    vocab=V, num_segments=num_segments, segment_mean=segment_mean,
                    ignore_index=ignore_index)
     grad = logits if in_place else torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
     for a, b in bounds:
         ce_shard_grad(logits[:, a:b], targets, row_state, grad_scale, grad[:, a:b], v0=a,
-                      ignore_index=ignore_index)
+                      row_weight=row_weight, ignore_index=ignore_index)
     return loss, grad, seg, row_state

@@ -24,6 +24,8 @@ CE_ERR_HIP = 5
 
 CE_FLAG_SEGMENT_MEAN = 0x1
 
+ROW_STATE = 8   # floats of saved state per row (ce_rows_finish)
+
 # Every symbol include/ce_fused.h declares.
 EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_shard_stats", "ce_rows_finish",
            "ce_shard_grad", "ce_status_string")
@@ -83,7 +85,7 @@ def _load():
         vp, ctypes.c_size_t, vp,
     ]
     lib.ce_rows_finish.restype = ctypes.c_int
-    lib.ce_shard_grad.argtypes = [ctypes.POINTER(CeShard), vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.ce_shard_grad.argtypes = [ctypes.POINTER(CeShard), vp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.ce_shard_grad.restype = ctypes.c_int
     lib.ce_status_string.argtypes = [ctypes.c_int]
     lib.ce_status_string.restype = ctypes.c_char_p
@@ -124,7 +126,7 @@ def rows_finish_raw(problem, num_shards, stats, targets, mask, segment_ids, z_al
         row_state or None, workspace or None, int(workspace_bytes_), stream or None))
 
 
-def shard_grad_raw(shard, logits, targets, row_state, grad_scale, grad_out, stream):
+def shard_grad_raw(shard, logits, targets, row_state, row_weight, grad_scale, grad_out, stream):
     return int(LIB.ce_shard_grad(ctypes.byref(shard), logits or None, targets or None,
-                                 row_state or None, float(grad_scale), grad_out or None,
-                                 stream or None))
+                                 row_state or None, row_weight or None, float(grad_scale),
+                                 grad_out or None, stream or None))

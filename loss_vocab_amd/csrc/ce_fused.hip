@@ -160,7 +160,8 @@ struct RowParams {
   float z_alpha, grad_scale;
   int64_t v0;                // global index of the first column of these rows
   float* stats;              // statistics mode: [T, 3] (shift, sum, target logit)
-  const float* row_state;    // gradient mode: [T, 4] saved per-row state
+  const float* row_state;    // gradient mode: [T, kRowState] saved per-row state
+  const float* row_weight;   // gradient mode: [T] weights of the NLL term, or null
 };
 
 // What a row-kernel launch does.
@@ -170,8 +171,12 @@ enum RowMode : int {
   kGrad = 2     // pass 2 only, from a saved per-row state
 };
 
-// Row state kinds stored in the 4th float of a saved row state.
+// Saved per-row state: kRowState floats per row,
+//   [0] lse log2(e)   [1] p_nt = sigmoid(LSE_nt - z_t)   [2] p_t = sigmoid(z_t - LSE_nt)
+//   [3] 2 alpha lse   [4] segment factor (1 / length, or 1)   [5] kind   [6..7] zero
+constexpr int kRowState = 8;
 constexpr float kRowValid = 0.f, kRowIgnored = 1.f, kRowPoisoned = 2.f;
+
 
 // Per-row results of the epilogue that pass 2 needs.
 struct RowOut {
@@ -185,6 +190,19 @@ struct RowOut {
 // Block-reduced (M, S) of the non-target columns -> loss, NLL, gradient
 // factors, all in fp64 (the NLL of a confident row is ~e^-40 and keeps its
 // relative accuracy only if LSE_nt - z_t is formed in fp64).
+// Gradient factors of a saved row: the NLL term weighted by w (the row's
+// weight, or grad_scale * segment factor), the z-loss term by grad_scale *
+// segment factor.
+__device__ __forceinline__ RowOut saved_row(const RowParams& p, const float* rs, int64_t r) {
+  const float zw = p.grad_scale * rs[4];
+  const float w = p.row_weight ? p.row_weight[r] : zw;
+  RowOut o{};
+  o.kl = rs[0];
+  o.cnt = w + zw * rs[3];
+  o.g_t = -w * rs[1] + zw * rs[3] * rs[2];
+  return o;
+}
+
 // The per-row loss terms from the non-target logsumexp and the target logit.
 struct RowLoss {
   double nll;   // softplus(LSE_nt - z_t)
@@ -305,15 +323,13 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
     const bool owned = tl >= 0 && tl < static_cast<int64_t>(V);
     RowOut o{};
     if constexpr (MODE == kGrad) {
-      const float* rs = p.row_state + 4 * r;
-      if (rs[3] != kRowValid) {
-        fill_row<TO, BLOCK>(p, r, grow, V, rs[3] == kRowIgnored ? 0.f : __builtin_nanf(""), true,
+      const float* rs = p.row_state + kRowState * r;
+      if (rs[5] != kRowValid) {
+        fill_row<TO, BLOCK>(p, r, grow, V, rs[5] == kRowIgnored ? 0.f : __builtin_nanf(""), true,
                             false);
         continue;
       }
-      o.kl = rs[0];
-      o.cnt = p.grad_scale * rs[1];
-      o.g_t = p.grad_scale * rs[2];
+      o = saved_row(p, rs, r);
     } else {
       const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
       if constexpr (MODE == kStats) {
@@ -426,7 +442,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   const size_t in_row_bytes = static_cast<size_t>(p.ld_in) * Elem<TI>::BYTES;
   const size_t out_row_bytes = static_cast<size_t>(p.ld_out) * Elem<TO>::BYTES;
   const uint32_t neg_w = Elem<TI>::NEG_INF_WORD;
-  const u32x4 neg4 = {neg_w, neg_w, neg_w, neg_w};
+  [[maybe_unused]] const u32x4 neg4 = {neg_w, neg_w, neg_w, neg_w};
 
   int par = 0;
   for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
@@ -439,16 +455,14 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
     if constexpr (MODE == kGrad) {
       // The saved state says whether the row is ignored (+0.0), poisoned
       // (NaN) or carries gradient factors.
-      const float* rs = p.row_state + 4 * r;
-      const float kind = rs[3];
+      const float* rs = p.row_state + kRowState * r;
+      const float kind = rs[5];
       if (kind != kRowValid) {
         fill_row<TO, BLOCK>(p, r, grow, V, kind == kRowIgnored ? 0.f : __builtin_nanf(""), true,
                             false);
         continue;
       }
-      saved.kl = rs[0];
-      saved.cnt = p.grad_scale * rs[1];
-      saved.g_t = p.grad_scale * rs[2];
+      saved = saved_row(p, rs, r);
     } else {
       const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
       if constexpr (MODE == kStats) {
@@ -841,9 +855,7 @@ __global__ __launch_bounds__(256) void ce_seg_sum_kernel(const float* __restrict
 
 // Merge the (shift, sum, target logit) statistics of P column shards of each
 // row and finish the row: loss, NLL staging for segment sums, and the saved
-// state the gradient pass needs: (lse log2 e, non-target factor, target
-// gradient, kind), the factors already divided by the segment length under
-// the segment-mean flag and still to be multiplied by the upstream scale.
+// state the gradient pass needs (kRowState floats, laid out above).
 struct FinishParams {
   const float* stats;        // [P, T, 3]
   const int64_t* targets;
@@ -852,7 +864,7 @@ struct FinishParams {
   const int32_t* seg_start;
   float* loss_out;
   float* nll_ws;
-  float* row_state;          // [T, 4]
+  float* row_state;          // [T, kRowState]
   int64_t T, V, ignore_index;
   int32_t P, num_segments, seg_mean;
   float z_alpha;
@@ -863,15 +875,14 @@ __global__ __launch_bounds__(256) void ce_finish_kernel(FinishParams f) {
   if (r >= f.T) return;
   const int64_t t = f.targets[r];
   const bool valid = (t != f.ignore_index) && (f.mask == nullptr || f.mask[r] != 0);
-  float* rs = f.row_state + 4 * r;
+  float* rs = f.row_state + kRowState * r;
   if (!valid || t < 0 || t >= f.V) {
     const float fill = valid ? __builtin_nanf("") : 0.f;
     f.loss_out[r] = fill;
     if (f.nll_ws) f.nll_ws[r] = fill;
-    rs[0] = 0.f;
-    rs[1] = 0.f;
-    rs[2] = 0.f;
-    rs[3] = valid ? kRowPoisoned : kRowIgnored;
+#pragma unroll
+    for (int k = 0; k < kRowState; ++k) rs[k] = 0.f;
+    rs[5] = valid ? kRowPoisoned : kRowIgnored;
     return;
   }
   // Merge in fp64 in shard order: max shift, rescaled sums, owner's logit.
@@ -896,9 +907,13 @@ __global__ __launch_bounds__(256) void ce_finish_kernel(FinishParams f) {
   f.loss_out[r] = static_cast<float>(L.nll + ((alpha == 0.0) ? 0.0 : alpha * L.lse * L.lse));
   if (f.nll_ws) f.nll_ws[r] = static_cast<float>(L.nll);
   rs[0] = static_cast<float>(static_cast<double>(kL2E) * L.lse);
-  rs[1] = static_cast<float>(seg * (1.0 + zfac));
-  rs[2] = static_cast<float>(seg * (-L.p_nt + zfac * L.p_t));
-  rs[3] = kRowValid;
+  rs[1] = static_cast<float>(L.p_nt);
+  rs[2] = static_cast<float>(L.p_t);
+  rs[3] = static_cast<float>(zfac);
+  rs[4] = static_cast<float>(seg);
+  rs[5] = kRowValid;
+  rs[6] = 0.f;
+  rs[7] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -1271,8 +1286,8 @@ ce_status ce_rows_finish(const ce_problem* p, int32_t num_shards, const float* s
 }
 
 ce_status ce_shard_grad(const ce_shard* sh, const void* logits, const int64_t* targets,
-                        const float* row_state, float grad_scale, void* grad_out,
-                        void* stream_ptr) {
+                        const float* row_state, const float* row_weight, float grad_scale,
+                        void* grad_out, void* stream_ptr) {
   size_t in_bytes = 0, out_bytes = 0;
   const ce_status chk = check_shard(sh, &in_bytes);
   if (chk != CE_OK) return chk;
@@ -1292,6 +1307,7 @@ ce_status ce_shard_grad(const ce_shard* sh, const void* logits, const int64_t* t
   rp.grad = grad_out;
   rp.ld_out = sh->ld_grad;
   rp.row_state = row_state;
+  rp.row_weight = row_weight;
   rp.grad_scale = grad_scale;
   const int bi = dtype_bytes(sh->logits_dtype), bo = dtype_bytes(sh->grad_dtype);
   const bool vec = rows_vec(logits, sh->ld_logits, bi) && rows_vec(grad_out, sh->ld_grad, bo);

@@ -84,11 +84,12 @@ def segment_lengths(segment_ids, num_segments):
     return np.bincount(ids, minlength=num_segments)[:num_segments].astype(np.int64)
 
 
-def _row_block(z, t, valid, z_alpha, scale, want_grad):
+def _row_block(z, t, valid, z_alpha, scale, want_grad, weight=None):
     """Loss pieces and gradient for one block of rows, all in float64.
 
     z: [R, V] float64 logits; t: [R] int64 targets; valid: [R] bool;
-    scale: [R] float64 per-row gradient scale.
+    scale: [R] float64 per-row gradient scale; weight: [R] weights of the
+    NLL term's gradient (None: the scale).
     """
     R, V = z.shape
     in_range = (t >= 0) & (t < V)
@@ -136,21 +137,23 @@ def _row_block(z, t, valid, z_alpha, scale, want_grad):
     if want_grad:
         grad = np.zeros((R, V), dtype=np.float64)
         sc = scale[rows]
-        # Non-target columns: softmax probability times the shared factor of
-        # CE and z-loss, scale * (1 + 2 alpha lse).
+        w = sc if weight is None else weight[rows]   # weight of the NLL gradient
+        zl = sc * 2.0 * z_alpha * lse                # weight of the softmax in the z-loss gradient
+        # Non-target columns: softmax probability times the NLL weight plus
+        # the z-loss factor.
         with np.errstate(invalid="ignore", over="ignore"):
             p = np.exp(z_nt - lse[:, None])
-        g = (sc * (1.0 + 2.0 * z_alpha * lse))[:, None] * p
-        # Target column: the CE part is p_t - 1 = -p_nt exactly (torchtitan
+        g = (w + zl)[:, None] * p
+        # Target column: the NLL part is p_t - 1 = -p_nt exactly (torchtitan
         # #5661, Numerics, "target gradient"); the z-loss part is 2 alpha lse p_t.
-        g[np.arange(rows.size), tl] = sc * (-p_nt + 2.0 * z_alpha * lse * p_t)
+        g[np.arange(rows.size), tl] = -w * p_nt + zl * p_t
         grad[rows] = g
         grad[bad] = np.nan
     return loss, nll_all, lse_all, grad
 
 
 def ce_oracle(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
-              z_alpha=0.0, grad_scale=1.0, segment_mean=False,
+              z_alpha=0.0, grad_scale=1.0, segment_mean=False, row_weight=None,
               ignore_index=IGNORE_INDEX, want_grad=True, block_rows=256):
     """Fused CE (+ z-loss) forward and backward over a [T, V] logit matrix.
 
@@ -164,6 +167,10 @@ def ce_oracle(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
     z_alpha : z-loss weight alpha
     grad_scale : gamma, the upstream gradient factor (e.g. 1 / n_valid)
     segment_mean : divide row r's gradient scale by the length of its segment
+    row_weight : optional [T] weights of each row's NLL gradient, chosen after
+        the forward (a GSPO/GRPO-style child sharing the softmax: Fast-LLM
+        #552, PR body, Approach); the z-loss gradient keeps the row's scale.
+        The loss values do not depend on it.
 
     Returns a dict with float64 arrays
     ``loss[T]`` (NLL + alpha lse^2, 0 for ignored rows), ``nll[T]``, ``lse[T]``,
@@ -194,8 +201,9 @@ def ce_oracle(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
     for r0 in range(0, T, block_rows):
         r1 = min(T, r0 + block_rows)
         zb = z_all[r0:r1].astype(np.float64)
+        wb = None if row_weight is None else np.asarray(row_weight, dtype=np.float64)[r0:r1]
         lb, nb, eb, gb = _row_block(zb, t_all[r0:r1], valid[r0:r1],
-                                    float(z_alpha), scale[r0:r1], want_grad)
+                                    float(z_alpha), scale[r0:r1], want_grad, wb)
         loss[r0:r1] = lb
         nll[r0:r1] = nb
         lse[r0:r1] = eb

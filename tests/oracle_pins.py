@@ -205,6 +205,27 @@ def pin_torch_library(fn):
     _close(out["mean"], float(per_row.detach().sum() / valid.sum()), 1e-12, 0, "torch mean")
 
 
+def pin_row_weights(fn):
+    """Per-row NLL weights chosen after the forward: torch fp64 autograd of
+    sum_r w_r CE_r + gamma alpha lse_r^2 (the z-loss keeps the uniform scale)."""
+    g = torch.Generator().manual_seed(21)
+    T, V = 10, 33
+    z = torch.randn(T, V, generator=g, dtype=torch.float64) * 2.0
+    t = torch.randint(0, V, (T,), generator=g)
+    t[4] = IGNORE
+    w = torch.randn(T, generator=g, dtype=torch.float64)
+    alpha, gamma = 5e-3, 0.3
+    valid = (t != IGNORE).double()
+    zr = z.clone().requires_grad_(True)
+    ce = torch.nn.functional.cross_entropy(zr, t, reduction="none", ignore_index=IGNORE)
+    total = (w * ce).sum() + gamma * (alpha * torch.logsumexp(zr, dim=1) ** 2 * valid).sum()
+    total.backward()
+    out = fn(z.numpy(), t.numpy(), z_alpha=alpha, grad_scale=gamma, row_weight=w.numpy())
+    _close(out["grad"], zr.grad.numpy(), 1e-10, 1e-18, "row-weight grad")
+    plain = fn(z.numpy(), t.numpy(), z_alpha=alpha, grad_scale=gamma)
+    assert np.array_equal(out["loss"], plain["loss"])
+
+
 # ---------------------------------------------------------------------------
 # Invariants, masking, segments
 # ---------------------------------------------------------------------------
@@ -326,6 +347,7 @@ ALL_PINS = [
     pin_single_column_and_infinities,
     pin_mpmath_bruteforce,
     pin_torch_library,
+    pin_row_weights,
     pin_row_sums,
     pin_masking,
     pin_out_of_range_target,

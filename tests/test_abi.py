@@ -203,12 +203,12 @@ def test_shard_stats_null_pointers():
     ("in place other dtype", dict(gdt=1), A_LOGITS, 3),
 ])
 def test_shard_grad_validation(case, kw, grad, expect):
-    st = _lib().shard_grad_raw(_shard(**kw), A_LOGITS, A_TGT, A_WS, 1.0, grad, 0)
+    st = _lib().shard_grad_raw(_shard(**kw), A_LOGITS, A_TGT, A_WS, 0, 1.0, grad, 0)
     assert st == expect, case
 
 
 def test_shard_grad_nonfinite_scale():
-    assert _lib().shard_grad_raw(_shard(), A_LOGITS, A_TGT, A_WS, float("nan"), A_GRAD, 0) == 1
+    assert _lib().shard_grad_raw(_shard(), A_LOGITS, A_TGT, A_WS, 0, float("nan"), A_GRAD, 0) == 1
 
 
 @pytest.mark.parametrize("case,pkw,kw,expect", [

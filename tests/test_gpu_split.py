@@ -83,7 +83,7 @@ def test_split_matches_oracle(dtype, T, V, shards, align, alpha, S):
     if S:
         check_loss(_np(segsum), ref["seg_nll"], "split seg")
     rs = _np(row_state)
-    assert np.all(rs[~ref["valid"], 3] == 1.0) and np.all(rs[ref["valid"], 3] == 0.0)
+    assert np.all(rs[~ref["valid"], 5] == 1.0) and np.all(rs[ref["valid"], 5] == 0.0)
 
 
 @pytest.mark.parametrize("dtype,align", [(torch.bfloat16, 8), (torch.float32, 4), (torch.bfloat16, 1)])
@@ -169,3 +169,33 @@ def test_split_pages_share_full_size():
     check_zero_rows(loss[inv], grad[inv])
     del inp, grad
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype,shards", [(torch.bfloat16, 2), (torch.float32, 3)])
+def test_weighted_backward(dtype, shards):
+    """A deferred child sharing the softmax: forward (statistics + finish with
+    per-segment NLL sums), then per-row weights fixed between forward and
+    backward (here seeded per-segment weights broadcast to their rows, as a
+    GSPO-style seam would produce), then the weighted gradient."""
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(31 + shards)
+    T, V, S = 200, 5003, 8
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[[3, 50, 51]] = -100
+    seg = torch.sort(torch.randint(0, S, (T,), generator=g, device=DEV)).values.to(torch.int32)
+    w_seg = torch.randn(S, generator=torch.Generator().manual_seed(7), dtype=torch.float32)
+    w_row = w_seg.to(DEV)[seg.long()].contiguous()
+    alpha, gamma = 1e-3, 0.5
+    loss, grad, segsum, rs = L.ce_split(z, t, shards=shards, segment_ids=seg, num_segments=S,
+                                        z_alpha=alpha, grad_scale=gamma, row_weight=w_row,
+                                        align=8 if dtype == torch.bfloat16 else 4)
+    torch.cuda.synchronize()
+    ref = run_oracle(to_np64(z), _np(t), segment_ids=_np(seg), num_segments=S, z_alpha=alpha,
+                     grad_scale=gamma)
+    ref_w = __import__("oracle").ce_oracle(to_np64(z), _np(t), segment_ids=_np(seg),
+                                           num_segments=S, z_alpha=alpha, grad_scale=gamma,
+                                           row_weight=_np(w_row).astype(np.float64))
+    check_loss(_np(loss), ref["loss"], "weighted loss")
+    check_loss(_np(segsum), ref["seg_nll"], "weighted seg")
+    check_grad(to_np64(grad), ref_w["grad"], dtype, "weighted grad")

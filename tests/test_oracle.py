@@ -81,14 +81,16 @@ MUTANTS = [
      "loss[rows] = nll + z_alpha * lse * lse", "loss[rows] = nll"),
     ("z-loss not squared", "loss[rows] = nll + z_alpha * lse * lse",
      "loss[rows] = nll + z_alpha * lse"),
-    ("z-loss factor on non-targets halved",
-     "(1.0 + 2.0 * z_alpha * lse)", "(1.0 + z_alpha * lse)"),
+    ("z-loss gradient factor halved",
+     "zl = sc * 2.0 * z_alpha * lse", "zl = sc * z_alpha * lse"),
     ("z-loss gradient on the target loses p_t",
-     "-p_nt + 2.0 * z_alpha * lse * p_t", "-p_nt + 2.0 * z_alpha * lse"),
-    ("target gradient sign flipped",
-     "-p_nt + 2.0 * z_alpha * lse * p_t", "p_nt + 2.0 * z_alpha * lse * p_t"),
+     "-w * p_nt + zl * p_t", "-w * p_nt + zl"),
+    ("target gradient sign flipped", "-w * p_nt + zl * p_t", "w * p_nt + zl * p_t"),
     ("target gradient uses p_t instead of -p_nt",
-     "-p_nt + 2.0 * z_alpha * lse * p_t", "-p_t + 2.0 * z_alpha * lse * p_t"),
+     "-w * p_nt + zl * p_t", "-w * p_t + zl * p_t"),
+    ("z-loss gradient weighted by the row weight",
+     "zl = sc * 2.0 * z_alpha * lse", "zl = w * 2.0 * z_alpha * lse"),
+    ("row weight ignored", "w = sc if weight is None else weight[rows]", "w = sc"),
     ("gradient not scaled", "sc = scale[rows]", "sc = np.ones(rows.size)"),
     ("mask array ignored", "valid &= np.asarray(mask).reshape(T) != 0", "pass"),
     ("segment scale multiplies by the length",
