@@ -129,6 +129,40 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p,
                            void* stream);
 
 /*
+ * Forward only, with per-row statistics a caller may want from the same read
+ * of the logits: the full logsumexp and the entropy of the row's softmax.
+ * torchtitan PR #5661 "fix softmax collapse with improved CE perf" (fourth
+ * review, inline diff) keeps the input logits unmodified because callers
+ * reuse them for such quantities, entropy named among them; this entry
+ * computes them in the loss pass instead of a second read.
+ *
+ *  p, logits, targets, mask, segment_ids, z_alpha, loss_out, seg_loss_out,
+ *  workspace, stream: as for ce_fused_fwd_bwd (p->grad_dtype and p->ld_grad
+ *                are not used; the logits are never written).
+ *  lse_out       [T] float or NULL: logsumexp_j z_j (all columns) of valid
+ *                rows, +0.0 for ignored rows, NaN for a valid row whose
+ *                target is outside [0, V).
+ *  entropy_out   [T] float or NULL: -sum_j p_j ln p_j of the row's softmax
+ *                (0 ln 0 = 0), formed without cancellation: the target's
+ *                term as p_t NLL_r, every other term as p_j (lse - z_j) >= 0.
+ *                +0.0 for ignored rows, NaN for out-of-range targets.
+ *  Neither output may overlap the logits (CE_ERR_ALIAS).
+ */
+ce_status ce_fused_forward(const ce_problem* p,
+                           const void* logits,
+                           const int64_t* targets,
+                           const uint8_t* mask,
+                           const int32_t* segment_ids,
+                           float z_alpha,
+                           float* loss_out,
+                           float* seg_loss_out,
+                           float* lse_out,
+                           float* entropy_out,
+                           void* workspace,
+                           size_t workspace_bytes,
+                           void* stream);
+
+/*
  * Split form: statistics over column shards, a per-row finish, and a
  * gradient pass from saved per-row state.
  *

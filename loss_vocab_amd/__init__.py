@@ -124,6 +124,49 @@ def ce_fused(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
     return loss, grad, seg
 
 
+def ce_fused_forward(logits, targets, mask, segment_ids, z_alpha, loss_out, seg_loss_out,
+                     lse_out, entropy_out, *, num_segments=0, ignore_index=IGNORE_INDEX,
+                     workspace=None, stream=None):
+    """Same-named wrapper of the forward-only C entry point: loss_out [T] f32,
+    seg_loss_out [S] f32 or None, lse_out / entropy_out [T] f32 or None."""
+    p = make_problem(logits, num_segments=num_segments, ignore_index=ignore_index)
+    for name, t, dt in (("targets", targets, torch.int64), ("mask", mask, torch.uint8),
+                        ("segment_ids", segment_ids, torch.int32),
+                        ("loss_out", loss_out, torch.float32),
+                        ("seg_loss_out", seg_loss_out, torch.float32),
+                        ("lse_out", lse_out, torch.float32),
+                        ("entropy_out", entropy_out, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous {dt} tensor")
+    need = _lib.workspace_bytes(p)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.forward_raw(p, _ptr(logits), _ptr(targets), _ptr(mask), _ptr(segment_ids), z_alpha,
+                          _ptr(loss_out), _ptr(seg_loss_out), _ptr(lse_out), _ptr(entropy_out),
+                          _ptr(workspace), ws_bytes, _stream(logits, stream))
+    if st != CE_OK:
+        raise CeError(st, "ce_fused_forward")
+
+
+def ce_forward(logits, targets, *, mask=None, segment_ids=None, num_segments=0, z_alpha=0.0,
+               entropy=True, ignore_index=IGNORE_INDEX):
+    """Allocate and run the forward-only call.
+
+    Returns ``(loss[T], lse[T], entropy[T] or None, seg_loss[S] or None)``.
+    """
+    T = logits.shape[0]
+    dev = logits.device
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    ent = torch.empty(T, dtype=torch.float32, device=dev) if entropy else None
+    seg = (torch.empty(num_segments, dtype=torch.float32, device=dev)
+           if segment_ids is not None else None)
+    ce_fused_forward(logits, targets, mask, segment_ids, z_alpha, loss, seg, lse, ent,
+                     num_segments=num_segments, ignore_index=ignore_index)
+    return loss, lse, ent, seg
+
+
 # ---------------------------------------------------------------------------
 # Split form: per-shard statistics, per-row finish, per-shard gradient.
 # ---------------------------------------------------------------------------

@@ -27,8 +27,8 @@ CE_FLAG_SEGMENT_MEAN = 0x1
 ROW_STATE = 8   # floats of saved state per row (ce_rows_finish)
 
 # Every symbol include/ce_fused.h declares.
-EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_shard_stats", "ce_rows_finish",
-           "ce_shard_grad", "ce_status_string")
+EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_fused_forward", "ce_shard_stats",
+           "ce_rows_finish", "ce_shard_grad", "ce_status_string")
 
 
 class CeProblem(ctypes.Structure):
@@ -67,7 +67,7 @@ class CeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m loss_vocab_amd.build` "
+            f"{LIB_PATH} is not built; run `python loss_vocab_amd/build.py` "
             "(the fused CE has no CPU fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     vp = ctypes.c_void_p
@@ -78,6 +78,11 @@ def _load():
         vp, vp, vp, vp, ctypes.c_size_t, vp,
     ]
     lib.ce_fused_fwd_bwd.restype = ctypes.c_int
+    lib.ce_fused_forward.argtypes = [
+        ctypes.POINTER(CeProblem), vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+        ctypes.c_size_t, vp,
+    ]
+    lib.ce_fused_forward.restype = ctypes.c_int
     lib.ce_shard_stats.argtypes = [ctypes.POINTER(CeShard), vp, vp, vp, vp, vp]
     lib.ce_shard_stats.restype = ctypes.c_int
     lib.ce_rows_finish.argtypes = [
@@ -111,6 +116,16 @@ def call_raw(problem, logits, targets, mask, segment_ids, z_alpha, grad_scale,
         segment_ids or None, float(z_alpha), float(grad_scale), loss_out or None,
         seg_loss_out or None, grad_out or None, workspace or None,
         int(workspace_bytes_), stream or None))
+
+
+def forward_raw(problem, logits, targets, mask, segment_ids, z_alpha, loss_out, seg_loss_out,
+                lse_out, entropy_out, workspace, workspace_bytes_, stream):
+    """Call ce_fused_forward with integer addresses (0 = NULL); returns the status."""
+    return int(LIB.ce_fused_forward(
+        ctypes.byref(problem), logits or None, targets or None, mask or None,
+        segment_ids or None, float(z_alpha), loss_out or None, seg_loss_out or None,
+        lse_out or None, entropy_out or None, workspace or None, int(workspace_bytes_),
+        stream or None))
 
 
 def shard_stats_raw(shard, logits, targets, mask, stats, stream):

@@ -1,8 +1,9 @@
 """Build the in-tree HIP library ``libce_fused.so`` for gfx950.
 
-Run ``python -m loss_vocab_amd.build`` (or ``__graft_entry__.build()``). The
-library is compiled by hipcc straight from ``csrc/ce_fused.hip``; it needs no
-GPU to build.
+Run ``python loss_vocab_amd/build.py`` (or ``__graft_entry__.build()``); not
+``python -m``, which imports the package and with it the library this builds.
+The library is compiled by hipcc straight from ``csrc/ce_fused.hip``; it needs
+no GPU to build. This file imports nothing of the package.
 """
 
 from __future__ import annotations

@@ -139,6 +139,52 @@ __device__ __forceinline__ void online_group(float& mL, float& s, const float* x
   mL = mn;
 }
 
+// Entropy partials (m, s, u): s = sum 2^d_j and u = sum 2^d_j d_j with
+// d_j = y_j - m, y_j the value in log2 units. Rebasing to a shift M >= m
+// multiplies both by 2^(m - M) and adds (m - M) s to u.
+__device__ __forceinline__ void rebase3(float m, float& s, float& u, float M) {
+  if (s == 0.f) {
+    u = 0.f;
+    return;
+  }
+  const float dm = m - M;
+  const float f = fexp2(dm);
+  u = f * (u + dm * s);
+  s *= f;
+}
+
+__device__ __forceinline__ void merge3(float& m, float& s, float& u, float m2, float s2, float u2) {
+  const float mn = fmaxf(m, m2);
+  const float sh = (mn == kNegInf) ? 0.f : mn;
+  rebase3(m, s, u, sh);
+  rebase3(m2, s2, u2, sh);
+  s += s2;
+  u += u2;
+  m = (mn == kNegInf) ? kNegInf : sh;
+}
+
+template <int G>
+__device__ __forceinline__ void online_group3(float& mL, float& s, float& u, const float* x) {
+  float gmax = kNegInf;
+#pragma unroll
+  for (int k = 0; k < G; ++k) gmax = fmaxf(gmax, x[k]);
+  const float mn = fmaxf(mL, gmax * kL2E);
+  const float sh = (mn == kNegInf) ? 0.f : mn;
+  float acc = 0.f, accu = 0.f;
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    // d <= -256 gives e = 0 and e d = 0 (no -inf * 0)
+    const float d = fmaxf(__builtin_fmaf(x[k], kL2E, -sh), -256.f);
+    const float e = fexp2(d);
+    acc += e;
+    accu = __builtin_fmaf(e, d, accu);
+  }
+  rebase3(mL, s, u, sh);
+  s += acc;
+  u += accu;
+  mL = (mn == kNegInf) ? kNegInf : sh;
+}
+
 __device__ __forceinline__ double sigmoid_d(double x) {
   if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
   const double e = exp(x);
@@ -162,6 +208,8 @@ struct RowParams {
   float* stats;              // statistics mode: [T, 3] (shift, sum, target logit)
   const float* row_state;    // gradient mode: [T, kRowState] saved per-row state
   const float* row_weight;   // gradient mode: [T] weights of the NLL term, or null
+  float* lse_out;            // optional [T] full logsumexp
+  float* ent_out;            // optional [T] softmax entropy (entropy variant only)
 };
 
 // What a row-kernel launch does.
@@ -251,6 +299,7 @@ __device__ __forceinline__ RowOut row_epilogue(const RowParams& p, int64_t r, fl
     const double loss = nll + ((alpha == 0.0) ? 0.0 : alpha * lse * lse);
     p.loss_out[r] = static_cast<float>(loss);
     if (p.nll_ws) p.nll_ws[r] = static_cast<float>(nll);
+    if (p.lse_out) p.lse_out[r] = static_cast<float>(lse);
   }
   RowOut o;
   o.cnt_d = scale * (1.0 + zfac);
@@ -284,6 +333,50 @@ __device__ __forceinline__ void block_reduce(float& mL, float& s, float (&red_m)
   s = S;
 }
 
+// The same for entropy partials (m, s, u).
+template <int BLOCK>
+__device__ __forceinline__ void block_reduce3(float& mL, float& s, float& u,
+                                              float (&red_m)[2][BLOCK / 64],
+                                              float (&red_s)[2][BLOCK / 64],
+                                              float (&red_u)[2][BLOCK / 64], int par,
+                                              uint32_t lane, uint32_t wid) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(mL, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    const float u2 = __shfl_xor(u, off, 64);
+    merge3(mL, s, u, m2, s2, u2);
+  }
+  if (lane == 0) {
+    red_m[par][wid] = mL;
+    red_s[par][wid] = s;
+    red_u[par][wid] = u;
+  }
+  __syncthreads();
+  float M = red_m[par][0], S = red_s[par][0], Uu = red_u[par][0];
+#pragma unroll
+  for (int w = 1; w < BLOCK / 64; ++w) merge3(M, S, Uu, red_m[par][w], red_s[par][w], red_u[par][w]);
+  mL = M;
+  s = S;
+  u = Uu;
+}
+
+// Softmax entropy from the non-target partial (M, S, U) and the target
+// logit, in fp64: H = p_t NLL + ln2 2^(M - L2) ((L2 - M) S - U), L2 = lse
+// log2(e). Every term is >= 0, so a confident row (H ~ p_nt) keeps its
+// relative accuracy.
+__device__ __forceinline__ float row_entropy(float M, float S, float U, float zt) {
+  const double Md = M == kNegInf ? -HUGE_VAL : static_cast<double>(M);
+  const RowLoss L = row_loss(lse_from_partial(Md, static_cast<double>(S)), static_cast<double>(zt));
+  double h = (L.p_t > 0.0) ? L.p_t * L.nll : 0.0;
+  if (Md != -HUGE_VAL && S > 0.f) {
+    const double L2 = static_cast<double>(kL2E) * L.lse;
+    h += 0.6931471805599453 * exp2(Md - L2) * ((L2 - Md) * static_cast<double>(S) -
+                                                static_cast<double>(U));
+  }
+  return static_cast<float>(h);
+}
+
 // Fill an ignored (0) or poisoned (NaN) gradient row and its loss.
 template <typename TO, int BLOCK>
 __device__ __forceinline__ void fill_row(const RowParams& p, int64_t r, void* grow, uint32_t V,
@@ -291,6 +384,8 @@ __device__ __forceinline__ void fill_row(const RowParams& p, int64_t r, void* gr
   if (write_loss && threadIdx.x == 0) {
     p.loss_out[r] = fill;
     if (p.nll_ws) p.nll_ws[r] = fill;
+    if (p.lse_out) p.lse_out[r] = fill;
+    if (p.ent_out) p.ent_out[r] = fill;
   }
   if (!write) return;
   constexpr int VEC = Elem<TO>::VEC;
@@ -307,10 +402,12 @@ __device__ __forceinline__ void fill_row(const RowParams& p, int64_t r, void* gr
 // One-element kernel: rows whose start or stride is not 16-byte aligned.
 // Two streamed passes, one element per lane and step.
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int BLOCK, bool WRITE, int MODE = kFused>
+template <typename TI, typename TO, int BLOCK, bool WRITE, int MODE = kFused, bool ENT = false>
 __global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
+  static_assert(!ENT || (MODE == kFused && !WRITE), "the entropy variant is a forward");
   __shared__ float red_m[2][BLOCK / 64];
   __shared__ float red_s[2][BLOCK / 64];
+  __shared__ float red_u[ENT ? 2 : 1][ENT ? BLOCK / 64 : 1];
   const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
   const uint32_t V = static_cast<uint32_t>(p.V);
   const size_t in_row_bytes = static_cast<size_t>(p.ld_in) * Elem<TI>::BYTES;
@@ -351,6 +448,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
     if constexpr (MODE != kGrad) {
       const float zt = owned ? Elem<TI>::load1(zrow, t) : kNegInf;
       float mL = kNegInf, s = 0.f;
+      [[maybe_unused]] float hs = 0.f;
       for (uint32_t b = 0; b < V; b += 4 * BLOCK) {
         float x[4];
 #pragma unroll
@@ -358,9 +456,18 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
           const uint32_t j = b + u * BLOCK + tid;
           x[u] = (j < V && j != t) ? Elem<TI>::load1(zrow, j) : kNegInf;
         }
-        online_group<4>(mL, s, x);
+        if constexpr (ENT) {
+          online_group3<4>(mL, s, hs, x);
+        } else {
+          online_group<4>(mL, s, x);
+        }
       }
-      block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+      if constexpr (ENT) {
+        block_reduce3<BLOCK>(mL, s, hs, red_m, red_s, red_u, par, lane, wid);
+        if (tid == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
+      } else {
+        block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+      }
       if constexpr (MODE == kStats) {
         if (tid == 0) {
           p.stats[3 * r] = mL;
@@ -408,6 +515,7 @@ __device__ __forceinline__ void mask_target_slot(u32x4 (&v)[N], uint32_t k, u32x
 //   PF     : double-buffer the streamed loops (2 U slots in flight per lane)
 //   EPI1   : one wave runs the fp64 epilogue and shares it through LDS
 //   OG     : streamed slots per online (max, sum) update (divides U)
+//   ENT    : also accumulate sum e d for the softmax entropy (forward only)
 // Slot i of thread tid is chunk c = i * BLOCK + tid (a chunk is 16 bytes of
 // input). Slots [0, NRES) are exp-resident, then NRAW raw-resident, then NLDS
 // in LDS; later slots are streamed. Loads never branch per lane: a lane past
@@ -415,9 +523,11 @@ __device__ __forceinline__ void mask_target_slot(u32x4 (&v)[N], uint32_t k, u32x
 // by -inf; only stores are predicated, and only in the row's partial slot.
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
-          bool PF, bool EPI1, int OG = U, int MODE = kFused>
+          bool PF, bool EPI1, int OG = U, int MODE = kFused, bool ENT = false>
 __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   static_assert(U % OG == 0, "online groups split the step evenly");
+  static_assert(!ENT || (MODE == kFused && !WRITE && NRES + NRAW + NLDS == 0),
+                "the entropy variant is a streamed forward");
   static_assert(MODE != kGrad || (NRES + NRAW + NLDS == 0 && WRITE), "gradient mode streams");
   static_assert(MODE != kStats || !WRITE, "statistics mode writes no gradient");
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
@@ -426,6 +536,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   static_assert(BLOCK % 64 == 0, "whole waves");
   __shared__ float red_m[2][BLOCK / 64];
   __shared__ float red_s[2][BLOCK / 64];
+  __shared__ float red_u[ENT ? 2 : 1][ENT ? BLOCK / 64 : 1];
   __shared__ u32x4 stage[NLDS > 0 ? NLDS : 1][NLDS > 0 ? BLOCK : 1];
   __shared__ float epi[2][4];
 
@@ -551,6 +662,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
     }
 
     float mL = kNegInf, s = 0.f;
+    [[maybe_unused]] float hs = 0.f;   // entropy variant: sum e d
 
     // ---- pass 1a: exp-resident slots ---------------------------------------
     float e[NRES > 0 ? NRES : 1][W];
@@ -643,7 +755,11 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 #pragma unroll
           for (int k = 0; k < W; ++k) x[(u - g0) * W + k] = xu[k];
         }
-        online_group<OG * W>(mL, s, x);
+        if constexpr (ENT) {
+          online_group3<OG * W>(mL, s, hs, x);
+        } else {
+          online_group<OG * W>(mL, s, x);
+        }
       }
     };
     if constexpr (MODE == kGrad) {
@@ -677,10 +793,18 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
     if (MODE != kGrad && tid < V - tail_begin) {
       const uint32_t j = tail_begin + tid;
       const float xv = (j == t) ? kNegInf : Elem<TI>::load1(zrow, j);
-      merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
+      if constexpr (ENT) {
+        merge3(mL, s, hs, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f, 0.f);
+      } else {
+        merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
+      }
     }
 
-    if constexpr (MODE != kGrad) block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+    if constexpr (ENT) {
+      block_reduce3<BLOCK>(mL, s, hs, red_m, red_s, red_u, par, lane, wid);
+    } else if constexpr (MODE != kGrad) {
+      block_reduce<BLOCK>(mL, s, red_m, red_s, par, lane, wid);
+    }
     if constexpr (MODE == kStats) {
       if (tid == 0) {
         p.stats[3 * r] = mL;
@@ -709,6 +833,9 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       o.kl = epi[par][2];
     } else {
       o = row_epilogue(p, r, mL, s, zt, tid == 0);
+    }
+    if constexpr (ENT) {
+      if (tid == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
     }
 
     // ---- pass 2: gradient ----------------------------------------------------
@@ -963,18 +1090,19 @@ ce_status launch_persistent(Kern kern, int block, std::atomic<int>& occ, const R
 }
 
 template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int U, bool WRITE,
-          bool PF = false, bool EPI1 = false, int OG = U, int MODE = kFused>
+          bool PF = false, bool EPI1 = false, int OG = U, int MODE = kFused, bool ENT = false>
 ce_status launch_rows(const RowParams& rp, hipStream_t stream, int per_cu_cap = 0) {
   static std::atomic<int> occ{0};
   return launch_persistent(
-      ce_rows_kernel<TI, TO, BLOCK, NRES, NRAW, NLDS, U, WRITE, PF, EPI1, OG, MODE>, BLOCK, occ,
-      rp, stream, per_cu_cap);
+      ce_rows_kernel<TI, TO, BLOCK, NRES, NRAW, NLDS, U, WRITE, PF, EPI1, OG, MODE, ENT>, BLOCK,
+      occ, rp, stream, per_cu_cap);
 }
 
-template <typename TI, typename TO, bool WRITE, int MODE = kFused>
+template <typename TI, typename TO, bool WRITE, int MODE = kFused, bool ENT = false>
 ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
   static std::atomic<int> occ{0};
-  return launch_persistent(ce_rows_scalar_kernel<TI, TO, 256, WRITE, MODE>, 256, occ, rp, stream);
+  return launch_persistent(ce_rows_scalar_kernel<TI, TO, 256, WRITE, MODE, ENT>, 256, occ, rp,
+                           stream);
 }
 
 // Pick a kernel variant for (input type, output type, vector path or not).
@@ -1002,6 +1130,14 @@ ce_status dispatch_out(const RowParams& rp, int32_t grad_dtype, bool write, bool
   if (!write) return dispatch_rows<TI, TI, false>(rp, vec, stream);
   if (grad_dtype == CE_DTYPE_F32) return dispatch_rows<TI, float, true>(rp, vec, stream);
   return dispatch_rows<TI, bf16_t, true>(rp, vec, stream);
+}
+
+// The entropy forward reads each row once and writes no gradient: the
+// short-row streaming shape serves every row length.
+template <typename TI>
+ce_status dispatch_entropy(const RowParams& rp, bool vec, hipStream_t stream) {
+  if (!vec) return launch_rows_scalar<TI, TI, false, kFused, true>(rp, stream);
+  return launch_rows<TI, TI, 256, 0, 0, 0, 4, false, true, true, 4, kFused, true>(rp, stream, 64);
 }
 
 // Statistics and gradient passes of a shard stream whole rows (nothing is
@@ -1080,34 +1216,13 @@ RowParams shard_params(const ce_shard* s, const void* logits, const int64_t* tar
   return rp;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t ce_workspace_bytes(const ce_problem* p) {
-  if (p == nullptr || p->T < 0 || p->num_segments < 0) return 0;
-  if (p->num_segments == 0) return 0;
-  return align_up(static_cast<size_t>(p->T) * sizeof(float)) +
-         align_up((static_cast<size_t>(p->num_segments) + 1) * sizeof(int32_t));
-}
-
-const char* ce_status_string(int status) {
-  switch (status) {
-    case CE_OK: return "CE_OK";
-    case CE_ERR_INVALID_ARG: return "CE_ERR_INVALID_ARG";
-    case CE_ERR_UNSUPPORTED: return "CE_ERR_UNSUPPORTED";
-    case CE_ERR_ALIAS: return "CE_ERR_ALIAS";
-    case CE_ERR_WORKSPACE: return "CE_ERR_WORKSPACE";
-    case CE_ERR_HIP: return "CE_ERR_HIP";
-    default: return "CE_ERR_UNKNOWN";
-  }
-}
-
-ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_t* targets,
-                           const uint8_t* mask, const int32_t* segment_ids, float z_alpha,
-                           float grad_scale, float* loss_out, float* seg_loss_out,
-                           void* grad_out, void* workspace, size_t workspace_bytes,
-                           void* stream_ptr) {
+// Validation and launches shared by the fused entry points. grad_out null
+// is a forward; lse_out / ent_out (forward only) are optional [T] outputs.
+ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targets,
+                   const uint8_t* mask, const int32_t* segment_ids, float z_alpha,
+                   float grad_scale, float* loss_out, float* seg_loss_out, void* grad_out,
+                   float* lse_out, float* ent_out, void* workspace, size_t workspace_bytes,
+                   void* stream_ptr) {
   // ---- host validation: nothing is enqueued on failure ----
   if (p == nullptr) return CE_ERR_INVALID_ARG;
   const int64_t T = p->T, V = p->V;
@@ -1152,6 +1267,14 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_
                                 static_cast<size_t>(out_elems) * bo))
       return CE_ERR_ALIAS;
   }
+  // The per-row outputs may not overlap the logits.
+  for (const float* o : {static_cast<const float*>(loss_out), static_cast<const float*>(lse_out),
+                         static_cast<const float*>(ent_out)}) {
+    if (o && T > 0 &&
+        ranges_overlap(reinterpret_cast<uintptr_t>(logits), static_cast<size_t>(in_elems) * bi,
+                       reinterpret_cast<uintptr_t>(o), static_cast<size_t>(T) * sizeof(float)))
+      return CE_ERR_ALIAS;
+  }
   const size_t need = ce_workspace_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CE_ERR_WORKSPACE;
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0) return CE_ERR_WORKSPACE;
@@ -1190,6 +1313,8 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_
     rp.seg_mean = (p->flags & CE_FLAG_SEGMENT_MEAN) ? 1 : 0;
     rp.z_alpha = z_alpha;
     rp.grad_scale = grad_scale;
+    rp.lse_out = lse_out;
+    rp.ent_out = ent_out;
 
     const bool vec_in = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) &&
                         ((p->ld_logits * bi) % 16 == 0);
@@ -1197,9 +1322,14 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_
                                        ((p->ld_grad * bo) % 16 == 0));
     const bool vec = vec_in && vec_out;
     (void)hipGetLastError();
-    ce_status st = (p->logits_dtype == CE_DTYPE_F32)
-                       ? dispatch_out<float>(rp, p->grad_dtype, grad_out != nullptr, vec, stream)
-                       : dispatch_out<bf16_t>(rp, p->grad_dtype, grad_out != nullptr, vec, stream);
+    ce_status st;
+    if (ent_out)
+      st = (p->logits_dtype == CE_DTYPE_F32) ? dispatch_entropy<float>(rp, vec, stream)
+                                             : dispatch_entropy<bf16_t>(rp, vec, stream);
+    else
+      st = (p->logits_dtype == CE_DTYPE_F32)
+               ? dispatch_out<float>(rp, p->grad_dtype, grad_out != nullptr, vec, stream)
+               : dispatch_out<bf16_t>(rp, p->grad_dtype, grad_out != nullptr, vec, stream);
     if (st != CE_OK) return st;
   }
 
@@ -1209,6 +1339,48 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
   return CE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ce_workspace_bytes(const ce_problem* p) {
+  if (p == nullptr || p->T < 0 || p->num_segments < 0) return 0;
+  if (p->num_segments == 0) return 0;
+  return align_up(static_cast<size_t>(p->T) * sizeof(float)) +
+         align_up((static_cast<size_t>(p->num_segments) + 1) * sizeof(int32_t));
+}
+
+const char* ce_status_string(int status) {
+  switch (status) {
+    case CE_OK: return "CE_OK";
+    case CE_ERR_INVALID_ARG: return "CE_ERR_INVALID_ARG";
+    case CE_ERR_UNSUPPORTED: return "CE_ERR_UNSUPPORTED";
+    case CE_ERR_ALIAS: return "CE_ERR_ALIAS";
+    case CE_ERR_WORKSPACE: return "CE_ERR_WORKSPACE";
+    case CE_ERR_HIP: return "CE_ERR_HIP";
+    default: return "CE_ERR_UNKNOWN";
+  }
+}
+
+ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_t* targets,
+                           const uint8_t* mask, const int32_t* segment_ids, float z_alpha,
+                           float grad_scale, float* loss_out, float* seg_loss_out,
+                           void* grad_out, void* workspace, size_t workspace_bytes,
+                           void* stream_ptr) {
+  return run_rows(p, logits, targets, mask, segment_ids, z_alpha, grad_scale, loss_out,
+                  seg_loss_out, grad_out, nullptr, nullptr, workspace, workspace_bytes,
+                  stream_ptr);
+}
+
+ce_status ce_fused_forward(const ce_problem* p, const void* logits, const int64_t* targets,
+                           const uint8_t* mask, const int32_t* segment_ids, float z_alpha,
+                           float* loss_out, float* seg_loss_out, float* lse_out,
+                           float* entropy_out, void* workspace, size_t workspace_bytes,
+                           void* stream_ptr) {
+  return run_rows(p, logits, targets, mask, segment_ids, z_alpha, 1.0f, loss_out, seg_loss_out,
+                  nullptr, lse_out, entropy_out, workspace, workspace_bytes, stream_ptr);
 }
 
 ce_status ce_shard_stats(const ce_shard* sh, const void* logits, const int64_t* targets,

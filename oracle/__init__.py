@@ -15,6 +15,7 @@ paragraphs for z-loss sharing the softmax and per-segment sums) in float64 numpy
 from .ce_oracle import (  # noqa: F401
     IGNORE_INDEX,
     ce_oracle,
+    row_entropy,
     segment_lengths,
     shard_nontarget_lse,
     sigmoid,

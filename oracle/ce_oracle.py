@@ -259,3 +259,44 @@ def shard_nontarget_lse(z_shard, targets, v0, *, mask=None, ignore_index=IGNORE_
         if np.isfinite(m) or m > 0:
             lse[r] = m + np.log(np.exp(row - m).sum())
     return lse, zt
+
+
+def row_entropy(logits, targets, *, mask=None, ignore_index=IGNORE_INDEX):
+    """Entropy of each row's softmax, H = -sum_j p_j log p_j (0 log 0 = 0), in
+    float64; 0 for ignored rows, NaN for valid rows whose target is outside
+    [0, V). Callers reuse the logits for such quantities (torchtitan #5661,
+    fourth review, inline diff: the input logits are never modified, e.g. for
+    entropy). Also returns the full logsumexp per row (0 / NaN likewise).
+
+    The target's term -p_t log p_t = p_t softplus(LSE_nt - z_t) is formed from
+    the non-target logsumexp, as the NLL is (revised PR description,
+    Numerics): written as p_t (lse - z_t) it rounds to 0 once the target
+    dominates, even in float64. The other terms p_j (lse - z_j) are all >= 0.
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    T, V = z.shape
+    t = np.asarray(targets, dtype=np.int64).reshape(T)
+    valid = t != ignore_index
+    if mask is not None:
+        valid &= np.asarray(mask).reshape(T) != 0
+    H = np.zeros(T)
+    lse = np.zeros(T)
+    for r in range(T):
+        if not valid[r]:
+            continue
+        if not (0 <= t[r] < V):
+            H[r] = lse[r] = np.nan
+            continue
+        zt = z[r, t[r]]
+        z_nt = np.delete(z[r], t[r])
+        m = z_nt.max() if z_nt.size else _NEG_INF
+        lse_nt = m + np.log(np.exp(z_nt - m).sum()) if np.isfinite(m) else _NEG_INF
+        x = lse_nt - zt
+        nll = float(softplus(x))
+        lse[r] = max(lse_nt, zt) + np.log1p(np.exp(-abs(x)))
+        p_t = float(sigmoid(np.array([-x]))[0])
+        p = np.exp(z_nt - lse[r])
+        with np.errstate(invalid="ignore"):
+            terms = np.where(p > 0, p * (lse[r] - z_nt), 0.0)
+        H[r] = (p_t * nll if p_t > 0 else 0.0) + terms.sum()
+    return H, lse

@@ -340,6 +340,30 @@ def pin_shard_nontarget_lse(shard_fn):
     assert zt[0] == 2.5
 
 
+def pin_row_entropy(ent_fn):
+    """Entropy: uniform rows give ln V, a single finite column gives 0, and
+    random rows match 120-digit brute force of -sum p log p."""
+    H, lse = ent_fn(np.full((2, 7), 1.5), np.array([0, 6]))
+    _close(H, [math.log(7)] * 2, 1e-14, 0, "uniform entropy")
+    _close(lse, [1.5 + math.log(7)] * 2, 1e-14, 0, "uniform lse")
+    z = np.full((1, 5), -np.inf)
+    z[0, 2] = 3.0
+    H, lse = ent_fn(z, np.array([2]))
+    assert H[0] == 0.0 and lse[0] == 3.0
+    rng = np.random.default_rng(4)
+    z = rng.normal(0, 3, size=(4, 6))
+    z[1, 2] = 80.0           # confident row: entropy ~ 1e-33
+    H, _ = ent_fn(z, np.array([0, 2, 5, 1]))
+    mpmath.mp.dps = 120
+    for r in range(4):
+        zs = [mpmath.mpf(float(v)) for v in z[r]]
+        lse_r = mpmath.log(mpmath.fsum([mpmath.exp(v) for v in zs]))
+        ref = -mpmath.fsum([mpmath.exp(v - lse_r) * (v - lse_r) for v in zs])
+        _close(H[r], float(ref), 1e-10, 1e-300, f"entropy row {r}")
+    H, _ = ent_fn(np.zeros((3, 4)), np.array([-100, 9, 1]))
+    assert H[0] == 0.0 and np.isnan(H[1]) and H[2] > 0
+
+
 ALL_PINS = [
     pin_margin20,
     pin_collapse_is_avoided,

@@ -224,3 +224,43 @@ def test_rows_finish_validation(case, pkw, kw, expect):
     st = _lib().rows_finish_raw(p, kw.get("n", 2), kw.get("stats", A_LOGITS), A_TGT, 0,
                                 kw.get("seg", 0), 0.0, A_LOSS, 0, kw.get("rs", A_GRAD), 0, 0, 0)
     assert st == expect, case
+
+
+def test_build_script_does_not_import_the_package():
+    """The build must run where the library is absent or stale, so loading
+    build.py may not import the package (which loads the library)."""
+    code = ("import sys, importlib.util;"
+            f"spec = importlib.util.spec_from_file_location('b', {os.path.join(ROOT, 'loss_vocab_amd', 'build.py')!r});"
+            "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m);"
+            "assert 'loss_vocab_amd' not in sys.modules and 'loss_vocab_amd._lib' not in sys.modules;"
+            "assert callable(m.build)")
+    subprocess.run(["python", "-c", code], check=True, cwd="/")
+
+
+def _fwd(p, logits=A_LOGITS, targets=A_TGT, loss=A_LOSS, lse=0, ent=0, seg=0, seg_out=0, ws=0,
+         ws_bytes=0, za=0.0):
+    return _lib().forward_raw(p, logits, targets, 0, seg, za, loss, seg_out, lse, ent, ws,
+                              ws_bytes, 0)
+
+
+@pytest.mark.parametrize("case,kw,pkw,expect", [
+    ("null loss", dict(loss=0), {}, 1),
+    ("null logits", dict(logits=0), {}, 1),
+    ("lse overlaps logits", dict(lse=A_LOGITS + 16), {}, 3),
+    ("entropy overlaps logits", dict(ent=A_LOGITS + 8 * 100 * 4 - 4), {}, 3),
+    ("loss overlaps logits", dict(loss=A_LOGITS), {}, 3),
+    ("non-finite z_alpha", dict(za=float("inf")), {}, 1),
+    ("segments without workspace", dict(seg=A_SEG), dict(S=2), 4),
+    ("bad logits dtype", {}, dict(dt=2), 1),
+])
+def test_forward_validation(case, kw, pkw, expect):
+    st = _fwd(_problem(**pkw), **kw)
+    assert st == expect, (case, _lib().status_string(st))
+
+
+def test_forward_ignores_grad_fields():
+    """grad_dtype and ld_grad are not read by the forward entry: a problem
+    whose gradient fields are invalid still fails only on other checks."""
+    p = _problem(gdt=9, ldg=1)
+    assert _fwd(p, loss=0) == 1
+    assert _fwd(p, lse=A_LOGITS) == 3

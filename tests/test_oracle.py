@@ -10,7 +10,7 @@ import torch
 import oracle
 from oracle import ce_oracle
 
-from oracle_pins import ALL_PINS, GOLDEN, pin_shard_nontarget_lse
+from oracle_pins import ALL_PINS, GOLDEN, pin_row_entropy, pin_shard_nontarget_lse
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -22,6 +22,10 @@ def test_pin(pin):
 
 def test_pin_shard_nontarget_lse():
     pin_shard_nontarget_lse(oracle.shard_nontarget_lse)
+
+
+def test_pin_row_entropy():
+    pin_row_entropy(oracle.row_entropy)
 
 
 def test_shard_lses_merge_to_the_row():
