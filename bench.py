@@ -27,6 +27,8 @@ if ROOT not in sys.path:
 DEFAULT_WORKLOAD = "cez_bf16_T8192_V32000_collapse"
 HBM_PEAK_GBPS = 8000.0
 METRIC = "fused CE fwd+bwd logit elems/sec + achieved HBM GB/s (% of peak)"
+METRIC_FORWARD = "CE forward + logsumexp + entropy logit elems/sec + achieved HBM GB/s (% of peak)"
+METRIC_FORWARD_LSE = "CE forward + logsumexp logit elems/sec + achieved HBM GB/s (% of peak)"
 
 
 def kernel_source_sha():
@@ -47,17 +49,22 @@ def traffic_from_profiles(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, rows, threads):
+def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0):
     """Time the fp64 oracle on ``rows`` rows of the workload recipe (generated
-    on the host), split in 256-row blocks over a thread pool."""
+    on the host), split in 256-row blocks over a thread pool, repeating the
+    sample until ``min_seconds`` have passed. ``forward``: loss, logsumexp and
+    entropy without the gradient. A segmented recipe keeps its minimum segment
+    length, with fewer segments when the sample is short."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
 
-    from oracle import ce_oracle
+    from oracle import ce_oracle, row_entropy
     from workloads import make_inputs
 
     sample = wl.scaled(T=rows) if rows != wl.T else wl
+    if wl.num_segments and rows < wl.num_segments * wl.seg_min_len * 2:
+        sample = wl.scaled(T=rows, num_segments=max(1, rows // (2 * wl.seg_min_len)))
     inp = make_inputs(sample, device="cpu")
     z = inp["logits"]
     t = inp["targets"].numpy()
@@ -67,20 +74,30 @@ def cpu_baseline(wl, rows, threads):
     def work(b):
         r0, r1 = b
         zb = z[r0:r1].double().numpy()
-        return ce_oracle(zb, t[r0:r1], z_alpha=inp["z_alpha"], grad_scale=inp["grad_scale"],
-                         segment_ids=None if seg is None else seg[r0:r1],
-                         num_segments=inp["num_segments"],
-                         segment_mean=False)["loss"].sum()
+        out = ce_oracle(zb, t[r0:r1], z_alpha=inp["z_alpha"], grad_scale=inp["grad_scale"],
+                        segment_ids=None if seg is None else seg[r0:r1],
+                        num_segments=inp["num_segments"], segment_mean=False,
+                        want_grad=not forward)["loss"].sum()
+        if forward:
+            out += row_entropy(zb, t[r0:r1])[0].sum()
+        return out
 
+    passes = 0
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        tot = sum(ex.map(work, blocks))
-    dt = time.perf_counter() - t0
-    assert np.isfinite(tot)
-    return {"value": rows * wl.V / dt, "unit": "logit elems/s", "cores": threads,
+        while True:
+            tot = sum(ex.map(work, blocks))
+            assert np.isfinite(tot)
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    what = "loss+logsumexp+entropy" if forward else "loss+gradient"
+    segs = f", {sample.num_segments} segments" if sample.num_segments else ""
+    return {"value": passes * rows * wl.V / dt, "unit": "logit elems/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
-            "sample": f"{rows} rows x V={wl.V} of the same recipe generated on the host; "
-                      f"fp64 numpy loss+gradient in 256-row blocks on {threads} threads"}
+            "sample": f"{rows} rows x V={wl.V} of the same recipe{segs} generated on the host, "
+                      f"{passes} passes; fp64 numpy {what} in 256-row blocks on {threads} threads"}
 
 
 def main():
@@ -92,11 +109,17 @@ def main():
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum time of the CPU oracle baseline (the sample is repeated)")
+    ap.add_argument("--no-entropy", action="store_true",
+                    help="forward path: logsumexp only, no entropy output")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of the plain device copy timed after the run (0: skip)")
-    ap.add_argument("--path", choices=["fused", "split"], default="fused",
+    ap.add_argument("--path", choices=["fused", "split", "forward"], default="fused",
                     help="fused: one ce_fused_fwd_bwd call per step; split: per-shard statistics, "
-                         "finish, per-shard gradient (the vocabulary-parallel form on one GPU)")
+                         "finish, per-shard gradient (the vocabulary-parallel form on one GPU); "
+                         "forward: one ce_fused_forward call with logsumexp and entropy outputs "
+                         "(another metric: no gradient)")
     ap.add_argument("--shards", type=int, default=2)
     args = ap.parse_args()
 
@@ -115,7 +138,8 @@ def main():
     if not args.no_cpu_baseline:
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         rows = args.cpu_rows or min(wl.T, max(256, int(3e8 // wl.V) // 256 * 256))
-        cpu = cpu_baseline(wl, rows, threads)
+        cpu = cpu_baseline(wl, rows, threads, forward=args.path == "forward",
+                           min_seconds=args.cpu_seconds)
 
     import torch
 
@@ -131,8 +155,12 @@ def main():
         inp = make_inputs(wl, device=dev, seed_offset=i)
         in_place = wl.grad == "inplace"
         loss = torch.empty(wl.T, dtype=torch.float32, device=dev)
-        grad = inp["logits"] if in_place else torch.empty((wl.T, wl.V), dtype=wl.grad_torch_dtype,
-                                                          device=dev)
+        if args.path == "forward":
+            grad = None
+        elif in_place:
+            grad = inp["logits"]
+        else:
+            grad = torch.empty((wl.T, wl.V), dtype=wl.grad_torch_dtype, device=dev)
         seg = (torch.empty(wl.num_segments, dtype=torch.float32, device=dev)
                if wl.num_segments else None)
         ws_n = L.workspace_bytes(inp["logits"], num_segments=wl.num_segments)
@@ -148,6 +176,11 @@ def main():
             split_bufs.append((torch.empty((len(bounds), wl.T, 3), dtype=torch.float32, device=dev),
                                torch.empty((wl.T, 8), dtype=torch.float32, device=dev)))
     phase_ev = []   # split path: (stats, finish, grad) event triples per step
+    fwd_bufs = []
+    if args.path == "forward":
+        for _ in sets:
+            fwd_bufs.append((torch.empty(wl.T, dtype=torch.float32, device=dev),
+                             torch.empty(wl.T, dtype=torch.float32, device=dev)))
 
     def step(i):
         inp, loss, grad, seg, ws = sets[i % len(sets)]
@@ -155,6 +188,13 @@ def main():
             L.ce_fused_fwd_bwd(inp["logits"], inp["targets"], None, inp["segment_ids"],
                                inp["z_alpha"], inp["grad_scale"], loss, seg, grad,
                                num_segments=wl.num_segments, segment_mean=inp["segment_mean"],
+                               workspace=ws, stream=stream.cuda_stream)
+            return
+        if args.path == "forward":
+            lse, ent = fwd_bufs[i % len(sets)]
+            L.ce_fused_forward(inp["logits"], inp["targets"], None, inp["segment_ids"],
+                               inp["z_alpha"], loss, seg, lse, None if args.no_entropy else ent,
+                               num_segments=wl.num_segments,
                                workspace=ws, stream=stream.cuda_stream)
             return
         stats, row_state = split_bufs[i % len(sets)]
@@ -243,8 +283,19 @@ def main():
         achieved = grad_bytes / (ms[2] * 1e-3) / 1e9
         avg_call_ms = ms[2]
         traffic = None
+    metric = METRIC
+    if args.path == "forward":
+        # Valid rows read once; targets read, loss / lse / entropy written
+        # (the segment terms of the fused call stay the same).
+        b_in = 4 if wl.dtype == "f32" else 2
+        nbytes = wl.n_valid * wl.V * b_in + wl.T * (8 + (2 if args.no_entropy else 3) * 4)
+        if wl.num_segments:
+            nbytes += wl.T * (4 + 8) + wl.num_segments * 4
+        achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
+        traffic = None
+        metric = METRIC_FORWARD_LSE if args.no_entropy else METRIC_FORWARD
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": elems / (ms_per_step * 1e-3),
         "unit": "logit elems/s",
         "n_gpus": 1,
@@ -263,6 +314,7 @@ def main():
             "ignored_rows": wl.n_masked, "segments": wl.num_segments,
             "rotating_buffer_sets": args.rotate, "alg_bytes_per_step": nbytes,
             "path": args.path,
+            **({"entropy": not args.no_entropy} if args.path == "forward" else {}),
         },
         "alg_GBps": nbytes / (ms_per_step * 1e-3) / 1e9,
         "pct_of_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -526,8 +526,8 @@ template <typename TI, typename TO, int BLOCK, int NRES, int NRAW, int NLDS, int
           bool PF, bool EPI1, int OG = U, int MODE = kFused, bool ENT = false>
 __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   static_assert(U % OG == 0, "online groups split the step evenly");
-  static_assert(!ENT || (MODE == kFused && !WRITE && NRES + NRAW + NLDS == 0),
-                "the entropy variant is a streamed forward");
+  static_assert(!ENT || (MODE == kFused && !WRITE && NRES + NRAW == 0),
+                "the entropy variant is a forward with streamed or LDS-staged slots");
   static_assert(MODE != kGrad || (NRES + NRAW + NLDS == 0 && WRITE), "gradient mode streams");
   static_assert(MODE != kStats || !WRITE, "statistics mode writes no gradient");
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
@@ -737,7 +737,11 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
         if (mine && i0 + i == static_cast<int>(st)) v = (v & and_m) | or_m;
         float x[W];
         Elem<TI>::unpack(v, x);
-        online_group<W>(mL, s, x);
+        if constexpr (ENT) {
+          online_group3<W>(mL, s, hs, x);
+        } else {
+          online_group<W>(mL, s, x);
+        }
       }
     }
 
@@ -827,15 +831,19 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
           epi[par][2] = o.kl;
         }
       }
+      if constexpr (ENT) {
+        // the entropy's fp64 epilogue runs on another wave, beside the loss's
+        if (wid == (BLOCK > 64 ? 1u : 0u) && lane == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
+      }
       __syncthreads();
       o.g_t = epi[par][0];
       o.cnt = epi[par][1];
       o.kl = epi[par][2];
     } else {
       o = row_epilogue(p, r, mL, s, zt, tid == 0);
-    }
-    if constexpr (ENT) {
-      if (tid == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
+      if constexpr (ENT) {
+        if (tid == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
+      }
     }
 
     // ---- pass 2: gradient ----------------------------------------------------
@@ -1124,20 +1132,40 @@ ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
 }
 
+// Forward only (no gradient): nothing is reused, so no slot is kept for a
+// second pass; LDS staging serves only to keep more of a row in flight.
+// Shapes by row length, measured on MI355X (the entropy variant carries two
+// more ALU ops per element, so it keeps fewer elements per online update):
+//  * short rows (<= 8192 chunks): streamed, 256 lanes;
+//  * medium rows (<= 20000 chunks): 256 lanes, plain forward with 8 slots
+//    per lane staged in LDS;
+//  * long rows: plain fp32 1024 lanes with 9 LDS slots, plain bf16 256 lanes
+//    with 16; the fp32 entropy variant 256 lanes with 16 LDS slots.
+template <typename TI, bool ENT>
+ce_status dispatch_forward(const RowParams& rp, bool vec, hipStream_t stream) {
+  if (!vec) return launch_rows_scalar<TI, TI, false, kFused, ENT>(rp, stream);
+  const int64_t nchunk = rp.V / Elem<TI>::VEC;
+  if constexpr (ENT) {
+    if (nchunk <= 8192)
+      return launch_rows<TI, TI, 256, 0, 0, 0, 2, false, true, true, 2, kFused, true>(rp, stream, 64);
+    if (Elem<TI>::BYTES == 4 && nchunk > 20000)
+      return launch_rows<TI, TI, 256, 0, 0, 16, 4, false, true, true, 2, kFused, true>(rp, stream, 64);
+    return launch_rows<TI, TI, 256, 0, 0, 0, 4, false, true, true, 2, kFused, true>(rp, stream, 64);
+  } else {
+    if (nchunk <= 8192) return launch_rows<TI, TI, 256, 0, 0, 0, 4, false, true, true>(rp, stream, 64);
+    if (nchunk <= 20000) return launch_rows<TI, TI, 256, 0, 0, 8, 4, false, true, true>(rp, stream, 64);
+    if (Elem<TI>::BYTES == 4)
+      return launch_rows<TI, TI, 1024, 0, 0, 9, 4, false, true, true, 1>(rp, stream, 64);
+    return launch_rows<TI, TI, 256, 0, 0, 16, 4, false, true, true>(rp, stream, 64);
+  }
+}
+
 template <typename TI>
 ce_status dispatch_out(const RowParams& rp, int32_t grad_dtype, bool write, bool vec,
                        hipStream_t stream) {
-  if (!write) return dispatch_rows<TI, TI, false>(rp, vec, stream);
+  if (!write) return dispatch_forward<TI, false>(rp, vec, stream);
   if (grad_dtype == CE_DTYPE_F32) return dispatch_rows<TI, float, true>(rp, vec, stream);
   return dispatch_rows<TI, bf16_t, true>(rp, vec, stream);
-}
-
-// The entropy forward reads each row once and writes no gradient: the
-// short-row streaming shape serves every row length.
-template <typename TI>
-ce_status dispatch_entropy(const RowParams& rp, bool vec, hipStream_t stream) {
-  if (!vec) return launch_rows_scalar<TI, TI, false, kFused, true>(rp, stream);
-  return launch_rows<TI, TI, 256, 0, 0, 0, 4, false, true, true, 4, kFused, true>(rp, stream, 64);
 }
 
 // Statistics and gradient passes of a shard stream whole rows (nothing is
@@ -1324,8 +1352,8 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
     (void)hipGetLastError();
     ce_status st;
     if (ent_out)
-      st = (p->logits_dtype == CE_DTYPE_F32) ? dispatch_entropy<float>(rp, vec, stream)
-                                             : dispatch_entropy<bf16_t>(rp, vec, stream);
+      st = (p->logits_dtype == CE_DTYPE_F32) ? dispatch_forward<float, true>(rp, vec, stream)
+                                             : dispatch_forward<bf16_t, true>(rp, vec, stream);
     else
       st = (p->logits_dtype == CE_DTYPE_F32)
                ? dispatch_out<float>(rp, p->grad_dtype, grad_out != nullptr, vec, stream)

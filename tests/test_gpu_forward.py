@@ -172,6 +172,34 @@ def test_forward_without_entropy():
     check_loss(_np(lse), lse_ref, "lse without entropy")
 
 
+SHAPES = [(torch.float32, 50001), (torch.bfloat16, 100003), (torch.float32, 170003),
+          (torch.bfloat16, 170003)]
+
+
+@pytest.mark.parametrize("dtype,V", SHAPES, ids=[f"{str(d)[6:]}-{v}" for d, v in SHAPES])
+def test_forward_row_shapes(dtype, V):
+    """Medium and long rows take the LDS-staged forward shapes: with and
+    without the entropy output, and the fused call without a gradient."""
+    import loss_vocab_amd as L
+    print(f"[forward] shapes V={V} {dtype}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V)
+    T = 6
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[2] = -100
+    z[4, t[4]] = z[4].max() + 30          # a confident row
+    compare_forward(z, t, alpha=1e-4, what=f"shape V={V}")
+    loss2, lse2, ent2, _ = L.ce_forward(z, t, z_alpha=1e-4, entropy=False)
+    loss3, _, _ = L.ce_fused(z, t, z_alpha=1e-4, want_grad=False)
+    torch.cuda.synchronize()
+    z64 = to_np64(z)
+    ref = ce_oracle(z64, _np(t), z_alpha=1e-4, want_grad=False)
+    _, lse_ref = row_entropy(z64, _np(t))
+    check_loss(_np(loss2), ref["loss"], "forward without entropy")
+    check_loss(_np(lse2), lse_ref, "lse without entropy")
+    check_loss(_np(loss3), ref["loss"], "fused without gradient")
+
+
 FULL = ["ce_f32_T256_V4096_mask10", "cez_bf16_T8192_V32000_collapse",
         "ce_bf16_T16384_V128256_zipf_inplace", "cez_f32_T32768_V151936_peaked",
         "cezseg_bf16_T65536_V201088_seg512"]
