@@ -9,7 +9,8 @@ What it computes is written out from the pages' definitions (torchtitan PR #5661
 "fix softmax collapse with improved CE perf": the revised PR description's
 Numerics paragraph and the second review's margin-20 example; Fast-LLM PR #552
 "Fuse GSPO into the monolithic compiled loss": the PR body's What/Approach
-paragraphs for z-loss sharing the softmax and per-segment sums) in float64 numpy.
+paragraphs for z-loss sharing the softmax and per-segment sums) in float64 numpy. ``lmhead_ce`` composes that loss with a linear LM head
+(logits = hidden @ weight.T) and writes the chain rule out.
 """
 
 from .ce_oracle import (  # noqa: F401
@@ -21,3 +22,4 @@ from .ce_oracle import (  # noqa: F401
     sigmoid,
     softplus,
 )
+from .lmhead_oracle import lmhead_ce  # noqa: F401

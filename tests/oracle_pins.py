@@ -364,6 +364,43 @@ def pin_row_entropy(ent_fn):
     assert H[0] == 0.0 and np.isnan(H[1]) and H[2] > 0
 
 
+def pin_lmhead(lm_fn):
+    """Loss behind a linear head: torch fp64 autograd of F.linear followed by
+    cross-entropy + z-loss gives the loss, dX and dW; a zero weight gives the
+    uniform closed form (loss ln V, dX = 0, dW = G^T X with G written out)."""
+    g = torch.Generator().manual_seed(33)
+    T, H, V = 12, 20, 37
+    X = torch.randn(T, H, generator=g, dtype=torch.float64)
+    W = torch.randn(V, H, generator=g, dtype=torch.float64) * 0.5
+    t = torch.randint(0, V, (T,), generator=g)
+    t[5] = IGNORE
+    alpha, gamma = 2e-3, 0.125
+    valid = (t != IGNORE).double()
+    Xr = X.clone().requires_grad_(True)
+    Wr = W.clone().requires_grad_(True)
+    z = torch.nn.functional.linear(Xr, Wr)
+    ce = torch.nn.functional.cross_entropy(z, t, reduction="none", ignore_index=IGNORE)
+    lse = torch.logsumexp(z, dim=1)
+    per_row = ce + alpha * lse ** 2 * valid
+    (gamma * per_row.sum()).backward()
+    out = lm_fn(X.numpy(), W.numpy(), t.numpy(), z_alpha=alpha, grad_scale=gamma)
+    _close(out["loss"], per_row.detach().numpy(), 1e-12, 1e-15, "lm-head loss")
+    _close(out["lse"], (lse * valid).detach().numpy(), 1e-13, 1e-15, "lm-head lse")
+    _close(out["dhidden"], Xr.grad.numpy(), 1e-10, 1e-16, "lm-head dX")
+    _close(out["dweight"], Wr.grad.numpy(), 1e-10, 1e-16, "lm-head dW")
+    # zero head: every logit 0, softmax uniform
+    Wz = np.zeros((V, H))
+    out = lm_fn(X.numpy(), Wz, t.numpy(), z_alpha=alpha, grad_scale=gamma)
+    v = valid.numpy().astype(bool)
+    _close(out["loss"][v], np.full(v.sum(), math.log(V) + alpha * math.log(V) ** 2), 1e-13, 0,
+           "zero-head loss")
+    assert np.all(out["dhidden"] == 0)
+    Gz = np.zeros((T, V))
+    Gz[v] = gamma * (1.0 + 2 * alpha * math.log(V)) / V
+    Gz[np.nonzero(v)[0], t.numpy()[v]] -= gamma
+    _close(out["dweight"], Gz.T @ X.numpy(), 1e-12, 1e-15, "zero-head dW")
+
+
 ALL_PINS = [
     pin_margin20,
     pin_collapse_is_avoided,

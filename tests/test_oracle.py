@@ -131,3 +131,33 @@ def test_mutant_is_caught(name, old, new):
         except Exception as e:  # AssertionError, or a shape error the mistake causes
             failures.append((pin.__name__, type(e).__name__))
     assert failures, f"mutant {name!r} passed every pin"
+
+
+def test_pin_lmhead():
+    from oracle_pins import pin_lmhead
+    pin_lmhead(oracle.lmhead_ce)
+
+
+LM_MUTANTS = [
+    ("logits use a permuted hidden index", "z = X @ W.T", "z = X @ W[:, ::-1].T"),
+    ("dX uses the weight rows in the wrong order", 'out["dhidden"] = G @ W',
+     'out["dhidden"] = G @ W[::-1]'),
+    ("dW rows in the wrong order", 'out["dweight"] = G.T @ X', 'out["dweight"] = G.T[::-1] @ X'),
+    ("dW misses the scale", 'out["dweight"] = G.T @ X', 'out["dweight"] = G.T @ X / 0.125'),
+]
+
+
+@pytest.mark.parametrize("name,old,new", LM_MUTANTS, ids=[m[0] for m in LM_MUTANTS])
+def test_lmhead_mutant_is_caught(name, old, new):
+    import importlib.util
+    import types
+    from oracle_pins import pin_lmhead
+    path = os.path.join(os.path.dirname(oracle.__file__), "lmhead_oracle.py")
+    with open(path) as f:
+        src = f.read()
+    assert old in src, old
+    src = src.replace(old, new).replace("from .ce_oracle import", "from oracle.ce_oracle import")
+    mod = types.ModuleType("lmhead_mutant")
+    exec(compile(src, path, "exec"), mod.__dict__)
+    with pytest.raises(Exception):
+        pin_lmhead(mod.lmhead_ce)
