@@ -247,6 +247,66 @@ ce_status ce_shard_grad(const ce_shard* s, const void* logits, const int64_t* ta
                         const float* row_state, const float* row_weight, float grad_scale,
                         void* grad_out, void* stream);
 
+/*
+ * The loss behind a linear LM head, with the logits never stored whole.
+ *
+ * The logits are z = X W^T for hidden states X [T, H] and the head's weight W
+ * [V, H] (one row per vocabulary entry), both bf16; the per-row loss, z-loss,
+ * ignore rules and scales are those of ce_fused_fwd_bwd (the collapse-free
+ * loss of torchtitan PR #5661, revised PR description, Numerics). Fast-LLM PR
+ * #552 (PR body, the LM-head layer tests) puts the loss directly after such a
+ * head; fusing the head's product into the loss is this library's design, not
+ * the pages'. Forward: logit tiles are formed on the matrix cores and reduced
+ * to per-row statistics over vocabulary ranges, merged as by ce_rows_finish.
+ * Backward (dhidden or dweight given): per chunk of chunk_rows rows the logit
+ * tiles are recomputed and turned into dL/dz (bf16, one chunk at a time in
+ * the workspace), then dX = G W and dW = sum over chunks of G^T X.
+ *
+ *  T, V, H       rows, vocabulary size, hidden size (H a multiple of 8).
+ *  ld_hidden     elements between rows of hidden (>= H, multiple of 8).
+ *  ld_weight     elements between rows of weight (>= H, multiple of 8).
+ *  ignore_index  target value of an ignored row.
+ *  dhidden_dtype CE_DTYPE_F32 or CE_DTYPE_BF16.
+ *  chunk_rows    rows per backward chunk (0: 4096); rounded up to 128. The
+ *                workspace grows with it (about 4 V chunk_rows bytes).
+ */
+typedef struct ce_lmhead {
+  int64_t T;
+  int64_t V;
+  int64_t H;
+  int64_t ld_hidden;
+  int64_t ld_weight;
+  int64_t ignore_index;
+  int32_t dhidden_dtype;
+  int32_t chunk_rows;
+} ce_lmhead;
+
+/* Device workspace (bytes) of ce_lmhead_fwd_bwd: forward only (backward ==
+ * 0) or with a backward. 0 for a null or invalid problem. */
+size_t ce_lmhead_workspace_bytes(const ce_lmhead* p, int32_t backward);
+
+/*
+ *  hidden        [T, ld_hidden] bf16, 16-byte aligned. Read only.
+ *  weight        [V, ld_weight] bf16, 16-byte aligned. Read only.
+ *  targets, mask, z_alpha, grad_scale: as for ce_fused_fwd_bwd.
+ *  loss_out      [T] float, as for ce_fused_fwd_bwd. Required.
+ *  lse_out       [T] float or NULL: full logsumexp (0 ignored, NaN poisoned).
+ *  dhidden       [T, H] (contiguous) of dhidden_dtype or NULL: dL/dX.
+ *  dweight       [V, H] float (contiguous) or NULL: dL/dW, overwritten.
+ *  workspace     at least ce_lmhead_workspace_bytes(p, dhidden || dweight)
+ *                bytes, 256-byte aligned; contents on entry do not matter.
+ * Here L = sum_r s_r loss_r over valid rows. A valid row with a target outside
+ * [0, V) gives a NaN loss, a NaN dX row and NaN in every dW element (its
+ * gradient row enters every column sum). Outputs may not overlap the inputs
+ * or the workspace (CE_ERR_ALIAS). Unaligned operands or H % 8 != 0 return
+ * CE_ERR_UNSUPPORTED. The call is asynchronous and deterministic.
+ */
+ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* weight,
+                            const int64_t* targets, const uint8_t* mask, float z_alpha,
+                            float grad_scale, float* loss_out, float* lse_out, void* dhidden,
+                            float* dweight, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* ce_status_string(int status);
 

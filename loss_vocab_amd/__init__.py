@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     CE_FLAG_SEGMENT_MEAN,
     CE_OK,
     CeError,
+    CeLmhead,
     CeProblem,
     CeShard,
     status_string,
@@ -276,3 +277,66 @@ def ce_split(logits, targets, *, shards=2, mask=None, segment_ids=None, num_segm
         ce_shard_grad(logits[:, a:b], targets, row_state, grad_scale, grad[:, a:b], v0=a,
                       row_weight=row_weight, ignore_index=ignore_index)
     return loss, grad, seg, row_state
+
+
+# ---------------------------------------------------------------------------
+# Loss behind a linear LM head (logits never stored whole).
+# ---------------------------------------------------------------------------
+
+def make_lmhead(hidden, weight, *, dhidden_dtype=torch.float32, chunk_rows=0,
+                ignore_index=IGNORE_INDEX):
+    for name, t in (("hidden", hidden), ("weight", weight)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    T, H = hidden.shape
+    V, H2 = weight.shape
+    if H != H2:
+        raise ValueError("hidden and weight disagree on the hidden size")
+    p = CeLmhead()
+    p.T, p.V, p.H = T, V, H
+    p.ld_hidden = _rows(hidden, "hidden")
+    p.ld_weight = _rows(weight, "weight")
+    p.ignore_index = int(ignore_index)
+    p.dhidden_dtype = _DTYPES[dhidden_dtype]
+    p.chunk_rows = int(chunk_rows)
+    return p
+
+
+def ce_lmhead_fwd_bwd(hidden, weight, targets, mask, z_alpha, grad_scale, loss_out, lse_out,
+                      dhidden, dweight, *, chunk_rows=0, ignore_index=IGNORE_INDEX,
+                      workspace=None, stream=None):
+    """Same-named wrapper of the C entry point: hidden [T, H] bf16, weight
+    [V, H] bf16, targets [T] int64, mask [T] uint8 or None, loss_out [T] f32,
+    lse_out [T] f32 or None, dhidden [T, H] f32/bf16 or None, dweight [V, H]
+    f32 or None (both None: forward only)."""
+    p = make_lmhead(hidden, weight, dhidden_dtype=dhidden.dtype if dhidden is not None
+                    else torch.float32, chunk_rows=chunk_rows, ignore_index=ignore_index)
+    backward = dhidden is not None or dweight is not None
+    need = _lib.lmhead_workspace_bytes(p, backward)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    for name, t in (("dhidden", dhidden), ("dweight", dweight)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    st = _lib.lmhead_raw(p, _ptr(hidden), _ptr(weight), _ptr(targets), _ptr(mask), z_alpha,
+                         grad_scale, _ptr(loss_out), _ptr(lse_out), _ptr(dhidden), _ptr(dweight),
+                         _ptr(workspace), ws_bytes, _stream(hidden, stream))
+    if st != CE_OK:
+        raise CeError(st, "ce_lmhead_fwd_bwd")
+
+
+def ce_lmhead(hidden, weight, targets, *, mask=None, z_alpha=0.0, grad_scale=1.0,
+              want_grad=True, dhidden_dtype=torch.float32, chunk_rows=0,
+              ignore_index=IGNORE_INDEX):
+    """Allocate and run. Returns ``(loss[T], lse[T], dhidden or None, dweight or None)``."""
+    T, H = hidden.shape
+    V = weight.shape[0]
+    dev = hidden.device
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    dh = torch.empty((T, H), dtype=dhidden_dtype, device=dev) if want_grad else None
+    dw = torch.empty((V, H), dtype=torch.float32, device=dev) if want_grad else None
+    ce_lmhead_fwd_bwd(hidden, weight, targets, mask, z_alpha, grad_scale, loss, lse, dh, dw,
+                      chunk_rows=chunk_rows, ignore_index=ignore_index)
+    return loss, lse, dh, dw

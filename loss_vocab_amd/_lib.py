@@ -28,7 +28,8 @@ ROW_STATE = 8   # floats of saved state per row (ce_rows_finish)
 
 # Every symbol include/ce_fused.h declares.
 EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_fused_forward", "ce_shard_stats",
-           "ce_rows_finish", "ce_shard_grad", "ce_status_string")
+           "ce_rows_finish", "ce_shard_grad", "ce_lmhead_workspace_bytes", "ce_lmhead_fwd_bwd",
+           "ce_status_string")
 
 
 class CeProblem(ctypes.Structure):
@@ -55,6 +56,19 @@ class CeShard(ctypes.Structure):
         ("logits_dtype", ctypes.c_int32),
         ("grad_dtype", ctypes.c_int32),
         ("ignore_index", ctypes.c_int64),
+    ]
+
+
+class CeLmhead(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("ld_hidden", ctypes.c_int64),
+        ("ld_weight", ctypes.c_int64),
+        ("ignore_index", ctypes.c_int64),
+        ("dhidden_dtype", ctypes.c_int32),
+        ("chunk_rows", ctypes.c_int32),
     ]
 
 
@@ -92,6 +106,13 @@ def _load():
     lib.ce_rows_finish.restype = ctypes.c_int
     lib.ce_shard_grad.argtypes = [ctypes.POINTER(CeShard), vp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.ce_shard_grad.restype = ctypes.c_int
+    lib.ce_lmhead_workspace_bytes.argtypes = [ctypes.POINTER(CeLmhead), ctypes.c_int32]
+    lib.ce_lmhead_workspace_bytes.restype = ctypes.c_size_t
+    lib.ce_lmhead_fwd_bwd.argtypes = [
+        ctypes.POINTER(CeLmhead), vp, vp, vp, vp, ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
+        vp, ctypes.c_size_t, vp,
+    ]
+    lib.ce_lmhead_fwd_bwd.restype = ctypes.c_int
     lib.ce_status_string.argtypes = [ctypes.c_int]
     lib.ce_status_string.restype = ctypes.c_char_p
     return lib
@@ -145,3 +166,15 @@ def shard_grad_raw(shard, logits, targets, row_state, row_weight, grad_scale, gr
     return int(LIB.ce_shard_grad(ctypes.byref(shard), logits or None, targets or None,
                                  row_state or None, row_weight or None, float(grad_scale),
                                  grad_out or None, stream or None))
+
+
+def lmhead_workspace_bytes(problem, backward):
+    return int(LIB.ce_lmhead_workspace_bytes(ctypes.byref(problem), int(bool(backward))))
+
+
+def lmhead_raw(problem, hidden, weight, targets, mask, z_alpha, grad_scale, loss_out, lse_out,
+               dhidden, dweight, workspace, workspace_bytes_, stream):
+    return int(LIB.ce_lmhead_fwd_bwd(
+        ctypes.byref(problem), hidden or None, weight or None, targets or None, mask or None,
+        float(z_alpha), float(grad_scale), loss_out or None, lse_out or None, dhidden or None,
+        dweight or None, workspace or None, int(workspace_bytes_), stream or None))

@@ -2,7 +2,7 @@
 
 Run ``python loss_vocab_amd/build.py`` (or ``__graft_entry__.build()``); not
 ``python -m``, which imports the package and with it the library this builds.
-The library is compiled by hipcc straight from ``csrc/ce_fused.hip``; it needs
+The library is compiled by hipcc straight from ``csrc/*.hip``; it needs
 no GPU to build. This file imports nothing of the package.
 """
 
@@ -15,7 +15,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "ce_fused.hip")
+SRCS = [os.path.join(PKG, "csrc", "ce_fused.hip"), os.path.join(PKG, "csrc", "lmhead_ce.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libce_fused.so")
 ARCH = "gfx950"
@@ -37,7 +37,7 @@ def hipcc():
 
 def build(verbose=False, extra=()):
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", INC, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIP_FLAGS, *extra, "-I", INC, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

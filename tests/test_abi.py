@@ -40,7 +40,8 @@ def test_library_exports_every_declared_symbol():
         assert name in exported, name
 
 
-@pytest.mark.parametrize("ctype,pytype", [("ce_problem", "CeProblem"), ("ce_shard", "CeShard")])
+@pytest.mark.parametrize("ctype,pytype", [("ce_problem", "CeProblem"), ("ce_shard", "CeShard"),
+                                          ("ce_lmhead", "CeLmhead")])
 def test_struct_layout_matches_header(tmp_path, ctype, pytype):
     """Compile a C probe with gcc against the header and compare offsets."""
     L = _lib()
@@ -264,3 +265,60 @@ def test_forward_ignores_grad_fields():
     p = _problem(gdt=9, ldg=1)
     assert _fwd(p, loss=0) == 1
     assert _fwd(p, lse=A_LOGITS) == 3
+
+
+def _lm(T=8, V=100, H=64, ldh=None, ldw=None, dt=0, chunk=0):
+    L = _lib()
+    p = L.CeLmhead()
+    p.T, p.V, p.H = T, V, H
+    p.ld_hidden = H if ldh is None else ldh
+    p.ld_weight = H if ldw is None else ldw
+    p.ignore_index = -100
+    p.dhidden_dtype = dt
+    p.chunk_rows = chunk
+    return p
+
+
+A_W = 0x70000000
+A_DW = 0x90000000
+
+
+def _lmcall(p, hidden=A_LOGITS, weight=A_W, targets=A_TGT, loss=A_LOSS, lse=0, dh=0, dw=0,
+            ws=A_WS, ws_bytes=1 << 40, za=0.0, gs=1.0):
+    return _lib().lmhead_raw(p, hidden, weight, targets, 0, za, gs, loss, lse, dh, dw, ws,
+                             ws_bytes, 0)
+
+
+@pytest.mark.parametrize("case,pkw,kw,expect", [
+    ("V < 1", dict(V=0), {}, 1),
+    ("H < 1", dict(H=0), {}, 1),
+    ("ld_hidden < H", dict(ldh=32), {}, 1),
+    ("ld_weight < H", dict(ldw=8), {}, 1),
+    ("bad dhidden dtype", dict(dt=4), {}, 1),
+    ("negative chunk", dict(chunk=-1), {}, 1),
+    ("H not a multiple of 8", dict(H=60), {}, 2),
+    ("unaligned hidden", {}, dict(hidden=A_LOGITS + 2), 2),
+    ("odd weight stride", dict(ldw=66), {}, 2),
+    ("null weight", {}, dict(weight=0), 1),
+    ("null loss", {}, dict(loss=0), 1),
+    ("non-finite scale", {}, dict(gs=float("nan")), 1),
+    ("workspace too small", {}, dict(ws_bytes=16), 4),
+    ("unaligned workspace", {}, dict(ws=A_WS + 64), 4),
+    ("dweight overlaps weight", {}, dict(dw=A_W + 128), 3),
+    ("dhidden overlaps hidden", {}, dict(dh=A_LOGITS), 3),
+    ("loss inside the workspace", {}, dict(loss=A_WS + 256), 3),
+])
+def test_lmhead_validation(case, pkw, kw, expect):
+    st = _lmcall(_lm(**pkw), **kw)
+    assert st == expect, (case, _lib().status_string(st))
+
+
+def test_lmhead_workspace_grows_with_backward_and_chunk():
+    L = _lib()
+    p = _lm(T=1000, V=5000, H=256)
+    fwd = L.lmhead_workspace_bytes(p, False)
+    bwd = L.lmhead_workspace_bytes(p, True)
+    assert 0 < fwd < bwd
+    p.chunk_rows = 128
+    assert L.lmhead_workspace_bytes(p, True) < bwd
+    assert L.LIB.ce_lmhead_workspace_bytes(None, 1) == 0
