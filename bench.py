@@ -100,6 +100,130 @@ def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0):
                       f"{passes} passes; fp64 numpy {what} in 256-row blocks on {threads} threads"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC_LMHEAD = "fused LM-head + CE fwd+bwd tokens/sec + achieved matrix-core TFLOP/s (% of bf16 peak)"
+DEFAULT_LMHEAD = "lmhead_bf16_T16384_V128256_H4096"
+
+
+def cpu_baseline_lmhead(wl, rows, threads, min_seconds):
+    """The oracle on the first ``rows`` rows (the whole weight): logits, loss,
+    dX and dW of those rows in fp64, 8-row blocks over a thread pool, repeated
+    until ``min_seconds`` have passed."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import lmhead_ce
+    from workloads import make_lmhead_inputs
+
+    inp = make_lmhead_inputs(wl, device="cpu", rows=rows)
+    X = inp["hidden"].double().numpy()
+    W = inp["weight"].double().numpy()
+    t = inp["targets"].numpy()
+    blocks = [(r0, min(rows, r0 + 8)) for r0 in range(0, rows, 8)]
+
+    def work(b):
+        out = lmhead_ce(X[b[0]:b[1]], W, t[b[0]:b[1]], grad_scale=inp["grad_scale"])
+        return float(np.nansum(out["loss"])) + float(out["dweight"][0, 0])
+
+    passes = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(work, blocks))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    return {"value": passes * rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{rows} rows of the recipe (whole weight V={wl.V} x H={wl.H}) generated on "
+                      f"the host, {passes} passes; fp64 numpy logits, loss, dX and dW in 8-row "
+                      f"blocks on {threads} threads"}
+
+
+def bench_lmhead(args):
+    """One step = one ce_lmhead_fwd_bwd call (forward statistics, finish, and
+    the chunked backward with dX and dW) on resident inputs."""
+    from workloads import LMHEAD_WORKLOADS, lmhead_flops
+
+    name = args.workload if args.workload in LMHEAD_WORKLOADS else DEFAULT_LMHEAD
+    wl = LMHEAD_WORKLOADS[name]
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        cpu = cpu_baseline_lmhead(wl, args.cpu_rows or 32, threads, args.cpu_seconds)
+
+    import torch
+
+    import loss_vocab_amd as L
+    from workloads import make_lmhead_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_lmhead_inputs(wl, device=dev)
+    X, W, t = inp["hidden"], inp["weight"], inp["targets"]
+    loss = torch.empty(wl.T, dtype=torch.float32, device=dev)
+    lse = torch.empty(wl.T, dtype=torch.float32, device=dev)
+    dh = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((wl.V, wl.H), dtype=torch.float32, device=dev)
+    p = L.make_lmhead(X, W, dhidden_dtype=torch.bfloat16)
+    ws = torch.empty(L._lib.lmhead_workspace_bytes(p, True), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        L.ce_lmhead_fwd_bwd(X, W, t, None, inp["z_alpha"], inp["grad_scale"], loss, lse, dh, dw,
+                            workspace=ws, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    per_call = sorted(a.elapsed_time(b) for a, b in ev)
+    avg_call = sum(per_call) / len(per_call)
+    flops = lmhead_flops(wl)
+    achieved = flops / (avg_call * 1e-3) / 1e12
+    out = {
+        "metric": METRIC_LMHEAD,
+        "value": wl.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "V": wl.V, "H": wl.H,
+                   "ignored_rows": wl.n_masked, "dhidden_dtype": "bf16", "dweight_dtype": "f32",
+                   "flops_per_step": flops, "path": "lmhead"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "call_ms_avg": avg_call,
+                     "call_ms_median": per_call[len(per_call) // 2]},
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,11 +239,12 @@ def main():
                     help="forward path: logsumexp only, no entropy output")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of the plain device copy timed after the run (0: skip)")
-    ap.add_argument("--path", choices=["fused", "split", "forward"], default="fused",
+    ap.add_argument("--path", choices=["fused", "split", "forward", "lmhead"], default="fused",
                     help="fused: one ce_fused_fwd_bwd call per step; split: per-shard statistics, "
                          "finish, per-shard gradient (the vocabulary-parallel form on one GPU); "
                          "forward: one ce_fused_forward call with logsumexp and entropy outputs "
-                         "(another metric: no gradient)")
+                         "(another metric: no gradient); lmhead: ce_lmhead_fwd_bwd from hidden "
+                         "states and the head weight (another metric: matrix-core bound)")
     ap.add_argument("--shards", type=int, default=2)
     args = ap.parse_args()
 
@@ -128,6 +253,9 @@ def main():
               "(rows shard across GPUs with no exchange beyond a token count; "
               "see the design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.path == "lmhead":
+        return bench_lmhead(args)
 
     from workloads import WORKLOADS, alg_bytes
 

@@ -258,17 +258,20 @@ ce_status ce_shard_grad(const ce_shard* s, const void* logits, const int64_t* ta
  * head; fusing the head's product into the loss is this library's design, not
  * the pages'. Forward: logit tiles are formed on the matrix cores and reduced
  * to per-row statistics over vocabulary ranges, merged as by ce_rows_finish.
- * Backward (dhidden or dweight given): per chunk of chunk_rows rows the logit
- * tiles are recomputed and turned into dL/dz (bf16, one chunk at a time in
- * the workspace), then dX = G W and dW = sum over chunks of G^T X.
+ * Backward (dhidden or dweight given): per chunk of chunk_cols vocabulary
+ * columns the logit tiles of every row are recomputed and turned into dL/dz
+ * (bf16, one chunk at a time in the workspace), then the chunk's rows of
+ * dW = G^T X and its share of dX = sum over chunks of G W_chunk.
  *
  *  T, V, H       rows, vocabulary size, hidden size (H a multiple of 8).
  *  ld_hidden     elements between rows of hidden (>= H, multiple of 8).
  *  ld_weight     elements between rows of weight (>= H, multiple of 8).
  *  ignore_index  target value of an ignored row.
  *  dhidden_dtype CE_DTYPE_F32 or CE_DTYPE_BF16.
- *  chunk_rows    rows per backward chunk (0: 4096); rounded up to 128. The
- *                workspace grows with it (about 4 V chunk_rows bytes).
+ *  chunk_cols    vocabulary columns per backward chunk (0: 8192); rounded
+ *                up to 256. The workspace grows with it (about 4 T chunk_cols
+ *                bytes, plus 2 H T for X^T and 4 H T for a bf16 dX's fp32
+ *                accumulator).
  */
 typedef struct ce_lmhead {
   int64_t T;
@@ -278,7 +281,7 @@ typedef struct ce_lmhead {
   int64_t ld_weight;
   int64_t ignore_index;
   int32_t dhidden_dtype;
-  int32_t chunk_rows;
+  int32_t chunk_cols;
 } ce_lmhead;
 
 /* Device workspace (bytes) of ce_lmhead_fwd_bwd: forward only (backward ==

@@ -283,7 +283,7 @@ def ce_split(logits, targets, *, shards=2, mask=None, segment_ids=None, num_segm
 # Loss behind a linear LM head (logits never stored whole).
 # ---------------------------------------------------------------------------
 
-def make_lmhead(hidden, weight, *, dhidden_dtype=torch.float32, chunk_rows=0,
+def make_lmhead(hidden, weight, *, dhidden_dtype=torch.float32, chunk_cols=0,
                 ignore_index=IGNORE_INDEX):
     for name, t in (("hidden", hidden), ("weight", weight)):
         if t.dtype != torch.bfloat16:
@@ -298,19 +298,19 @@ def make_lmhead(hidden, weight, *, dhidden_dtype=torch.float32, chunk_rows=0,
     p.ld_weight = _rows(weight, "weight")
     p.ignore_index = int(ignore_index)
     p.dhidden_dtype = _DTYPES[dhidden_dtype]
-    p.chunk_rows = int(chunk_rows)
+    p.chunk_cols = int(chunk_cols)
     return p
 
 
 def ce_lmhead_fwd_bwd(hidden, weight, targets, mask, z_alpha, grad_scale, loss_out, lse_out,
-                      dhidden, dweight, *, chunk_rows=0, ignore_index=IGNORE_INDEX,
+                      dhidden, dweight, *, chunk_cols=0, ignore_index=IGNORE_INDEX,
                       workspace=None, stream=None):
     """Same-named wrapper of the C entry point: hidden [T, H] bf16, weight
     [V, H] bf16, targets [T] int64, mask [T] uint8 or None, loss_out [T] f32,
     lse_out [T] f32 or None, dhidden [T, H] f32/bf16 or None, dweight [V, H]
     f32 or None (both None: forward only)."""
     p = make_lmhead(hidden, weight, dhidden_dtype=dhidden.dtype if dhidden is not None
-                    else torch.float32, chunk_rows=chunk_rows, ignore_index=ignore_index)
+                    else torch.float32, chunk_cols=chunk_cols, ignore_index=ignore_index)
     backward = dhidden is not None or dweight is not None
     need = _lib.lmhead_workspace_bytes(p, backward)
     if workspace is None:
@@ -327,7 +327,7 @@ def ce_lmhead_fwd_bwd(hidden, weight, targets, mask, z_alpha, grad_scale, loss_o
 
 
 def ce_lmhead(hidden, weight, targets, *, mask=None, z_alpha=0.0, grad_scale=1.0,
-              want_grad=True, dhidden_dtype=torch.float32, chunk_rows=0,
+              want_grad=True, dhidden_dtype=torch.float32, chunk_cols=0,
               ignore_index=IGNORE_INDEX):
     """Allocate and run. Returns ``(loss[T], lse[T], dhidden or None, dweight or None)``."""
     T, H = hidden.shape
@@ -338,5 +338,5 @@ def ce_lmhead(hidden, weight, targets, *, mask=None, z_alpha=0.0, grad_scale=1.0
     dh = torch.empty((T, H), dtype=dhidden_dtype, device=dev) if want_grad else None
     dw = torch.empty((V, H), dtype=torch.float32, device=dev) if want_grad else None
     ce_lmhead_fwd_bwd(hidden, weight, targets, mask, z_alpha, grad_scale, loss, lse, dh, dw,
-                      chunk_rows=chunk_rows, ignore_index=ignore_index)
+                      chunk_cols=chunk_cols, ignore_index=ignore_index)
     return loss, lse, dh, dw

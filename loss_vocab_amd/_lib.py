@@ -68,7 +68,7 @@ class CeLmhead(ctypes.Structure):
         ("ld_weight", ctypes.c_int64),
         ("ignore_index", ctypes.c_int64),
         ("dhidden_dtype", ctypes.c_int32),
-        ("chunk_rows", ctypes.c_int32),
+        ("chunk_cols", ctypes.c_int32),
     ]
 
 

@@ -10,14 +10,16 @@
 //    and the saved per-row state (the collapse-free loss of torchtitan PR #5661,
 //    revised PR description, Numerics; the split over vocabulary ranges is its
 //    vocabulary-parallel merge, third review inline diff);
-//  * backward, per chunk of rows: the logit tiles are recomputed and turned into
-//    G = dL/dz from the saved state (approving review, "What this PR does":
-//    rebuild the softmax, put the target gradient in its slot, scale), written
-//    as bf16 in both orientations for one chunk only; then dX = G W and
-//    dW += G^T X run on the same matrix-core kernel.
-// Every product is C = A B^T with both operands K-contiguous; W^T and the
-// chunk's X^T are formed once by a transpose kernel so that dX and dW take the
-// same form.
+//  * backward, per chunk of vocabulary columns: the logit tiles of every row
+//    are recomputed and turned into G = dL/dz from the saved state (approving
+//    review, "What this PR does": rebuild the softmax, put the target gradient
+//    in its slot, scale), written as bf16 in both orientations for that chunk
+//    only; then the chunk's rows of dW = G^T X and its share of dX += G W run
+//    on the same matrix-core kernel, with operands that fit the last-level
+//    cache.
+// Every product is C = A B^T with both operands K-contiguous; X^T and the
+// chunk's W^T are formed by a transpose kernel so that dX and dW take that
+// form.
 
 #include <hip/hip_runtime.h>
 
@@ -33,24 +35,39 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;          // tile rows (A rows)
-constexpr int kBN = 128;          // tile columns (B rows)
-constexpr int kBK = 64;           // K per LDS stage
-constexpr int kLdsRow = kBK + 8;  // padded LDS row in bf16 (144 bytes)
-constexpr int kThreads = 256;     // 4 waves, 2 x 2, each a 64 x 64 sub-tile
-constexpr int kCRow = kBN + 4;    // padded fp32 row of the epilogue tile
+constexpr int kBM = 256;          // tile rows (A rows)
+constexpr int kBN = 256;          // tile columns (B rows)
+#ifndef LM_BK
+#define LM_BK 64
+#endif
+#ifndef LM_STAGES
+#define LM_STAGES 2
+#endif
+constexpr int kBK = LM_BK;        // K per LDS stage (32 or 64)
+constexpr int kStages = LM_STAGES;  // LDS ring: kStages - 1 stages in flight while one is consumed
+constexpr int kCPR = kBK / 8;     // 16-byte chunks per row of a stage
+constexpr int kLoadsPerStage = 2 * kBM * kCPR / 256;   // buffer loads per thread per stage
+constexpr int kThreads = 256;     // 4 waves, 2 x 2, each a 128 x 128 sub-tile of 4 x 4 MFMA blocks
+constexpr int kChunks = kBM * kBK / 8;   // 16-byte chunks per operand stage (1024)
+constexpr int kBand = 64;         // epilogue rows per LDS band
+constexpr int kCRow = kBN + 4;    // padded fp32 row of the epilogue band
 constexpr int kRowState = 8;
 constexpr float kL2E = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past every operand window
 
-// LDS: two operand stages, reused as the fp32 epilogue tile.
-struct OperandStages {
-  uint16_t a[2][kBM][kLdsRow];
-  uint16_t b[2][kBN][kLdsRow];
+// LDS: a ring of stages of both operands as 16-byte chunks; chunk c of row r
+// sits at r * kCPR + (c ^ ((r / (8 / kCPR)) % kCPR)), so the eight rows that
+// eight consecutive lanes read land on distinct banks. Reused as the fp32
+// epilogue band.
+struct Stages {
+  u32x4 a[kStages][kChunks];
+  u32x4 b[kStages][kChunks];
 };
-constexpr size_t kSmemBytes = sizeof(OperandStages) > sizeof(float) * kBM * kCRow
-                                  ? sizeof(OperandStages)
-                                  : sizeof(float) * kBM * kCRow;
+__device__ __forceinline__ int swz(int row, int kc) {
+  return row * kCPR + (kc ^ ((row / (8 / kCPR)) % kCPR));
+}
+static_assert(sizeof(float) * kBand * kCRow <= sizeof(Stages), "band fits in the stages");
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -62,7 +79,7 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// A row-major bf16 operand [rows, K] with K contiguous.
+// A row-major bf16 operand [rows, ld] with K contiguous.
 struct Operand {
   const uint16_t* p;
   int64_t rows;
@@ -72,7 +89,6 @@ struct Operand {
 struct GemmParams {
   Operand a, b;
   int64_t M, N, K;
-  // tile walk
   int32_t tiles_m, tiles_n;   // tiles of the problem
   int32_t n_ranges;           // statistics: vocabulary ranges (grid = tiles_m * n_ranges)
   // statistics
@@ -81,112 +97,143 @@ struct GemmParams {
   // gradient
   const float* row_state;     // [M, 8] state of the A rows
   float grad_scale;
-  uint16_t* g;                // [M rows of the chunk, ld_g] row-major G
+  int64_t v0;                 // vocabulary index of B row 0 (targets are global)
+  uint16_t* g;                // [M, ld_g] row-major G of this column chunk
   int64_t ld_g;
-  uint16_t* gt;               // [tiles_n * 128, ld_gt] transposed G
+  uint16_t* gt;               // [tiles_n * kBN, ld_gt] transposed G
   int64_t ld_gt;
   int64_t zero_rows;          // rows >= this (within the chunk) are written as 0
   // store
   void* c;
   int64_t ld_c;
-  int32_t c_bf16;
   int32_t accumulate;
 };
 
-// Loads of one K stage: 4 chunks of A and 4 of B per thread, 16 bytes each.
-struct StageRegs {
-  u32x4 a[4], b[4];
-};
+// Buffer window over the tile's rows [r0, r0 + 256) of an operand: loads past
+// its last row or with an offset of kOutOfRange read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const Operand& o, int64_t r0) {
+  const int64_t rows = o.rows - r0 < kBM ? o.rows - r0 : kBM;
+  const uint32_t bytes = rows > 0 ? static_cast<uint32_t>(rows * o.ld * 2) : 0u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(o.p + (rows > 0 ? r0 * o.ld : 0)),
+                                           0, bytes, 0x00020000);
+}
 
-__device__ __forceinline__ void load_stage(const GemmParams& p, int64_t m0, int64_t n0, int64_t k0,
-                                           StageRegs& r) {
-  const int tid = threadIdx.x;
+// One K stage of one operand, HBM -> LDS without registers: wave w fills row
+// groups i * 4 + w (8 rows each); lane l of a group loads row 8 g + l / 8,
+// chunk (l % 8) ^ (row % 8), which lands at LDS chunk 64 g + l.
+// Wave w fills row groups i * 4 + w (64 / kCPR rows each); lane l of a group
+// loads row g * 64 / kCPR + l / kCPR and the chunk that swz places at LDS
+// chunk 64 g + l.
+__device__ __forceinline__ void load_operand(__amdgpu_buffer_rsrc_t rsrc, const Operand& o,
+                                             int64_t K, int64_t k0, u32x4* stage) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c >> 3, kc = c & 7;
+  for (int i = 0; i < kBM * kCPR / kThreads; ++i) {
+    const int grp = i * 4 + wave;
+    const int row = grp * (64 / kCPR) + lane / kCPR;
+    const int kc = (lane % kCPR) ^ ((row / (8 / kCPR)) % kCPR);
     const int64_t k = k0 + kc * 8;
-    const bool kin = k < p.K;
-    const int64_t kk = kin ? k : 0;
-    const int64_t ra = std::min<int64_t>(m0 + row, p.a.rows - 1);
-    const int64_t rb = std::min<int64_t>(n0 + row, p.b.rows - 1);
-    const u32x4 va = *reinterpret_cast<const u32x4*>(p.a.p + ra * p.a.ld + kk);
-    const u32x4 vb = *reinterpret_cast<const u32x4*>(p.b.p + rb * p.b.ld + kk);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    r.a[i] = kin ? va : zero;
-    r.b[i] = kin ? vb : zero;
+    const uint32_t off = k < K ? static_cast<uint32_t>((row * o.ld + k) * 2) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(stage + grp * 64), 16, off, 0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_stage(OperandStages& s, int buf, const StageRegs& r) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + kThreads * i;
-    const int row = c >> 3, kc = c & 7;
-    *reinterpret_cast<u32x4*>(&s.a[buf][row][kc * 8]) = r.a[i];
-    *reinterpret_cast<u32x4*>(&s.b[buf][row][kc * 8]) = r.b[i];
-  }
-}
+// Wait until at most n stages of this thread's loads are still in flight
+// (loads complete in issue order; vmcnt is an immediate).
+// s_waitcnt immediate for vmcnt(n) with no wait on the other counters.
+constexpr int vmcnt_imm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 
-// acc[mi][ni] covers rows wm*64 + mi*32 + {8(q/4) + 4(lane/32) + q%4} and
-// column wn*64 + ni*32 + lane%32 of the tile (q = register index 0..15).
-__device__ __forceinline__ void tile_product(const GemmParams& p, OperandStages& s, int64_t m0,
-                                             int64_t n0, f32x16 (&acc)[2][2]) {
+__device__ __forceinline__ void wait_stages_left(int64_t n) {
+  if constexpr (kStages >= 4) {
+    if (n >= 2) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage));
+      return;
+    }
+  }
+  if constexpr (kStages >= 3) {
+    if (n >= 1) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStage));
+      return;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+static_assert(kStages <= 4 && 2 * kLoadsPerStage <= 63, "vmcnt holds the loads in flight");
+
+// acc[mi][ni] covers rows wm*128 + mi*32 + {8(q/4) + 4(lane/32) + q%4} and
+// column wn*128 + ni*32 + lane%32 of the tile (q = register index 0..15).
+__device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int64_t m0,
+                                             int64_t n0, f32x16 (&acc)[4][4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
+  const __amdgpu_buffer_rsrc_t ra = window(p.a, m0), rb = window(p.b, n0);
   const int64_t nk = (p.K + kBK - 1) / kBK;
-  StageRegs r;
-  load_stage(p, m0, n0, 0, r);
-  store_stage(s, 0, r);
+  // prologue: stages 0 .. kStages - 2 in flight, wait for stage 0
+  for (int64_t j = 0; j < kStages - 1 && j < nk; ++j) {
+    load_operand(ra, p.a, p.K, j * kBK, s.a[j]);
+    load_operand(rb, p.b, p.K, j * kBK, s.b[j]);
+  }
+  wait_stages_left(std::min<int64_t>(kStages - 2, nk - 1));
   __syncthreads();
   for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = static_cast<int>(kt & 1);
-    const bool more = kt + 1 < nk;
-    if (more) load_stage(p, m0, n0, (kt + 1) * kBK, r);
+    const int slot = static_cast<int>(kt % kStages);
+    const int64_t ahead = kt + kStages - 1;
+    if (ahead < nk) {
+      const int ws = static_cast<int>(ahead % kStages);
+      load_operand(ra, p.a, p.K, ahead * kBK, s.a[ws]);
+      load_operand(rb, p.b, p.K, ahead * kBK, s.b[ws]);
+    }
+    const u32x4* sa = s.a[slot];
+    const u32x4* sb = s.b[slot];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int kof = ks * 16 + (lane >> 5) * 8;
-      bf16x8 af[2], bfr[2];
+      const int kc = ks * 2 + (lane >> 5);
+      bf16x8 af[4], bfr[4];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(&s.a[buf][wm * 64 + mi * 32 + (lane & 31)][kof]);
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = __builtin_bit_cast(bf16x8, sa[swz(wm * 128 + mi * 32 + (lane & 31), kc)]);
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bfr[ni] = *reinterpret_cast<const bf16x8*>(&s.b[buf][wn * 64 + ni * 32 + (lane & 31)][kof]);
+      for (int ni = 0; ni < 4; ++ni)
+        bfr[ni] = __builtin_bit_cast(bf16x8, sb[swz(wn * 128 + ni * 32 + (lane & 31), kc)]);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < 4; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
     }
-    if (more) store_stage(s, buf ^ 1, r);
+    // stage kt + 1 must have landed: the stages after it may stay in flight
+    wait_stages_left(std::min<int64_t>(kStages - 2, std::max<int64_t>(0, nk - 2 - kt)));
     __syncthreads();
   }
 }
 
-// Spill the accumulators to the fp32 LDS tile (after the operand stages are
-// no longer read: tile_product ends with a barrier).
-__device__ __forceinline__ void acc_to_lds(float (*cs)[kCRow], const f32x16 (&acc)[2][2]) {
+// Rows [64 band, 64 band + 64) of the tile into the fp32 LDS band. Only the
+// two waves that own those rows write (wm = band / 2, mi = 2 (band % 2) + 0/1).
+__device__ __forceinline__ void band_to_lds(float (*cs)[kCRow], const f32x16 (&acc)[4][4],
+                                            int band) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  if (wm != band / 2) return;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int h = 0; h < 2; ++h) {
+    const int mi = 2 * (band % 2) + h;
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int row = wm * 64 + mi * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int col = wn * 64 + ni * 32 + (lane & 31);
+        const int row = h * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+        const int col = wn * 128 + ni * 32 + (lane & 31);
         cs[row][col] = acc[mi][ni][q];
       }
+  }
 }
 
 // Merge a (shift, sum) partial in log2 units into (mL, s); -inf shifts carry
@@ -198,183 +245,217 @@ __device__ __forceinline__ void merge(float& mL, float& s, float m2, float s2) {
   mL = mn;
 }
 
-// Statistics: grid = tiles_m * n_ranges; workgroup (mt, range) walks the
-// vocabulary tiles of its range. Thread (row = tid / 2, half = tid % 2)
-// reduces 64 columns of one row per tile.
+// Statistics: grid = tiles_m * n_ranges, range = block % n_ranges (so the
+// workgroups of one XCD walk one range and share its weight tiles); each
+// walks the vocabulary tiles of its range. Per tile and band, thread
+// (row = tid / 4, quarter = tid % 4) reduces 64 columns of one row.
 __global__ __launch_bounds__(kThreads) void lm_stats_kernel(GemmParams p) {
-  __shared__ __align__(16) unsigned char smem[kSmemBytes];
-  OperandStages& s = *reinterpret_cast<OperandStages*>(smem);
-  float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(smem);
-  const int mt = blockIdx.x % p.tiles_m;
-  const int range = blockIdx.x / p.tiles_m;
+  __shared__ __align__(16) Stages s;
+  float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
+  const int range = blockIdx.x % p.n_ranges;
+  const int mt = blockIdx.x / p.n_ranges;
   const int64_t per = (p.tiles_n + p.n_ranges - 1) / p.n_ranges;
   const int64_t nt0 = range * per, nt1 = std::min<int64_t>(p.tiles_n, nt0 + per);
   const int64_t m0 = static_cast<int64_t>(mt) * kBM;
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int64_t gr = m0 + row;
-  const int64_t t = gr < p.M ? p.targets[gr] : -1;
-  float mL = kNegInf, sum = 0.f, zt = kNegInf;
-  f32x16 acc[2][2];
+  const int row = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  int64_t t[4];
+  float mL[4], sum[4], zt[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t gr = m0 + b * kBand + row;
+    t[b] = gr < p.M ? p.targets[gr] : -1;
+    mL[b] = kNegInf;
+    sum[b] = 0.f;
+    zt[b] = kNegInf;
+  }
+  f32x16 acc[4][4];
   for (int64_t nt = nt0; nt < nt1; ++nt) {
     const int64_t n0 = nt * kBN;
     tile_product(p, s, m0, n0, acc);
-    acc_to_lds(cs, acc);
-    __syncthreads();
-    // two reads of the row's 64 columns from LDS: masked max, then the sum
-    const int64_t c0 = n0 + half * 64;
-    const int64_t tl = t - c0;                     // target's column in this half, if any
+    const int64_t c0 = n0 + quarter * 64;
     const int64_t nv = std::min<int64_t>(64, p.N - c0);   // columns inside the vocabulary
-    if (tl >= 0 && tl < 64) zt = cs[row][half * 64 + static_cast<int>(tl)];
-    float gmax = kNegInf;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      band_to_lds(cs, acc, b);
+      __syncthreads();
+      // two reads of the row's 64 columns: masked max, then the sum
+      const int64_t tl = t[b] - c0;
+      const float* crow = &cs[row][quarter * 64];
+      if (tl >= 0 && tl < 64) zt[b] = crow[tl];
+      float gmax = kNegInf;
 #pragma unroll 16
-    for (int j = 0; j < 64; ++j) {
-      const float v = cs[row][half * 64 + j];
-      gmax = fmaxf(gmax, (j < nv && j != tl) ? v : kNegInf);
-    }
-    const float mn = fmaxf(mL, gmax * kL2E);
-    if (mn != kNegInf) {
-      float acc_s = 0.f;
+      for (int j = 0; j < 64; ++j) gmax = fmaxf(gmax, (j < nv && j != tl) ? crow[j] : kNegInf);
+      const float mn = fmaxf(mL[b], gmax * kL2E);
+      if (mn != kNegInf) {
+        float acc_s = 0.f;
 #pragma unroll 16
-      for (int j = 0; j < 64; ++j) {
-        const float v = (j < nv && j != tl) ? cs[row][half * 64 + j] : kNegInf;
-        acc_s += fexp2(__builtin_fmaf(v, kL2E, -mn));
+        for (int j = 0; j < 64; ++j) {
+          const float v = (j < nv && j != tl) ? crow[j] : kNegInf;
+          acc_s += fexp2(__builtin_fmaf(v, kL2E, -mn));
+        }
+        sum[b] = (mL[b] == kNegInf ? 0.f : sum[b] * fexp2(mL[b] - mn)) + acc_s;
+        mL[b] = mn;
       }
-      sum = (mL == kNegInf ? 0.f : sum * fexp2(mL - mn)) + acc_s;
-      mL = mn;
+      __syncthreads();   // the band is rewritten next (or the stages reloaded)
     }
-    __syncthreads();   // the LDS tile is overwritten by the next tile's stages
   }
-  // the two halves of a row meet in adjacent lanes
-  const float m2 = __shfl_xor(mL, 1, 64);
-  const float s2 = __shfl_xor(sum, 1, 64);
-  const float z2 = __shfl_xor(zt, 1, 64);
-  merge(mL, sum, m2, s2);
-  zt = fmaxf(zt, z2);
-  if (half == 0 && gr < p.M) {
-    float* st = p.stats + 3 * (static_cast<int64_t>(range) * p.M + gr);
-    st[0] = mL;
-    st[1] = sum;
-    st[2] = zt;
+  // the four quarters of a row sit in adjacent lanes
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int off = 1; off <= 2; off <<= 1) {
+      const float m2 = __shfl_xor(mL[b], off, 64);
+      const float s2 = __shfl_xor(sum[b], off, 64);
+      const float z2 = __shfl_xor(zt[b], off, 64);
+      merge(mL[b], sum[b], m2, s2);
+      zt[b] = fmaxf(zt[b], z2);
+    }
+    const int64_t gr = m0 + b * kBand + row;
+    if (quarter == 0 && gr < p.M) {
+      float* st = p.stats + 3 * (static_cast<int64_t>(range) * p.M + gr);
+      st[0] = mL[b];
+      st[1] = sum[b];
+      st[2] = zt[b];
+    }
   }
 }
 
-// Gradient tiles of one chunk: grid = tiles_m * tiles_n, tile order chosen so
-// that consecutive workgroups share the weight tile.
-__global__ __launch_bounds__(kThreads) void lm_grad_kernel(GemmParams p) {
-  __shared__ __align__(16) unsigned char smem[kSmemBytes];
-  OperandStages& s = *reinterpret_cast<OperandStages*>(smem);
-  float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(smem);
-  const int mt = blockIdx.x % p.tiles_m;
-  const int nt = blockIdx.x / p.tiles_m;
-  const int64_t m0 = static_cast<int64_t>(mt) * kBM, n0 = static_cast<int64_t>(nt) * kBN;
-  f32x16 acc[2][2];
-  tile_product(p, s, m0, n0, acc);
-  acc_to_lds(cs, acc);
-  __syncthreads();
+// Tile order of the one-tile-per-workgroup kernels: blocks are dealt to the 8
+// XCDs in turn, so XCD x gets blocks x, x + 8, ...; those are mapped to one
+// contiguous run of tiles, M fastest, so the workgroups of an XCD share the B
+// tile they work on (and its L2).
+__device__ __forceinline__ void tile_of_block(const GemmParams& p, int64_t& m0, int64_t& n0,
+                                              bool& live) {
+  const int64_t ntiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
+  const int64_t per = (ntiles + 7) / 8;
+  const int64_t id = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  live = id < ntiles;
+  m0 = (id % p.tiles_m) * kBM;
+  n0 = (id / p.tiles_m) * kBN;
+}
 
-  // rows: dL/dz in place in the LDS tile, then row-major bf16 stores
-  {
-    const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int64_t gr = m0 + row;
-    float cnt = 0.f, gt = 0.f, kl = 0.f, fill = 0.f;
-    int64_t t = -1;
-    bool live = false;
-    if (gr < p.zero_rows) {
-      const float* rs = p.row_state + kRowState * gr;
-      const float kind = rs[5];
-      if (kind == 0.f) {
-        const float zw = p.grad_scale * rs[4];
-        kl = rs[0];
-        cnt = zw + zw * rs[3];
-        gt = -zw * rs[1] + zw * rs[3] * rs[2];
-        t = p.targets[gr];
-        live = true;
-      } else {
-        fill = (kind == 1.f) ? 0.f : __builtin_nanf("");
+// Gradient tiles of one column chunk: G = dL/dz for all rows and the chunk's
+// vocabulary columns, written row-major and transposed.
+__global__ __launch_bounds__(kThreads) void lm_grad_kernel(GemmParams p) {
+  __shared__ __align__(16) Stages s;
+  float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
+  int64_t m0, n0;
+  bool live_tile;
+  tile_of_block(p, m0, n0, live_tile);
+  if (!live_tile) return;
+  f32x16 acc[4][4];
+  tile_product(p, s, m0, n0, acc);
+  const int row = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    band_to_lds(cs, acc, b);
+    __syncthreads();
+    // rows: dL/dz in place in the band, then row-major bf16 stores
+    {
+      const int64_t gr = m0 + b * kBand + row;
+      float cnt = 0.f, gtv = 0.f, kl = 0.f, fill = 0.f;
+      int64_t t = -1;
+      bool live = false;
+      if (gr < p.zero_rows) {
+        const float* rs = p.row_state + kRowState * gr;
+        const float kind = rs[5];
+        if (kind == 0.f) {
+          const float zw = p.grad_scale * rs[4];
+          kl = rs[0];
+          cnt = zw + zw * rs[3];
+          gtv = -zw * rs[1] + zw * rs[3] * rs[2];
+          t = p.targets[gr];
+          live = true;
+        } else {
+          fill = (kind == 1.f) ? 0.f : __builtin_nanf("");
+        }
+      }
+      const int64_t c0 = n0 + quarter * 64;
+      float* crow = &cs[row][quarter * 64];
+      uint16_t* dst = gr < p.M ? p.g + gr * p.ld_g + c0 : nullptr;
+#pragma unroll
+      for (int j0 = 0; j0 < 64; j0 += 8) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int j = j0 + e;
+          const int64_t col = c0 + j;
+          float gv;
+          if (col >= p.N) {
+            gv = 0.f;
+          } else if (!live) {
+            gv = fill;
+          } else if (col + p.v0 == t) {
+            gv = gtv;
+          } else {
+            gv = cnt * fexp2(__builtin_fmaf(crow[j], kL2E, -kl));
+          }
+          const uint16_t h = to_bf16(gv);
+          crow[j] = __uint_as_float(static_cast<uint32_t>(h) << 16);
+          if (e & 1)
+            w[e >> 1] |= static_cast<uint32_t>(h) << 16;
+          else
+            w[e >> 1] = h;
+        }
+        if (dst) {
+          const u32x4 v = {w[0], w[1], w[2], w[3]};
+          *reinterpret_cast<u32x4*>(dst + j0) = v;
+        }
       }
     }
-    const int64_t c0 = n0 + half * 64;
-    uint16_t out[64];
+    __syncthreads();
+    // columns: transposed bf16 stores (rows of G^T); one column per thread
+    {
+      const int col = threadIdx.x;
+      uint16_t* dst = p.gt + (n0 + col) * p.ld_gt + m0 + b * kBand;
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const int64_t col = c0 + j;
-      float g;
-      if (col >= p.N) {
-        g = 0.f;
-      } else if (!live) {
-        g = fill;
-      } else if (col == t) {
-        g = gt;
-      } else {
-        g = cnt * fexp2(__builtin_fmaf(cs[row][half * 64 + j], kL2E, -kl));
-      }
-      out[j] = to_bf16(g);
-      cs[row][half * 64 + j] = __uint_as_float(static_cast<uint32_t>(out[j]) << 16);
-    }
-    if (gr < p.M) {
-      uint16_t* dst = p.g + gr * p.ld_g + c0;
-#pragma unroll
-      for (int j = 0; j < 64; j += 8) {
-        u32x4 v;
-        v.x = out[j] | (static_cast<uint32_t>(out[j + 1]) << 16);
-        v.y = out[j + 2] | (static_cast<uint32_t>(out[j + 3]) << 16);
-        v.z = out[j + 4] | (static_cast<uint32_t>(out[j + 5]) << 16);
-        v.w = out[j + 6] | (static_cast<uint32_t>(out[j + 7]) << 16);
-        *reinterpret_cast<u32x4*>(dst + j) = v;
-      }
-    }
-  }
-  __syncthreads();
-  // columns: transposed bf16 stores (rows of G^T), zeros past the chunk's rows
-  {
-    const int col = threadIdx.x >> 1, half = threadIdx.x & 1;
-    const int64_t gc = n0 + col;
-    uint16_t* dst = p.gt + gc * p.ld_gt + m0 + half * 64;
-    const int64_t rows_left = p.ld_gt - (m0 + half * 64);
-    if (rows_left >= 64) {
-#pragma unroll
-      for (int j = 0; j < 64; j += 8) {
+      for (int j = 0; j < kBand; j += 8) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = __float_as_uint(cs[half * 64 + j + 2 * e][col]) >> 16;
-          const uint32_t hi = __float_as_uint(cs[half * 64 + j + 2 * e + 1][col]) >> 16;
+          const uint32_t lo = __float_as_uint(cs[j + 2 * e][col]) >> 16;
+          const uint32_t hi = __float_as_uint(cs[j + 2 * e + 1][col]) >> 16;
           w[e] = lo | (hi << 16);
         }
         const u32x4 v = {w[0], w[1], w[2], w[3]};
         *reinterpret_cast<u32x4*>(dst + j) = v;
       }
     }
+    __syncthreads();
   }
 }
 
-// Plain product C = A B^T (fp32 or bf16 out, optional accumulate).
+// Plain product C = A B^T (fp32, optionally accumulated into C).
 __global__ __launch_bounds__(kThreads) void lm_store_kernel(GemmParams p) {
-  __shared__ __align__(16) unsigned char smem[kSmemBytes];
-  OperandStages& s = *reinterpret_cast<OperandStages*>(smem);
-  const int mt = blockIdx.x % p.tiles_m;
-  const int nt = blockIdx.x / p.tiles_m;
-  const int64_t m0 = static_cast<int64_t>(mt) * kBM, n0 = static_cast<int64_t>(nt) * kBN;
-  f32x16 acc[2][2];
+  __shared__ __align__(16) Stages s;
+  int64_t m0, n0;
+  bool live_tile;
+  tile_of_block(p, m0, n0, live_tile);
+  if (!live_tile) return;
+  f32x16 acc[4][4];
   tile_product(p, s, m0, n0, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int64_t col = n0 + wn * 64 + ni * 32 + (lane & 31);
-      if (col >= p.N) continue;
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t col = n0 + wn * 128 + ni * 32 + (lane & 31);
+      const int64_t row0 = m0 + wm * 128 + mi * 32 + 4 * (lane >> 5);
+      // the 16 old values of a block are loaded before any is stored, so
+      // the loads are in flight together
+      float old[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * 64 + mi * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        if (row >= p.M) continue;
-        if (p.c_bf16) {
-          static_cast<uint16_t*>(p.c)[row * p.ld_c + col] = to_bf16(acc[mi][ni][q]);
-        } else {
-          float* dst = static_cast<float*>(p.c) + row * p.ld_c + col;
-          *dst = p.accumulate ? *dst + acc[mi][ni][q] : acc[mi][ni][q];
-        }
+        const int64_t row = row0 + 8 * (q >> 2) + (q & 3);
+        const bool in = col < p.N && row < p.M;
+        old[q] = (in && p.accumulate) ? static_cast<const float*>(p.c)[row * p.ld_c + col] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = row0 + 8 * (q >> 2) + (q & 3);
+        if (col >= p.N || row >= p.M) continue;
+        static_cast<float*>(p.c)[row * p.ld_c + col] = old[q] + acc[mi][ni][q];
       }
     }
 }
@@ -419,40 +500,47 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 struct LmLayout {
-  int64_t chunk, ld_pad, n_ranges, tiles_m_all, tiles_n;
-  size_t off_stats, off_state, off_wt, off_g, off_gt, off_xt, total;
+  int64_t chunk;        // vocabulary columns per backward chunk (multiple of 256)
+  int64_t t_pad;        // rows rounded up to a tile (K of dW)
+  int64_t n_ranges, tiles_m_all, tiles_n;
+  size_t off_stats, off_state, off_g, off_gt, off_wt, off_xt, off_dx, total;
 };
 
-int64_t chunk_rows_of(const ce_lmhead* p) {
-  int64_t c = p->chunk_rows > 0 ? p->chunk_rows : 4096;
-  c = round_up(std::min<int64_t>(c, std::max<int64_t>(p->T, 1)), kBM);
-  return c;
+int64_t chunk_cols_of(const ce_lmhead* p) {
+  const int64_t c = p->chunk_cols > 0 ? p->chunk_cols : 8192;
+  return round_up(std::min<int64_t>(c, std::max<int64_t>(p->V, 1)), kBN);
 }
 
-LmLayout layout(const ce_lmhead* p, bool backward) {
+LmLayout layout(const ce_lmhead* p, bool backward, bool dx32) {
   LmLayout L{};
-  L.chunk = chunk_rows_of(p);
+  L.chunk = chunk_cols_of(p);
+  L.t_pad = round_up(std::max<int64_t>(p->T, 1), kBM);
   L.tiles_n = (p->V + kBN - 1) / kBN;
-  L.ld_pad = L.tiles_n * kBN;                       // padded vocabulary (zeros past V)
   L.tiles_m_all = (p->T + kBM - 1) / kBM;
-  // about 2048 workgroups (8 per compute unit of the 256), at least one tile each
-  const int64_t want = 2048;
-  L.n_ranges = std::max<int64_t>(1, std::min<int64_t>(L.tiles_n, (want + L.tiles_m_all - 1) /
-                                                                    std::max<int64_t>(L.tiles_m_all, 1)));
+  // one workgroup per compute unit (256), in a power-of-two number of ranges
+  // so that the workgroups of an XCD (block % 8) share one range
+  const int64_t tm = std::max<int64_t>(L.tiles_m_all, 1);
+  const int64_t want = (256 + tm - 1) / tm;
+  int64_t nr = 1;
+  while (nr < want && nr < L.tiles_n) nr *= 2;
+  L.n_ranges = std::min<int64_t>(nr, L.tiles_n);
   size_t off = 0;
   L.off_stats = off;
   off += align_up(static_cast<size_t>(L.n_ranges) * p->T * 3 * sizeof(float));
   L.off_state = off;
   off += align_up(static_cast<size_t>(p->T) * kRowState * sizeof(float));
   if (backward) {
-    L.off_wt = off;
-    off += align_up(static_cast<size_t>(p->H) * L.ld_pad * 2);
-    L.off_g = off;
-    off += align_up(static_cast<size_t>(L.chunk) * L.ld_pad * 2);
-    L.off_gt = off;
-    off += align_up(static_cast<size_t>(L.ld_pad) * L.chunk * 2);
-    L.off_xt = off;
-    off += align_up(static_cast<size_t>(p->H) * L.chunk * 2);
+    const size_t H = static_cast<size_t>(p->H);
+    L.off_g = off;     // G of a chunk [t_pad, chunk]
+    off += align_up(static_cast<size_t>(L.t_pad) * L.chunk * 2);
+    L.off_gt = off;    // G^T of a chunk [chunk, t_pad]
+    off += align_up(static_cast<size_t>(L.chunk) * L.t_pad * 2);
+    L.off_wt = off;    // W^T of a chunk [H, chunk]
+    off += align_up(H * L.chunk * 2);
+    L.off_xt = off;    // X^T [H, t_pad]
+    off += align_up(H * L.t_pad * 2);
+    L.off_dx = off;    // fp32 dX accumulator when dX is bf16
+    if (dx32) off += align_up(static_cast<size_t>(p->T) * H * 4);
   }
   L.total = off;
   return L;
@@ -467,11 +555,31 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a && b && an && bn && a0 < b0 + bn && b0 < a0 + an;
 }
 
+// One-tile-per-workgroup kernels get 8 * ceil(tiles / 8) blocks: the XCD
+// mapping of tile_of_block covers every tile only then (the extra blocks exit).
+int64_t tile_blocks(int64_t tiles) { return (tiles + 7) / 8 * 8; }
+
 ce_status launch(void (*kern)(GemmParams), int64_t blocks, const GemmParams& gp, hipStream_t st) {
   if (blocks <= 0) return CE_OK;
   if (blocks > INT32_MAX) return CE_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st, gp);
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+ce_status launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
+                           int64_t Rp, int64_t ld_out, hipStream_t st) {
+  hipLaunchKernelGGL(lm_transpose_kernel,
+                     dim3(static_cast<unsigned>(Rp / 64), static_cast<unsigned>((C + 63) / 64)),
+                     dim3(256), 0, st, in, R, C, ld_in, out, Rp, ld_out);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+// fp32 [n] -> bf16 [n], round to nearest even.
+__global__ __launch_bounds__(256) void lm_to_bf16_kernel(const float* __restrict__ in, int64_t n,
+                                                         uint16_t* __restrict__ out) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    out[i] = to_bf16(in[i]);
 }
 
 }  // namespace
@@ -480,7 +588,7 @@ extern "C" {
 
 size_t ce_lmhead_workspace_bytes(const ce_lmhead* p, int32_t backward) {
   if (p == nullptr || p->T < 0 || p->V < 1 || p->H < 1) return 0;
-  return layout(p, backward != 0).total;
+  return layout(p, backward != 0, p->dhidden_dtype == CE_DTYPE_BF16).total;
 }
 
 ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* weight,
@@ -490,23 +598,27 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
                             void* stream_ptr) {
   if (p == nullptr) return CE_ERR_INVALID_ARG;
   const int64_t T = p->T, V = p->V, H = p->H;
-  if (T < 0 || V < 1 || H < 1 || p->chunk_rows < 0) return CE_ERR_INVALID_ARG;
+  if (T < 0 || V < 1 || H < 1 || p->chunk_cols < 0) return CE_ERR_INVALID_ARG;
   if (p->ld_hidden < H || p->ld_weight < H) return CE_ERR_INVALID_ARG;
   if (p->dhidden_dtype != CE_DTYPE_F32 && p->dhidden_dtype != CE_DTYPE_BF16) return CE_ERR_INVALID_ARG;
   if (!std::isfinite(z_alpha) || !std::isfinite(grad_scale)) return CE_ERR_INVALID_ARG;
-  if (H % 8 != 0 || T > INT32_MAX || V > (int64_t{1} << 30) || H > (int64_t{1} << 20))
+  // operand windows of 256 rows are addressed with 31-bit byte offsets
+  constexpr int64_t kMaxLd = int64_t{1} << 21;
+  if (H % 8 != 0 || T > kMaxLd - kBM || V > kMaxLd - kBN || p->ld_hidden > kMaxLd ||
+      p->ld_weight > kMaxLd)
     return CE_ERR_UNSUPPORTED;
   if (!weight || (T > 0 && (!hidden || !targets || !loss_out))) return CE_ERR_INVALID_ARG;
   if ((hidden && !aligned16(hidden, p->ld_hidden)) || !aligned16(weight, p->ld_weight))
     return CE_ERR_UNSUPPORTED;
   const bool backward = dhidden != nullptr || dweight != nullptr;
-  const LmLayout L = layout(p, backward);
+  const bool dx_bf16 = p->dhidden_dtype == CE_DTYPE_BF16;
+  const LmLayout L = layout(p, backward, dx_bf16);
   if (workspace_bytes < L.total || (L.total > 0 && workspace == nullptr)) return CE_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return CE_ERR_WORKSPACE;
-  // outputs may not overlap the inputs
+  // outputs may not overlap the inputs or the workspace
   const size_t x_bytes = T > 0 ? static_cast<size_t>((T - 1) * p->ld_hidden + H) * 2 : 0;
   const size_t w_bytes = static_cast<size_t>((V - 1) * p->ld_weight + H) * 2;
-  const size_t dh_bytes = static_cast<size_t>(T * H) * (p->dhidden_dtype == CE_DTYPE_F32 ? 4 : 2);
+  const size_t dh_bytes = static_cast<size_t>(T * H) * (dx_bf16 ? 2 : 4);
   const size_t dw_bytes = static_cast<size_t>(V * H) * 4;
   const void* outs[4] = {loss_out, lse_out, dhidden, dweight};
   const size_t out_n[4] = {static_cast<size_t>(T) * 4, static_cast<size_t>(T) * 4, dh_bytes, dw_bytes};
@@ -565,78 +677,84 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
   }
   if (!backward) return CE_OK;
 
-  // ---- backward, chunk by chunk ----
-  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.off_wt);
+  // ---- backward, one chunk of vocabulary columns at a time ----
+  // G = dL/dz of the chunk for every row; dW rows of the chunk = G^T X
+  // (K = T); dX += G W_chunk (K = chunk). Every operand of a chunk stays far
+  // below the 256 MB last-level cache.
   uint16_t* g = reinterpret_cast<uint16_t*>(ws + L.off_g);
   uint16_t* gt = reinterpret_cast<uint16_t*>(ws + L.off_gt);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.off_wt);
   uint16_t* xt = reinterpret_cast<uint16_t*>(ws + L.off_xt);
-  if (dhidden) {
-    // W^T [H, ld_pad], zero past V
-    hipLaunchKernelGGL(lm_transpose_kernel,
-                       dim3(static_cast<unsigned>(L.ld_pad / 64), static_cast<unsigned>((H + 63) / 64)),
-                       dim3(256), 0, st, static_cast<const uint16_t*>(weight), V, H, p->ld_weight, wt,
-                       L.ld_pad, L.ld_pad);
-    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  float* dx = dx_bf16 ? reinterpret_cast<float*>(ws + L.off_dx) : static_cast<float*>(dhidden);
+  if (dweight) {
+    const ce_status sx = launch_transpose(X.p, T, H, X.ld, xt, L.t_pad, L.t_pad, st);   // X^T [H, t_pad]
+    if (sx != CE_OK) return sx;
   }
-  for (int64_t c0 = 0; c0 < T; c0 += L.chunk) {
-    const int64_t rows = std::min<int64_t>(L.chunk, T - c0);
-    const int64_t tiles_m = (rows + kBM - 1) / kBM;
+  const int64_t tiles_h = (H + kBN - 1) / kBN;
+  for (int64_t v0 = 0; v0 < V; v0 += L.chunk) {
+    const int64_t cols = std::min<int64_t>(L.chunk, V - v0);
+    const int64_t tiles_c = (cols + kBN - 1) / kBN;
+    const Operand Wc{W.p + v0 * W.ld, cols, W.ld};
     {
       GemmParams gp{};
-      gp.a = Operand{X.p + c0 * X.ld, rows, X.ld};
-      gp.b = W;
-      gp.M = rows;
-      gp.N = V;
+      gp.a = X;
+      gp.b = Wc;
+      gp.M = T;
+      gp.N = cols;
       gp.K = H;
-      gp.tiles_m = static_cast<int32_t>(tiles_m);
-      gp.tiles_n = static_cast<int32_t>(L.tiles_n);
-      gp.targets = targets + c0;
-      gp.row_state = state + kRowState * c0;
+      gp.tiles_m = static_cast<int32_t>(L.tiles_m_all);
+      gp.tiles_n = static_cast<int32_t>(tiles_c);
+      gp.targets = targets;
+      gp.row_state = state;
       gp.grad_scale = grad_scale;
+      gp.v0 = v0;
       gp.g = g;
-      gp.ld_g = L.ld_pad;
+      gp.ld_g = L.chunk;
       gp.gt = gt;
-      gp.ld_gt = L.chunk;
-      gp.zero_rows = rows;
-      const ce_status s3 = launch(lm_grad_kernel, tiles_m * L.tiles_n, gp, st);
+      gp.ld_gt = L.t_pad;
+      gp.zero_rows = T;
+      const ce_status s3 = launch(lm_grad_kernel, tile_blocks(L.tiles_m_all * tiles_c), gp, st);
       if (s3 != CE_OK) return s3;
     }
     if (dhidden) {
+      // W_chunk^T [H, chunk], zero past the chunk's columns
+      const ce_status sw = launch_transpose(Wc.p, cols, H, W.ld, wt, L.chunk, L.chunk, st);
+      if (sw != CE_OK) return sw;
       GemmParams gp{};
-      gp.a = Operand{g, rows, L.ld_pad};
-      gp.b = Operand{wt, H, L.ld_pad};
-      gp.M = rows;
+      gp.a = Operand{g, T, L.chunk};
+      gp.b = Operand{wt, H, L.chunk};
+      gp.M = T;
       gp.N = H;
-      gp.K = L.ld_pad;
-      gp.tiles_m = static_cast<int32_t>(tiles_m);
-      gp.tiles_n = static_cast<int32_t>((H + kBN - 1) / kBN);
-      const bool bf = p->dhidden_dtype == CE_DTYPE_BF16;
-      gp.c = static_cast<char*>(dhidden) + static_cast<size_t>(c0 * H) * (bf ? 2 : 4);
+      gp.K = round_up(cols, kBK);
+      gp.tiles_m = static_cast<int32_t>(L.tiles_m_all);
+      gp.tiles_n = static_cast<int32_t>(tiles_h);
+      gp.c = dx;
       gp.ld_c = H;
-      gp.c_bf16 = bf ? 1 : 0;
-      const ce_status s4 = launch(lm_store_kernel, tiles_m * gp.tiles_n, gp, st);
+      gp.accumulate = v0 > 0 ? 1 : 0;
+      const ce_status s4 = launch(lm_store_kernel, tile_blocks(L.tiles_m_all * tiles_h), gp, st);
       if (s4 != CE_OK) return s4;
     }
     if (dweight) {
-      // X_c^T [H, chunk], zero past the chunk's rows
-      hipLaunchKernelGGL(lm_transpose_kernel,
-                         dim3(static_cast<unsigned>(L.chunk / 64), static_cast<unsigned>((H + 63) / 64)),
-                         dim3(256), 0, st, X.p + c0 * X.ld, rows, H, X.ld, xt, L.chunk, L.chunk);
-      if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
       GemmParams gp{};
-      gp.a = Operand{gt, V, L.chunk};
-      gp.b = Operand{xt, H, L.chunk};
-      gp.M = V;
+      gp.a = Operand{gt, cols, L.t_pad};
+      gp.b = Operand{xt, H, L.t_pad};
+      gp.M = cols;
       gp.N = H;
-      gp.K = round_up(rows, kBK);
-      gp.tiles_m = static_cast<int32_t>(L.tiles_n);
-      gp.tiles_n = static_cast<int32_t>((H + kBN - 1) / kBN);
-      gp.c = dweight;
+      gp.K = L.t_pad;
+      gp.tiles_m = static_cast<int32_t>(tiles_c);
+      gp.tiles_n = static_cast<int32_t>(tiles_h);
+      gp.c = dweight + v0 * H;
       gp.ld_c = H;
-      gp.accumulate = c0 > 0 ? 1 : 0;
-      const ce_status s5 = launch(lm_store_kernel, static_cast<int64_t>(gp.tiles_m) * gp.tiles_n, gp, st);
+      const ce_status s5 = launch(lm_store_kernel, tile_blocks(tiles_c * tiles_h), gp, st);
       if (s5 != CE_OK) return s5;
     }
+  }
+  if (dhidden && dx_bf16) {
+    const int64_t n = T * H;
+    const unsigned nb = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 8192));
+    hipLaunchKernelGGL(lm_to_bf16_kernel, dim3(nb), dim3(256), 0, st, dx, n,
+                       static_cast<uint16_t*>(dhidden));
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
   return CE_OK;
 }

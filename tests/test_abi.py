@@ -275,7 +275,7 @@ def _lm(T=8, V=100, H=64, ldh=None, ldw=None, dt=0, chunk=0):
     p.ld_weight = H if ldw is None else ldw
     p.ignore_index = -100
     p.dhidden_dtype = dt
-    p.chunk_rows = chunk
+    p.chunk_cols = chunk
     return p
 
 
@@ -315,10 +315,13 @@ def test_lmhead_validation(case, pkw, kw, expect):
 
 def test_lmhead_workspace_grows_with_backward_and_chunk():
     L = _lib()
-    p = _lm(T=1000, V=5000, H=256)
+    p = _lm(T=1000, V=50000, H=256)
     fwd = L.lmhead_workspace_bytes(p, False)
     bwd = L.lmhead_workspace_bytes(p, True)
     assert 0 < fwd < bwd
-    p.chunk_rows = 128
+    p.chunk_cols = 256
     assert L.lmhead_workspace_bytes(p, True) < bwd
+    p.chunk_cols = 0
+    p.dhidden_dtype = 1      # a bf16 dX adds an fp32 accumulator
+    assert L.lmhead_workspace_bytes(p, True) > bwd
     assert L.LIB.ce_lmhead_workspace_bytes(None, 1) == 0

@@ -75,11 +75,11 @@ def check_products(got, ref, bound, what):
                              f"ref {ref[m][i]!r} bound {b[i]:.3e}")
 
 
-def run_and_compare(X, W, t, *, mask=None, z_alpha=0.0, grad_scale=1.0, chunk_rows=0,
+def run_and_compare(X, W, t, *, mask=None, z_alpha=0.0, grad_scale=1.0, chunk_cols=0,
                     dhidden_dtype=torch.float32, exact_logits=True, what=""):
     import loss_vocab_amd as L
     loss, lse, dh, dw = L.ce_lmhead(X, W, t, mask=mask, z_alpha=z_alpha, grad_scale=grad_scale,
-                                    chunk_rows=chunk_rows, dhidden_dtype=dhidden_dtype)
+                                    chunk_cols=chunk_cols, dhidden_dtype=dhidden_dtype)
     torch.cuda.synchronize()
     X64, W64 = to_np64(X), to_np64(W)
     ref = lmhead_ce(X64, W64, _np(t), mask=_np(mask), z_alpha=z_alpha, grad_scale=grad_scale)
@@ -116,14 +116,14 @@ def run_and_compare(X, W, t, *, mask=None, z_alpha=0.0, grad_scale=1.0, chunk_ro
 
 @pytest.mark.parametrize("T,V,H,chunk", [
     (128, 128, 64, 0),        # one tile
-    (300, 1000, 72, 128),     # ragged rows, vocabulary and K; three chunks
+    (300, 1000, 72, 128),     # ragged rows, vocabulary and K; four column chunks
     (257, 4099, 136, 0),      # one chunk, ragged everything
     (64, 50, 256, 0),         # vocabulary inside one tile
 ])
 def test_grid_inputs(T, V, H, chunk):
     print(f"[lmhead] grid T={T} V={V} H={H} chunk={chunk}", flush=True)
     X, W, t = grid_inputs(T, V, H, seed=T + V + H, ignore=(3, T - 1))
-    run_and_compare(X, W, t, z_alpha=1e-3, grad_scale=1.0 / T, chunk_rows=chunk,
+    run_and_compare(X, W, t, z_alpha=1e-3, grad_scale=1.0 / T, chunk_cols=chunk,
                     what=f"T{T} V{V} H{H}")
 
 
@@ -169,7 +169,7 @@ def test_gaussian_inputs():
     X, W, t = gauss_inputs(384, 3000, 512, seed=17)
     t[5] = -100
     run_and_compare(X, W, t, z_alpha=1e-4, grad_scale=1.0 / 383, exact_logits=False,
-                    chunk_rows=256, what="gauss")
+                    chunk_cols=256, what="gauss")
 
 
 def test_zero_rows():
@@ -183,19 +183,19 @@ def test_zero_rows():
 
 
 def test_mid_size_complete():
-    """T = 1024, V = 32000, H = 1024, four chunks: every element of loss, lse,
-    dX and dW against the oracle."""
+    """T = 1024, V = 32000, H = 1024, eight column chunks: every element of
+    loss, lse, dX and dW against the oracle."""
     print("[lmhead] mid T=1024 V=32000 H=1024", flush=True)
     X, W, t = gauss_inputs(1024, 32000, 1024, seed=23)
     t[::9] = -100
     run_and_compare(X, W, t, z_alpha=1e-4, grad_scale=1.0 / 900, exact_logits=False,
-                    chunk_rows=256, what="mid")
+                    chunk_cols=4096, what="mid")
 
 
 def test_full_shape_sampled():
     """T = 16384 rows of a Llama-3-8B-sized head (V = 128256, H = 4096), four
-    chunks: loss, lse and dX on sampled rows vs the oracle (its logits for those
-    rows in fp64); every output finite."""
+    column chunks: loss, lse and dX on sampled rows vs the oracle (its logits
+    for those rows in fp64); every output finite."""
     import loss_vocab_amd as L
     T, V, H = 16384, 128256, 4096
     print(f"[lmhead] full T={T} V={V} H={H}", flush=True)

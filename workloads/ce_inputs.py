@@ -225,3 +225,77 @@ def alg_bytes(w: Workload):
         nbytes += w.T * (4 + 8) + w.num_segments * 4
     return nbytes
 
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the loss behind a linear LM head: hidden states and head weight.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class LmHeadWorkload:
+    """Hidden states X [T, H] ~ N(0, 1) and head weight W [V, H] ~ N(0,
+    (sigma / sqrt(H))^2), both bf16 (RNE from fp32 draws), so the logits are
+    ~ N(0, sigma^2); targets Zipf(s) over [0, V) with an exact count of
+    ignored rows. The shape is the pages' measured one (T = 16384, V = 128256)
+    with a Llama-3-8B hidden size (H = 4096)."""
+    name: str
+    index: int
+    T: int
+    V: int
+    H: int
+    sigma: float = 2.0
+    zipf_s: float = 1.1
+    mask_frac: float = 0.2
+    z_alpha: float = 0.0
+
+    @property
+    def n_masked(self):
+        return int(round(self.mask_frac * self.T))
+
+    @property
+    def n_valid(self):
+        return self.T - self.n_masked
+
+    def scaled(self, T=None, V=None, H=None):
+        kw = {k: v for k, v in (("T", T), ("V", V), ("H", H)) if v is not None}
+        return dataclasses.replace(self, name=self.name + "_scaled", **kw)
+
+
+LMHEAD_WORKLOADS = {
+    w.name: w for w in [
+        LmHeadWorkload("lmhead_bf16_T16384_V128256_H4096", 10, 16384, 128256, 4096),
+    ]
+}
+
+
+def lmhead_flops(w: LmHeadWorkload, backward=True):
+    """Matrix-core flops of one call: the logit product once forward and once
+    more in the backward (recomputed), plus dX = G W and dW = G^T X."""
+    return (8 if backward else 2) * w.T * w.V * w.H
+
+
+def make_lmhead_inputs(w: LmHeadWorkload, device="cpu", seed_offset=0, rows=None):
+    """``hidden`` [T, H] bf16, ``weight`` [V, H] bf16, ``targets`` [T] int64.
+    ``rows`` (optional) generates only the first ``rows`` rows of hidden and
+    targets (the weight is always whole)."""
+    T = w.T if rows is None else rows
+    dev = torch.device(device)
+    k = w.index * 1000 + seed_offset
+    rng = _np_rng(k, 1)
+    tgt = _zipf_targets(w.T, w.V, w.zipf_s, rng)
+    masked = rng.choice(w.T, size=w.n_masked, replace=False) if w.n_masked else np.zeros(0, np.int64)
+    tgt[masked] = IGNORE_INDEX
+    hidden = torch.empty((T, w.H), dtype=torch.bfloat16, device=dev)
+    for c0 in range(0, T, 4096):
+        c1 = min(T, c0 + 4096)
+        g = _gen(dev, k, 2, c0 // 4096)
+        hidden[c0:c1].copy_(torch.randn((c1 - c0, w.H), generator=g, dtype=torch.float32, device=dev))
+    weight = torch.empty((w.V, w.H), dtype=torch.bfloat16, device=dev)
+    for c0 in range(0, w.V, 8192):
+        c1 = min(w.V, c0 + 8192)
+        g = _gen(dev, k, 3, c0 // 8192)
+        block = torch.randn((c1 - c0, w.H), generator=g, dtype=torch.float32, device=dev)
+        weight[c0:c1].copy_(block.mul_(w.sigma / np.sqrt(w.H)))
+    return {"hidden": hidden, "weight": weight,
+            "targets": torch.as_tensor(tgt[:T], device=dev), "z_alpha": w.z_alpha,
+            "grad_scale": 1.0 / max(1, w.n_valid)}
