@@ -127,6 +127,18 @@ def test_grid_inputs(T, V, H, chunk):
                     what=f"T{T} V{V} H{H}")
 
 
+def test_strided_operands():
+    """hidden and weight as column slices of wider buffers (row strides 80
+    and 96 elements, still 16-byte aligned)."""
+    Xb, Wb, t = grid_inputs(150, 333, 96, seed=19, ignore=(0,))
+    X = Xb[:, :64]
+    W = Wb[:, 16:80]
+    assert X.stride(0) == 96 and W.stride(0) == 96
+    Xs = torch.empty((150, 80), dtype=torch.bfloat16, device=DEV)[:, :64]
+    Xs.copy_(X)
+    run_and_compare(Xs, W, t, z_alpha=1e-3, grad_scale=0.25, chunk_cols=256, what="strided")
+
+
 def test_mask_and_bf16_dhidden():
     X, W, t = grid_inputs(200, 777, 64, seed=5)
     mask = (torch.arange(200, device=DEV) % 7 != 0).to(torch.uint8)
