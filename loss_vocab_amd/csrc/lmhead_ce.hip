@@ -124,6 +124,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const Operand& o, int64
 // Wave w fills row groups i * 4 + w (64 / kCPR rows each); lane l of a group
 // loads row g * 64 / kCPR + l / kCPR and the chunk that swz places at LDS
 // chunk 64 g + l.
+template <bool KMASK>
 __device__ __forceinline__ void load_operand(__amdgpu_buffer_rsrc_t rsrc, const Operand& o,
                                              int64_t K, int64_t k0, u32x4* stage) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -133,7 +134,7 @@ __device__ __forceinline__ void load_operand(__amdgpu_buffer_rsrc_t rsrc, const 
     const int row = grp * (64 / kCPR) + lane / kCPR;
     const int kc = (lane % kCPR) ^ ((row / (8 / kCPR)) % kCPR);
     const int64_t k = k0 + kc * 8;
-    const uint32_t off = k < K ? static_cast<uint32_t>((row * o.ld + k) * 2) : kOutOfRange;
+    const uint32_t off = (!KMASK || k < K) ? static_cast<uint32_t>((row * o.ld + k) * 2) : kOutOfRange;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc, (__attribute__((address_space(3))) void*)(stage + grp * 64), 16, off, 0, 0, 0);
   }
@@ -163,6 +164,8 @@ static_assert(kStages <= 4 && 2 * kLoadsPerStage <= 63, "vmcnt holds the loads i
 
 // acc[mi][ni] covers rows wm*128 + mi*32 + {8(q/4) + 4(lane/32) + q%4} and
 // column wn*128 + ni*32 + lane%32 of the tile (q = register index 0..15).
+// KMASK: K is not a multiple of kBK, so the last stage masks its tail.
+template <bool KMASK>
 __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int64_t m0,
                                              int64_t n0, f32x16 (&acc)[4][4]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -178,8 +181,8 @@ __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int
   const int64_t nk = (p.K + kBK - 1) / kBK;
   // prologue: stages 0 .. kStages - 2 in flight, wait for stage 0
   for (int64_t j = 0; j < kStages - 1 && j < nk; ++j) {
-    load_operand(ra, p.a, p.K, j * kBK, s.a[j]);
-    load_operand(rb, p.b, p.K, j * kBK, s.b[j]);
+    load_operand<KMASK>(ra, p.a, p.K, j * kBK, s.a[j]);
+    load_operand<KMASK>(rb, p.b, p.K, j * kBK, s.b[j]);
   }
   wait_stages_left(std::min<int64_t>(kStages - 2, nk - 1));
   __syncthreads();
@@ -188,27 +191,33 @@ __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int
     const int64_t ahead = kt + kStages - 1;
     if (ahead < nk) {
       const int ws = static_cast<int>(ahead % kStages);
-      load_operand(ra, p.a, p.K, ahead * kBK, s.a[ws]);
-      load_operand(rb, p.b, p.K, ahead * kBK, s.b[ws]);
+      load_operand<KMASK>(ra, p.a, p.K, ahead * kBK, s.a[ws]);
+      load_operand<KMASK>(rb, p.b, p.K, ahead * kBK, s.b[ws]);
     }
     const u32x4* sa = s.a[slot];
     const u32x4* sb = s.b[slot];
+    // the stage's fragments; the compiler interleaves their reads with the
+    // products (pinning all reads first, or double-buffering them per k-step,
+    // measured slower on MI355X)
+    bf16x8 af[kBK / 16][4], bfr[kBK / 16][4];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kc = ks * 2 + (lane >> 5);
-      bf16x8 af[4], bfr[4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
-        af[mi] = __builtin_bit_cast(bf16x8, sa[swz(wm * 128 + mi * 32 + (lane & 31), kc)]);
+        af[ks][mi] = __builtin_bit_cast(bf16x8, sa[swz(wm * 128 + mi * 32 + (lane & 31), kc)]);
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni)
-        bfr[ni] = __builtin_bit_cast(bf16x8, sb[swz(wn * 128 + ni * 32 + (lane & 31), kc)]);
+        bfr[ks][ni] = __builtin_bit_cast(bf16x8, sb[swz(wn * 128 + ni * 32 + (lane & 31), kc)]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks)
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
-    }
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][mi], bfr[ks][ni], acc[mi][ni],
+                                                                0, 0, 0);
     // stage kt + 1 must have landed: the stages after it may stay in flight
     wait_stages_left(std::min<int64_t>(kStages - 2, std::max<int64_t>(0, nk - 2 - kt)));
     __syncthreads();
@@ -249,7 +258,9 @@ __device__ __forceinline__ void merge(float& mL, float& s, float m2, float s2) {
 // workgroups of one XCD walk one range and share its weight tiles); each
 // walks the vocabulary tiles of its range. Per tile and band, thread
 // (row = tid / 4, quarter = tid % 4) reduces 64 columns of one row.
-__global__ __launch_bounds__(kThreads) void lm_stats_kernel(GemmParams p) {
+template <bool KMASK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_stats_kernel(
+    GemmParams p) {
   __shared__ __align__(16) Stages s;
   float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
   const int range = blockIdx.x % p.n_ranges;
@@ -271,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void lm_stats_kernel(GemmParams p) {
   f32x16 acc[4][4];
   for (int64_t nt = nt0; nt < nt1; ++nt) {
     const int64_t n0 = nt * kBN;
-    tile_product(p, s, m0, n0, acc);
+    tile_product<KMASK>(p, s, m0, n0, acc);
     const int64_t c0 = n0 + quarter * 64;
     const int64_t nv = std::min<int64_t>(64, p.N - c0);   // columns inside the vocabulary
 #pragma unroll
@@ -336,7 +347,9 @@ __device__ __forceinline__ void tile_of_block(const GemmParams& p, int64_t& m0, 
 
 // Gradient tiles of one column chunk: G = dL/dz for all rows and the chunk's
 // vocabulary columns, written row-major and transposed.
-__global__ __launch_bounds__(kThreads) void lm_grad_kernel(GemmParams p) {
+template <bool KMASK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_grad_kernel(
+    GemmParams p) {
   __shared__ __align__(16) Stages s;
   float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
   int64_t m0, n0;
@@ -344,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void lm_grad_kernel(GemmParams p) {
   tile_of_block(p, m0, n0, live_tile);
   if (!live_tile) return;
   f32x16 acc[4][4];
-  tile_product(p, s, m0, n0, acc);
+  tile_product<KMASK>(p, s, m0, n0, acc);
   const int row = threadIdx.x >> 2, quarter = threadIdx.x & 3;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -426,14 +439,16 @@ __global__ __launch_bounds__(kThreads) void lm_grad_kernel(GemmParams p) {
 }
 
 // Plain product C = A B^T (fp32, optionally accumulated into C).
-__global__ __launch_bounds__(kThreads) void lm_store_kernel(GemmParams p) {
+template <bool KMASK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_store_kernel(
+    GemmParams p) {
   __shared__ __align__(16) Stages s;
   int64_t m0, n0;
   bool live_tile;
   tile_of_block(p, m0, n0, live_tile);
   if (!live_tile) return;
   f32x16 acc[4][4];
-  tile_product(p, s, m0, n0, acc);
+  tile_product<KMASK>(p, s, m0, n0, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
@@ -566,6 +581,16 @@ ce_status launch(void (*kern)(GemmParams), int64_t blocks, const GemmParams& gp,
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 
+// The kernel instance for gp.K: K-tail masking only when K is not a multiple
+// of the stage depth.
+template <template <bool> class Sel>
+ce_status launch_k(int64_t blocks, const GemmParams& gp, hipStream_t st) {
+  return gp.K % kBK == 0 ? launch(Sel<false>::fn, blocks, gp, st) : launch(Sel<true>::fn, blocks, gp, st);
+}
+template <bool KM> struct StatsSel { static constexpr void (*fn)(GemmParams) = lm_stats_kernel<KM>; };
+template <bool KM> struct GradSel { static constexpr void (*fn)(GemmParams) = lm_grad_kernel<KM>; };
+template <bool KM> struct StoreSel { static constexpr void (*fn)(GemmParams) = lm_store_kernel<KM>; };
+
 ce_status launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_in, uint16_t* out,
                            int64_t Rp, int64_t ld_out, hipStream_t st) {
   hipLaunchKernelGGL(lm_transpose_kernel,
@@ -656,7 +681,7 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
     gp.n_ranges = static_cast<int32_t>(L.n_ranges);
     gp.targets = targets;
     gp.stats = stats;
-    const ce_status s1 = launch(lm_stats_kernel, L.tiles_m_all * L.n_ranges, gp, st);
+    const ce_status s1 = launch_k<StatsSel>(L.tiles_m_all * L.n_ranges, gp, st);
     if (s1 != CE_OK) return s1;
   }
   {
@@ -713,7 +738,7 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
       gp.gt = gt;
       gp.ld_gt = L.t_pad;
       gp.zero_rows = T;
-      const ce_status s3 = launch(lm_grad_kernel, tile_blocks(L.tiles_m_all * tiles_c), gp, st);
+      const ce_status s3 = launch_k<GradSel>(tile_blocks(L.tiles_m_all * tiles_c), gp, st);
       if (s3 != CE_OK) return s3;
     }
     if (dhidden) {
@@ -731,7 +756,7 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
       gp.c = dx;
       gp.ld_c = H;
       gp.accumulate = v0 > 0 ? 1 : 0;
-      const ce_status s4 = launch(lm_store_kernel, tile_blocks(L.tiles_m_all * tiles_h), gp, st);
+      const ce_status s4 = launch_k<StoreSel>(tile_blocks(L.tiles_m_all * tiles_h), gp, st);
       if (s4 != CE_OK) return s4;
     }
     if (dweight) {
@@ -745,7 +770,7 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
       gp.tiles_n = static_cast<int32_t>(tiles_h);
       gp.c = dweight + v0 * H;
       gp.ld_c = H;
-      const ce_status s5 = launch(lm_store_kernel, tile_blocks(tiles_c * tiles_h), gp, st);
+      const ce_status s5 = launch_k<StoreSel>(tile_blocks(tiles_c * tiles_h), gp, st);
       if (s5 != CE_OK) return s5;
     }
   }
