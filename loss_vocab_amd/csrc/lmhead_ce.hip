@@ -46,8 +46,20 @@ constexpr int kBN = 256;          // tile columns (B rows)
 constexpr int kBK = LM_BK;        // K per LDS stage (32 or 64)
 constexpr int kStages = LM_STAGES;  // LDS ring: kStages - 1 stages in flight while one is consumed
 constexpr int kCPR = kBK / 8;     // 16-byte chunks per row of a stage
-constexpr int kLoadsPerStage = 2 * kBM * kCPR / 256;   // buffer loads per thread per stage
-constexpr int kThreads = 256;     // 4 waves, 2 x 2, each a 128 x 128 sub-tile of 4 x 4 MFMA blocks
+#ifndef LM_WAVES
+#define LM_WAVES 8
+#endif
+// Waves per workgroup: 4 (2 x 2, each 128 x 128 = 4 x 4 MFMA blocks) or 8
+// (4 x 2, each 64 x 128 = 2 x 4 blocks, two waves per SIMD).
+constexpr int kWaves = LM_WAVES;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWM = kWaves / 2;               // waves along M (2 along N)
+constexpr int kRW = kBM / kWM;                // rows per wave
+constexpr int kMI = kRW / 32;                 // MFMA blocks per wave along M
+constexpr int kNI = 4;                        // ... along N (128 columns)
+constexpr int kLoadsPerStage = 2 * kBM * kCPR / kThreads;   // buffer loads per thread per stage
+constexpr int kTPR = kThreads / 64;           // epilogue threads per band row
+constexpr int kCPT = kBN / kTPR;              // band columns per epilogue thread
 constexpr int kChunks = kBM * kBK / 8;   // 16-byte chunks per operand stage (1024)
 constexpr int kBand = 64;         // epilogue rows per LDS band
 constexpr int kCRow = kBN + 4;    // padded fp32 row of the epilogue band
@@ -57,15 +69,16 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past every operand window
 
 // LDS: a ring of stages of both operands as 16-byte chunks; chunk c of row r
-// sits at r * kCPR + (c ^ ((r / (8 / kCPR)) % kCPR)), so the eight rows that
-// eight consecutive lanes read land on distinct banks. Reused as the fp32
-// epilogue band.
+// sits at r * kCPR + (c ^ ((r / (16 / kCPR)) % kCPR)). A 128-bit LDS read is
+// served 16 lanes (256 bytes, all 64 banks) at a time, and the 16 rows that 16
+// consecutive lanes read then land on 16 distinct 16-byte bank groups.
+// Reused as the fp32 epilogue band.
 struct Stages {
   u32x4 a[kStages][kChunks];
   u32x4 b[kStages][kChunks];
 };
 __device__ __forceinline__ int swz(int row, int kc) {
-  return row * kCPR + (kc ^ ((row / (8 / kCPR)) % kCPR));
+  return row * kCPR + (kc ^ ((row / (16 / kCPR)) % kCPR));
 }
 static_assert(sizeof(float) * kBand * kCRow <= sizeof(Stages), "band fits in the stages");
 
@@ -121,7 +134,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const Operand& o, int64
 // One K stage of one operand, HBM -> LDS without registers: wave w fills row
 // groups i * 4 + w (8 rows each); lane l of a group loads row 8 g + l / 8,
 // chunk (l % 8) ^ (row % 8), which lands at LDS chunk 64 g + l.
-// Wave w fills row groups i * 4 + w (64 / kCPR rows each); lane l of a group
+// Wave w fills row groups i * kWaves + w (64 / kCPR rows each); lane l of a group
 // loads row g * 64 / kCPR + l / kCPR and the chunk that swz places at LDS
 // chunk 64 g + l.
 template <bool KMASK>
@@ -130,9 +143,9 @@ __device__ __forceinline__ void load_operand(__amdgpu_buffer_rsrc_t rsrc, const 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < kBM * kCPR / kThreads; ++i) {
-    const int grp = i * 4 + wave;
+    const int grp = i * kWaves + wave;
     const int row = grp * (64 / kCPR) + lane / kCPR;
-    const int kc = (lane % kCPR) ^ ((row / (8 / kCPR)) % kCPR);
+    const int kc = (lane % kCPR) ^ ((row / (16 / kCPR)) % kCPR);
     const int64_t k = k0 + kc * 8;
     const uint32_t off = (!KMASK || k < K) ? static_cast<uint32_t>((row * o.ld + k) * 2) : kOutOfRange;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -162,18 +175,18 @@ __device__ __forceinline__ void wait_stages_left(int64_t n) {
 }
 static_assert(kStages <= 4 && 2 * kLoadsPerStage <= 63, "vmcnt holds the loads in flight");
 
-// acc[mi][ni] covers rows wm*128 + mi*32 + {8(q/4) + 4(lane/32) + q%4} and
+// acc[mi][ni] covers rows wm*kRW + mi*32 + {8(q/4) + 4(lane/32) + q%4} and
 // column wn*128 + ni*32 + lane%32 of the tile (q = register index 0..15).
 // KMASK: K is not a multiple of kBK, so the last stage masks its tail.
 template <bool KMASK>
 __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int64_t m0,
-                                             int64_t n0, f32x16 (&acc)[4][4]) {
+                                             int64_t n0, f32x16 (&acc)[kMI][kNI]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < kNI; ++ni)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.f;
 
@@ -199,23 +212,23 @@ __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int
     // the stage's fragments; the compiler interleaves their reads with the
     // products (pinning all reads first, or double-buffering them per k-step,
     // measured slower on MI355X)
-    bf16x8 af[kBK / 16][4], bfr[kBK / 16][4];
+    bf16x8 af[kBK / 16][kMI], bfr[kBK / 16][kNI];
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       const int kc = ks * 2 + (lane >> 5);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[ks][mi] = __builtin_bit_cast(bf16x8, sa[swz(wm * 128 + mi * 32 + (lane & 31), kc)]);
+      for (int mi = 0; mi < kMI; ++mi)
+        af[ks][mi] = __builtin_bit_cast(bf16x8, sa[swz(wm * kRW + mi * 32 + (lane & 31), kc)]);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < kNI; ++ni)
         bfr[ks][ni] = __builtin_bit_cast(bf16x8, sb[swz(wn * 128 + ni * 32 + (lane & 31), kc)]);
     }
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
+        for (int ni = 0; ni < kNI; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][mi], bfr[ks][ni], acc[mi][ni],
                                                                 0, 0, 0);
     // stage kt + 1 must have landed: the stages after it may stay in flight
@@ -225,23 +238,27 @@ __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int
 }
 
 // Rows [64 band, 64 band + 64) of the tile into the fp32 LDS band. Only the
-// two waves that own those rows write (wm = band / 2, mi = 2 (band % 2) + 0/1).
-__device__ __forceinline__ void band_to_lds(float (*cs)[kCRow], const f32x16 (&acc)[4][4],
+// waves that own those rows write (blocks mi0, mi0 + 1 of wave row wm).
+__device__ __forceinline__ void band_to_lds(float (*cs)[kCRow], const f32x16 (&acc)[kMI][kNI],
                                             int band) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  if (wm != band / 2) return;
+  if (wm != band * kBand / kRW) return;
+  const int mi0 = (band * kBand - wm * kRW) / 32;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int mi = 2 * (band % 2) + h;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int mi = 0; mi < kMI; ++mi) {
+      if (mi != mi0 + h) continue;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = h * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int col = wn * 128 + ni * 32 + (lane & 31);
-        cs[row][col] = acc[mi][ni][q];
-      }
+      for (int ni = 0; ni < kNI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = h * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+          const int col = wn * 128 + ni * 32 + (lane & 31);
+          cs[row][col] = acc[mi][ni][q];
+        }
+    }
   }
 }
 
@@ -257,9 +274,9 @@ __device__ __forceinline__ void merge(float& mL, float& s, float m2, float s2) {
 // Statistics: grid = tiles_m * n_ranges, range = block % n_ranges (so the
 // workgroups of one XCD walk one range and share its weight tiles); each
 // walks the vocabulary tiles of its range. Per tile and band, thread
-// (row = tid / 4, quarter = tid % 4) reduces 64 columns of one row.
+// (row = tid / kTPR, part = tid % kTPR) reduces kCPT columns of one row.
 template <bool KMASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_stats_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void lm_stats_kernel(
     GemmParams p) {
   __shared__ __align__(16) Stages s;
   float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
@@ -268,7 +285,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t per = (p.tiles_n + p.n_ranges - 1) / p.n_ranges;
   const int64_t nt0 = range * per, nt1 = std::min<int64_t>(p.tiles_n, nt0 + per);
   const int64_t m0 = static_cast<int64_t>(mt) * kBM;
-  const int row = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  const int row = threadIdx.x / kTPR, part = threadIdx.x % kTPR;
   int64_t t[4];
   float mL[4], sum[4], zt[4];
 #pragma unroll
@@ -279,28 +296,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     sum[b] = 0.f;
     zt[b] = kNegInf;
   }
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
   for (int64_t nt = nt0; nt < nt1; ++nt) {
     const int64_t n0 = nt * kBN;
     tile_product<KMASK>(p, s, m0, n0, acc);
-    const int64_t c0 = n0 + quarter * 64;
-    const int64_t nv = std::min<int64_t>(64, p.N - c0);   // columns inside the vocabulary
+    const int64_t c0 = n0 + part * kCPT;
+    const int64_t nv = std::min<int64_t>(kCPT, p.N - c0);   // columns inside the vocabulary
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       band_to_lds(cs, acc, b);
       __syncthreads();
-      // two reads of the row's 64 columns: masked max, then the sum
+      // two reads of the row's columns: masked max, then the sum
       const int64_t tl = t[b] - c0;
-      const float* crow = &cs[row][quarter * 64];
-      if (tl >= 0 && tl < 64) zt[b] = crow[tl];
+      const float* crow = &cs[row][part * kCPT];
+      if (tl >= 0 && tl < kCPT) zt[b] = crow[tl];
       float gmax = kNegInf;
 #pragma unroll 16
-      for (int j = 0; j < 64; ++j) gmax = fmaxf(gmax, (j < nv && j != tl) ? crow[j] : kNegInf);
+      for (int j = 0; j < kCPT; ++j) gmax = fmaxf(gmax, (j < nv && j != tl) ? crow[j] : kNegInf);
       const float mn = fmaxf(mL[b], gmax * kL2E);
       if (mn != kNegInf) {
         float acc_s = 0.f;
 #pragma unroll 16
-        for (int j = 0; j < 64; ++j) {
+        for (int j = 0; j < kCPT; ++j) {
           const float v = (j < nv && j != tl) ? crow[j] : kNegInf;
           acc_s += fexp2(__builtin_fmaf(v, kL2E, -mn));
         }
@@ -310,11 +327,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       __syncthreads();   // the band is rewritten next (or the stages reloaded)
     }
   }
-  // the four quarters of a row sit in adjacent lanes
+  // the kTPR parts of a row sit in adjacent lanes
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
 #pragma unroll
-    for (int off = 1; off <= 2; off <<= 1) {
+    for (int off = 1; off < kTPR; off <<= 1) {
       const float m2 = __shfl_xor(mL[b], off, 64);
       const float s2 = __shfl_xor(sum[b], off, 64);
       const float z2 = __shfl_xor(zt[b], off, 64);
@@ -322,7 +339,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       zt[b] = fmaxf(zt[b], z2);
     }
     const int64_t gr = m0 + b * kBand + row;
-    if (quarter == 0 && gr < p.M) {
+    if (part == 0 && gr < p.M) {
       float* st = p.stats + 3 * (static_cast<int64_t>(range) * p.M + gr);
       st[0] = mL[b];
       st[1] = sum[b];
@@ -348,7 +365,7 @@ __device__ __forceinline__ void tile_of_block(const GemmParams& p, int64_t& m0, 
 // Gradient tiles of one column chunk: G = dL/dz for all rows and the chunk's
 // vocabulary columns, written row-major and transposed.
 template <bool KMASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_grad_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void lm_grad_kernel(
     GemmParams p) {
   __shared__ __align__(16) Stages s;
   float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
@@ -356,9 +373,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   bool live_tile;
   tile_of_block(p, m0, n0, live_tile);
   if (!live_tile) return;
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
   tile_product<KMASK>(p, s, m0, n0, acc);
-  const int row = threadIdx.x >> 2, quarter = threadIdx.x & 3;
+  const int row = threadIdx.x / kTPR, part = threadIdx.x % kTPR;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     band_to_lds(cs, acc, b);
@@ -383,11 +400,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           fill = (kind == 1.f) ? 0.f : __builtin_nanf("");
         }
       }
-      const int64_t c0 = n0 + quarter * 64;
-      float* crow = &cs[row][quarter * 64];
+      const int64_t c0 = n0 + part * kCPT;
+      float* crow = &cs[row][part * kCPT];
       uint16_t* dst = gr < p.M ? p.g + gr * p.ld_g + c0 : nullptr;
 #pragma unroll
-      for (int j0 = 0; j0 < 64; j0 += 8) {
+      for (int j0 = 0; j0 < kCPT; j0 += 8) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -417,12 +434,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
     }
     __syncthreads();
-    // columns: transposed bf16 stores (rows of G^T); one column per thread
+    // columns: transposed bf16 stores (rows of G^T); kThreads / 256 threads
+    // per column, each a run of band rows
     {
-      const int col = threadIdx.x;
-      uint16_t* dst = p.gt + (n0 + col) * p.ld_gt + m0 + b * kBand;
+      constexpr int kRPT = kBand * 256 / kThreads;   // band rows per thread
+      const int col = threadIdx.x % 256, r0 = (threadIdx.x / 256) * kRPT;
+      uint16_t* dst = p.gt + (n0 + col) * p.ld_gt + m0 + b * kBand + r0;
 #pragma unroll
-      for (int j = 0; j < kBand; j += 8) {
+      for (int j = r0; j < r0 + kRPT; j += 8) {
         uint32_t w[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -431,7 +450,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
           w[e] = lo | (hi << 16);
         }
         const u32x4 v = {w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<u32x4*>(dst + j) = v;
+        *reinterpret_cast<u32x4*>(dst + (j - r0)) = v;
       }
     }
     __syncthreads();
@@ -440,23 +459,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // Plain product C = A B^T (fp32, optionally accumulated into C).
 template <bool KMASK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void lm_store_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void lm_store_kernel(
     GemmParams p) {
   __shared__ __align__(16) Stages s;
   int64_t m0, n0;
   bool live_tile;
   tile_of_block(p, m0, n0, live_tile);
   if (!live_tile) return;
-  f32x16 acc[4][4];
+  f32x16 acc[kMI][kNI];
   tile_product<KMASK>(p, s, m0, n0, acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
+    for (int ni = 0; ni < kNI; ++ni) {
       const int64_t col = n0 + wn * 128 + ni * 32 + (lane & 31);
-      const int64_t row0 = m0 + wm * 128 + mi * 32 + 4 * (lane >> 5);
+      const int64_t row0 = m0 + wm * kRW + mi * 32 + 4 * (lane >> 5);
       // the 16 old values of a block are loaded before any is stored, so
       // the loads are in flight together
       float old[16];
@@ -599,6 +618,12 @@ ce_status launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ld_
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 
+__global__ __launch_bounds__(256) void lm_zero_kernel(float* __restrict__ out, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    out[i] = 0.f;
+}
+
 // fp32 [n] -> bf16 [n], round to nearest even.
 __global__ __launch_bounds__(256) void lm_to_bf16_kernel(const float* __restrict__ in, int64_t n,
                                                          uint16_t* __restrict__ out) {
@@ -659,8 +684,12 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
   (void)hipGetLastError();
 
   if (T == 0) {
+    // no rows: dW is zero (a kernel, not a memset, so the call can be captured)
     if (dweight) {
-      if (hipMemsetAsync(dweight, 0, dw_bytes, st) != hipSuccess) return CE_ERR_HIP;
+      const int64_t n = V * H;
+      const unsigned nb = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 8192));
+      hipLaunchKernelGGL(lm_zero_kernel, dim3(nb), dim3(256), 0, st, dweight, n);
+      if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
     }
     return CE_OK;
   }
