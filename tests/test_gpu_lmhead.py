@@ -157,6 +157,24 @@ def test_forward_only_matches():
     check_loss(_np(loss), ref["loss"], "forward-only loss")
 
 
+def test_partial_backward_and_null_lse():
+    """dX alone, dW alone and no lse output give exactly the values of the
+    full call (the same kernels run; the skipped products are not needed)."""
+    import loss_vocab_amd as L
+    X, W, t = grid_inputs(200, 700, 64, seed=29, ignore=(2,))
+    T, H, V = 200, 64, 700
+    full = L.ce_lmhead(X, W, t, z_alpha=1e-3, grad_scale=0.1, chunk_cols=256)
+    loss = torch.empty(T, device=DEV)
+    dh = torch.empty((T, H), device=DEV)
+    dw = torch.empty((V, H), device=DEV)
+    L.ce_lmhead_fwd_bwd(X, W, t, None, 1e-3, 0.1, loss, None, dh, None, chunk_cols=256)
+    torch.cuda.synchronize()
+    assert torch.equal(loss, full[0]) and torch.equal(dh, full[2])
+    L.ce_lmhead_fwd_bwd(X, W, t, None, 1e-3, 0.1, loss, None, None, dw, chunk_cols=256)
+    torch.cuda.synchronize()
+    assert torch.equal(dw, full[3])
+
+
 def test_out_of_range_target_poisons():
     X, W, t = grid_inputs(130, 300, 64, seed=11, oor=(7,))
     loss, lse, dh, dw, ref = run_and_compare(X, W, t, what="oor")
