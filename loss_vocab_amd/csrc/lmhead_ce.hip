@@ -4,7 +4,7 @@
 // The logits z = X W^T (hidden X [T, H], head weight W [V, H], both bf16) are
 // produced tile by tile on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
 // accumulation) and consumed in the tile's epilogue:
-//  * forward: each workgroup walks a range of vocabulary tiles for 128 rows and
+//  * forward: each workgroup walks a range of vocabulary tiles for 256 rows and
 //    keeps per-row online (shift, sum) statistics of the non-target columns and
 //    the target logit; ce_rows_finish merges the ranges in fp64 into the loss
 //    and the saved per-row state (the collapse-free loss of torchtitan PR #5661,
@@ -132,11 +132,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const Operand& o, int64
 }
 
 // One K stage of one operand, HBM -> LDS without registers: wave w fills row
-// groups i * 4 + w (8 rows each); lane l of a group loads row 8 g + l / 8,
-// chunk (l % 8) ^ (row % 8), which lands at LDS chunk 64 g + l.
-// Wave w fills row groups i * kWaves + w (64 / kCPR rows each); lane l of a group
-// loads row g * 64 / kCPR + l / kCPR and the chunk that swz places at LDS
-// chunk 64 g + l.
+// groups i * kWaves + w (64 / kCPR rows each); lane l of a group loads row
+// g * 64 / kCPR + l / kCPR and the chunk that swz places at LDS chunk 64 g + l.
 template <bool KMASK>
 __device__ __forceinline__ void load_operand(__amdgpu_buffer_rsrc_t rsrc, const Operand& o,
                                              int64_t K, int64_t k0, u32x4* stage) {
