@@ -22,4 +22,5 @@ from .ce_oracle import (  # noqa: F401
     sigmoid,
     softplus,
 )
+from .distill_oracle import distill_oracle  # noqa: F401
 from .lmhead_oracle import lmhead_ce  # noqa: F401

@@ -401,6 +401,72 @@ def pin_lmhead(lm_fn):
     _close(out["dweight"], Gz.T @ X.numpy(), 1e-12, 1e-15, "zero-head dW")
 
 
+def pin_distill(fn):
+    """Distillation child: teacher = student gives KL 0 and the CE values
+    exactly; kl_beta = 0 gives the CE values exactly; torch fp64 autograd of
+    CE + z-loss + beta KL (F.kl_div with log targets); 120-digit brute force
+    of KL including confident rows and -inf entries; the uniform-teacher
+    closed form KL = -log V - mean_j log pS_j; ignored rows 0, out-of-range
+    targets NaN."""
+    from oracle import ce_oracle
+    rng = np.random.default_rng(41)
+    T, V = 9, 23
+    zs = rng.normal(0, 2.5, size=(T, V))
+    zt = rng.normal(0, 2.0, size=(T, V))
+    t = rng.integers(0, V, size=T)
+    t[4] = IGNORE
+    ce = ce_oracle(zs, t, z_alpha=1e-3, grad_scale=0.2)
+    same = fn(zs, zs, t, z_alpha=1e-3, kl_beta=0.7, grad_scale=0.2)
+    assert np.all(same["kl"] == 0.0)
+    assert np.array_equal(same["grad"], ce["grad"]) and np.array_equal(same["loss"], ce["loss"])
+    nob = fn(zs, zt, t, z_alpha=1e-3, kl_beta=0.0, grad_scale=0.2)
+    assert np.array_equal(nob["grad"], ce["grad"]) and np.array_equal(nob["loss"], ce["loss"])
+    # torch fp64 autograd
+    alpha, beta, gamma = 2e-3, 0.6, 0.25
+    tt = torch.as_tensor(t)
+    valid = (tt != IGNORE).double()
+    zr = torch.tensor(zs, dtype=torch.float64, requires_grad=True)
+    ztt = torch.tensor(zt, dtype=torch.float64)
+    cel = torch.nn.functional.cross_entropy(zr, tt, reduction="none", ignore_index=IGNORE)
+    klr = torch.nn.functional.kl_div(torch.log_softmax(zr, 1), torch.log_softmax(ztt, 1),
+                                     reduction="none", log_target=True).sum(1)
+    per_row = cel + (alpha * torch.logsumexp(zr, 1) ** 2 + beta * klr) * valid
+    (gamma * per_row.sum()).backward()
+    out = fn(zs, zt, t, z_alpha=alpha, kl_beta=beta, grad_scale=gamma)
+    _close(out["loss"], per_row.detach().numpy(), 1e-12, 1e-15, "distill loss")
+    _close(out["kl"] * valid.numpy(), (klr * valid).detach().numpy(), 1e-12, 1e-15, "distill kl")
+    _close(out["grad"], zr.grad.numpy(), 1e-10, 1e-18, "distill grad")
+    # 120-digit brute force
+    mpmath.mp.dps = 120
+    zs2 = rng.normal(0, 3, size=(4, 5))
+    zt2 = rng.normal(0, 3, size=(4, 5))
+    t2 = np.array([0, 3, 4, 2])
+    zs2[1, 3] = 60.0                 # confident student
+    zt2[1, 3] = 55.0                 # confident teacher
+    zt2[2, 0] = -np.inf              # a column the teacher rules out
+    out = fn(zs2, zt2, t2, kl_beta=1.0)
+    for r in range(4):
+        a = [mpmath.mpf(float(v)) for v in zs2[r]]
+        b = [mpmath.mpf(float(v)) if np.isfinite(v) else None for v in zt2[r]]
+        la = mpmath.log(mpmath.fsum([mpmath.exp(v) for v in a]))
+        lb = mpmath.log(mpmath.fsum([mpmath.exp(v) for v in b if v is not None]))
+        ref = mpmath.fsum([mpmath.exp(bj - lb) * ((bj - lb) - (aj - la))
+                           for aj, bj in zip(a, b) if bj is not None])
+        _close(out["kl"][r], float(ref), 1e-9, 1e-300, f"distill kl row {r}")
+    # uniform teacher
+    out = fn(zs, np.zeros((T, V)), t, kl_beta=1.0)
+    lps = zs - (zs.max(1, keepdims=True) + np.log(np.exp(zs - zs.max(1, keepdims=True)).sum(1,
+                                                                                 keepdims=True)))
+    ref = -np.log(V) - lps.mean(axis=1)
+    v = t != IGNORE
+    _close(out["kl"][v], ref[v], 1e-12, 1e-15, "uniform-teacher kl")
+    # ignored / out of range
+    out = fn(zs[:3], zt[:3], np.array([IGNORE, V + 1, 0]), kl_beta=0.5)
+    assert out["kl"][0] == 0.0 and out["loss"][0] == 0.0
+    assert np.isnan(out["kl"][1]) and np.isnan(out["loss"][1])
+    assert np.all(np.isnan(out["grad"][1])) and np.all(out["grad"][0] == 0.0)
+
+
 ALL_PINS = [
     pin_margin20,
     pin_collapse_is_avoided,

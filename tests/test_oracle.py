@@ -161,3 +161,37 @@ def test_lmhead_mutant_is_caught(name, old, new):
     exec(compile(src, path, "exec"), mod.__dict__)
     with pytest.raises(Exception):
         pin_lmhead(mod.lmhead_ce)
+
+
+def test_pin_distill():
+    from oracle_pins import pin_distill
+    pin_distill(oracle.distill_oracle)
+
+
+DISTILL_MUTANTS = [
+    ("KL gradient sign flipped", "d = ps - pt", "d = pt - ps"),
+    ("teacher and student swapped in KL", "terms = np.where(pt > 0, pt * (lpt - lps), 0.0)",
+     "terms = np.where(ps > 0, ps * (lps - lpt), 0.0)"),
+    ("target term of KL dropped", "kl[rows] = terms.sum(axis=1) + tgt", "kl[rows] = terms.sum(axis=1)"),
+    ("KL not weighted in the loss", "loss = r[\"loss\"] + kl_beta * np.where(valid, kl, 0.0)",
+     "loss = r[\"loss\"] + np.where(valid, kl, 0.0)"),
+    ("KL gradient misses the row scale", "grad[rows] += (r[\"scale\"][rows] * kl_beta)[:, None] * d",
+     "grad[rows] += kl_beta * d"),
+    ("target column keeps the raw difference only for the student",
+     "d[ar, ti] = pt_nt - ps_nt", "d[ar, ti] = -ps_nt"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", DISTILL_MUTANTS, ids=[m[0] for m in DISTILL_MUTANTS])
+def test_distill_mutant_is_caught(name, old, new):
+    import types
+    from oracle_pins import pin_distill
+    path = os.path.join(os.path.dirname(oracle.__file__), "distill_oracle.py")
+    with open(path) as f:
+        src = f.read()
+    assert old in src, old
+    src = src.replace(old, new).replace("from .ce_oracle import", "from oracle.ce_oracle import")
+    mod = types.ModuleType("distill_mutant")
+    exec(compile(src, path, "exec"), mod.__dict__)
+    with pytest.raises(Exception):
+        pin_distill(mod.distill_oracle)
