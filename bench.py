@@ -28,6 +28,7 @@ DEFAULT_WORKLOAD = "cez_bf16_T8192_V32000_collapse"
 HBM_PEAK_GBPS = 8000.0
 METRIC = "fused CE fwd+bwd logit elems/sec + achieved HBM GB/s (% of peak)"
 METRIC_FORWARD = "CE forward + logsumexp + entropy logit elems/sec + achieved HBM GB/s (% of peak)"
+METRIC_DISTILL = "fused CE + distillation (KL to a teacher matrix) fwd+bwd logit elems/sec + achieved HBM GB/s (% of peak)"
 METRIC_FORWARD_LSE = "CE forward + logsumexp logit elems/sec + achieved HBM GB/s (% of peak)"
 
 
@@ -49,17 +50,18 @@ def traffic_from_profiles(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0):
+def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0, kl_beta=None):
     """Time the fp64 oracle on ``rows`` rows of the workload recipe (generated
     on the host), split in 256-row blocks over a thread pool, repeating the
     sample until ``min_seconds`` have passed. ``forward``: loss, logsumexp and
     entropy without the gradient. A segmented recipe keeps its minimum segment
-    length, with fewer segments when the sample is short."""
+    length, with fewer segments when the sample is short. ``kl_beta``: the
+    distillation oracle against a second draw of the recipe as teacher."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
 
-    from oracle import ce_oracle, row_entropy
+    from oracle import ce_oracle, distill_oracle, row_entropy
     from workloads import make_inputs
 
     sample = wl.scaled(T=rows) if rows != wl.T else wl
@@ -69,11 +71,16 @@ def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0):
     z = inp["logits"]
     t = inp["targets"].numpy()
     seg = inp["segment_ids"].numpy() if inp["segment_ids"] is not None else None
+    teacher = None if kl_beta is None else make_inputs(sample, device="cpu", seed_offset=100)["logits"]
     blocks = [(r0, min(rows, r0 + 256)) for r0 in range(0, rows, 256)]
 
     def work(b):
         r0, r1 = b
         zb = z[r0:r1].double().numpy()
+        if teacher is not None:
+            return distill_oracle(zb, teacher[r0:r1].double().numpy(), t[r0:r1],
+                                  z_alpha=inp["z_alpha"], kl_beta=kl_beta,
+                                  grad_scale=inp["grad_scale"])["loss"].sum()
         out = ce_oracle(zb, t[r0:r1], z_alpha=inp["z_alpha"], grad_scale=inp["grad_scale"],
                         segment_ids=None if seg is None else seg[r0:r1],
                         num_segments=inp["num_segments"], segment_mean=False,
@@ -94,6 +101,8 @@ def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0):
                 break
     what = "loss+logsumexp+entropy" if forward else "loss+gradient"
     segs = f", {sample.num_segments} segments" if sample.num_segments else ""
+    if teacher is not None:
+        what, segs = "CE+KL loss and gradient against a second draw as teacher", ""
     return {"value": passes * rows * wl.V / dt, "unit": "logit elems/s", "cores": threads,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"{rows} rows x V={wl.V} of the same recipe{segs} generated on the host, "
@@ -239,12 +248,16 @@ def main():
                     help="forward path: logsumexp only, no entropy output")
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of the plain device copy timed after the run (0: skip)")
-    ap.add_argument("--path", choices=["fused", "split", "forward", "lmhead"], default="fused",
+    ap.add_argument("--path", choices=["fused", "split", "forward", "lmhead", "distill"],
+                    default="fused",
                     help="fused: one ce_fused_fwd_bwd call per step; split: per-shard statistics, "
                          "finish, per-shard gradient (the vocabulary-parallel form on one GPU); "
                          "forward: one ce_fused_forward call with logsumexp and entropy outputs "
                          "(another metric: no gradient); lmhead: ce_lmhead_fwd_bwd from hidden "
-                         "states and the head weight (another metric: matrix-core bound)")
+                         "states and the head weight (another metric: matrix-core bound); "
+                         "distill: ce_fused_distill with a second draw of the recipe as teacher "
+                         "(another metric: two matrices read)")
+    ap.add_argument("--kl-beta", type=float, default=0.5)
     ap.add_argument("--shards", type=int, default=2)
     args = ap.parse_args()
 
@@ -267,7 +280,8 @@ def main():
         threads = max(1, min(16, len(os.sched_getaffinity(0))))
         rows = args.cpu_rows or min(wl.T, max(256, int(3e8 // wl.V) // 256 * 256))
         cpu = cpu_baseline(wl, rows, threads, forward=args.path == "forward",
-                           min_seconds=args.cpu_seconds)
+                           min_seconds=args.cpu_seconds,
+                           kl_beta=args.kl_beta if args.path == "distill" else None)
 
     import torch
 
@@ -304,6 +318,12 @@ def main():
             split_bufs.append((torch.empty((len(bounds), wl.T, 3), dtype=torch.float32, device=dev),
                                torch.empty((wl.T, 8), dtype=torch.float32, device=dev)))
     phase_ev = []   # split path: (stats, finish, grad) event triples per step
+    teachers = []
+    if args.path == "distill":
+        for i in range(len(sets)):
+            teachers.append((make_inputs(wl, device=dev, seed_offset=100 + i)["logits"],
+                             torch.empty(wl.T, dtype=torch.float32, device=dev)))
+        torch.cuda.synchronize()
     fwd_bufs = []
     if args.path == "forward":
         for _ in sets:
@@ -317,6 +337,12 @@ def main():
                                inp["z_alpha"], inp["grad_scale"], loss, seg, grad,
                                num_segments=wl.num_segments, segment_mean=inp["segment_mean"],
                                workspace=ws, stream=stream.cuda_stream)
+            return
+        if args.path == "distill":
+            teacher, kl = teachers[i % len(sets)]
+            L.ce_fused_distill(inp["logits"], teacher, inp["targets"], None, inp["z_alpha"],
+                               args.kl_beta, inp["grad_scale"], loss, kl, grad,
+                               stream=stream.cuda_stream)
             return
         if args.path == "forward":
             lse, ent = fwd_bufs[i % len(sets)]
@@ -412,6 +438,15 @@ def main():
         avg_call_ms = ms[2]
         traffic = None
     metric = METRIC
+    if args.path == "distill":
+        # Valid rows of both matrices read once; every gradient row written;
+        # targets read, loss and KL written.
+        b_in = 4 if wl.dtype == "f32" else 2
+        b_out = 4 if wl.grad_torch_dtype == torch.float32 else 2
+        nbytes = wl.n_valid * wl.V * 2 * b_in + wl.T * wl.V * b_out + wl.T * (8 + 2 * 4)
+        achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
+        traffic = None
+        metric = METRIC_DISTILL
     if args.path == "forward":
         # Valid rows read once; targets read, loss / lse / entropy written
         # (the segment terms of the fused call stay the same).
@@ -439,10 +474,13 @@ def main():
             "workload": wl.name, "T": wl.T, "V": wl.V, "logits_dtype": wl.dtype,
             "grad_dtype": "bf16" if wl.grad_torch_dtype == torch.bfloat16 else "f32",
             "in_place": wl.grad == "inplace", "z_alpha": wl.z_alpha,
-            "ignored_rows": wl.n_masked, "segments": wl.num_segments,
+            "ignored_rows": wl.n_masked,
+            "segments": 0 if args.path == "distill" else wl.num_segments,
             "rotating_buffer_sets": args.rotate, "alg_bytes_per_step": nbytes,
             "path": args.path,
             **({"entropy": not args.no_entropy} if args.path == "forward" else {}),
+            **({"kl_beta": args.kl_beta, "teacher": "second draw of the recipe, seed offset 100"}
+               if args.path == "distill" else {}),
         },
         "alg_GBps": nbytes / (ms_per_step * 1e-3) / 1e9,
         "pct_of_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,

@@ -163,6 +163,52 @@ ce_status ce_fused_forward(const ce_problem* p,
                            void* stream);
 
 /*
+ * Cross-entropy + z-loss with a distillation child on the same softmax pass.
+ *
+ * Fast-LLM PR #552 "Fuse GSPO into the monolithic compiled loss" (PR body,
+ * What) names distillation with CE and z-loss among the losses that share
+ * the vocabulary softmax and finish loss and gradient in one pass. The
+ * pages give no formula; this library's reading is the forward KL divergence
+ * from the teacher's softmax to the student's, per valid row:
+ *   loss_r = NLL_r + z_alpha lse_r^2 + kl_beta KL(softmax(y_r) || softmax(z_r))
+ *   grad_r = s (1 + 2 z_alpha lse_r + kl_beta) softmax(z_r) - s kl_beta softmax(y_r)
+ * with the target column formed from the non-target logsumexps (revised PR
+ * description of torchtitan #5661, Numerics):
+ *   grad_rt = s (-pS_nt + 2 z_alpha lse_r pS_t + kl_beta (pT_nt - pS_nt)).
+ *
+ *  p             as for ce_fused_fwd_bwd: the student logits' shape, strides
+ *                and dtypes, ignore_index; num_segments must be 0
+ *                (CE_ERR_UNSUPPORTED otherwise) and flags 0.
+ *  logits        [T, ld_logits] student logits (differentiated).
+ *  teacher       [T, ld_teacher] of teacher_dtype (CE_DTYPE_F32 or
+ *                CE_DTYPE_BF16), read only; never written.
+ *  targets, mask, z_alpha, grad_scale: as for ce_fused_fwd_bwd.
+ *  kl_beta       weight of the KL term (0: the gradient does not read the
+ *                teacher; the forward still does, for kl_out).
+ *  loss_out      [T] float, required; kl_out [T] float or NULL: KL_r.
+ *                Ignored rows +0.0; a valid row whose target is outside
+ *                [0, V) gets NaN in both and a NaN gradient row.
+ *  grad_out      [T, ld_grad] or NULL (forward only); may equal logits (in
+ *                place, same dtype and stride); may not overlap teacher.
+ * One pass over both matrices computes the statistics; the gradient pass
+ * reads them again. Asynchronous, deterministic, allocates nothing.
+ */
+ce_status ce_fused_distill(const ce_problem* p,
+                           const void* logits,
+                           const void* teacher,
+                           int64_t ld_teacher,
+                           int32_t teacher_dtype,
+                           const int64_t* targets,
+                           const uint8_t* mask,
+                           float z_alpha,
+                           float kl_beta,
+                           float grad_scale,
+                           float* loss_out,
+                           float* kl_out,
+                           void* grad_out,
+                           void* stream);
+
+/*
  * Split form: statistics over column shards, a per-row finish, and a
  * gradient pass from saved per-row state.
  *

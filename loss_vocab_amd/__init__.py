@@ -340,3 +340,45 @@ def ce_lmhead(hidden, weight, targets, *, mask=None, z_alpha=0.0, grad_scale=1.0
     ce_lmhead_fwd_bwd(hidden, weight, targets, mask, z_alpha, grad_scale, loss, lse, dh, dw,
                       chunk_cols=chunk_cols, ignore_index=ignore_index)
     return loss, lse, dh, dw
+
+
+# ---------------------------------------------------------------------------
+# Distillation child on the same softmax pass.
+# ---------------------------------------------------------------------------
+
+def ce_fused_distill(logits, teacher, targets, mask, z_alpha, kl_beta, grad_scale, loss_out,
+                     kl_out, grad_out, *, ignore_index=IGNORE_INDEX, stream=None):
+    """Same-named wrapper of the C entry point: logits / teacher [T, V]
+    f32/bf16 (unit column stride), loss_out [T] f32, kl_out [T] f32 or None,
+    grad_out [T, V] f32/bf16, ``logits`` (in place) or None."""
+    if teacher.dtype not in _DTYPES or tuple(teacher.shape) != tuple(logits.shape):
+        raise ValueError("teacher must be float32/bfloat16 with the logits' shape")
+    p = make_problem(logits, grad_out, ignore_index=ignore_index)
+    for name, t, dt in (("targets", targets, torch.int64), ("mask", mask, torch.uint8),
+                        ("loss_out", loss_out, torch.float32), ("kl_out", kl_out, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous {dt} tensor")
+    st = _lib.distill_raw(p, _ptr(logits), _ptr(teacher), _rows(teacher, "teacher"),
+                          _DTYPES[teacher.dtype], _ptr(targets), _ptr(mask), z_alpha, kl_beta,
+                          grad_scale, _ptr(loss_out), _ptr(kl_out), _ptr(grad_out),
+                          _stream(logits, stream))
+    if st != CE_OK:
+        raise CeError(st, "ce_fused_distill")
+
+
+def ce_distill(logits, teacher, targets, *, mask=None, z_alpha=0.0, kl_beta=1.0, grad_scale=1.0,
+               grad_dtype=None, in_place=False, want_grad=True, ignore_index=IGNORE_INDEX):
+    """Allocate and run. Returns ``(loss[T], kl[T], grad[T, V] or None)``."""
+    T, V = logits.shape
+    dev = logits.device
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    kl = torch.empty(T, dtype=torch.float32, device=dev)
+    if not want_grad:
+        grad = None
+    elif in_place:
+        grad = logits
+    else:
+        grad = torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
+    ce_fused_distill(logits, teacher, targets, mask, z_alpha, kl_beta, grad_scale, loss, kl, grad,
+                     ignore_index=ignore_index)
+    return loss, kl, grad

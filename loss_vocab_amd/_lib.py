@@ -29,7 +29,7 @@ ROW_STATE = 8   # floats of saved state per row (ce_rows_finish)
 # Every symbol include/ce_fused.h declares.
 EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_fused_forward", "ce_shard_stats",
            "ce_rows_finish", "ce_shard_grad", "ce_lmhead_workspace_bytes", "ce_lmhead_fwd_bwd",
-           "ce_status_string")
+           "ce_fused_distill", "ce_status_string")
 
 
 class CeProblem(ctypes.Structure):
@@ -113,6 +113,11 @@ def _load():
         vp, ctypes.c_size_t, vp,
     ]
     lib.ce_lmhead_fwd_bwd.restype = ctypes.c_int
+    lib.ce_fused_distill.argtypes = [
+        ctypes.POINTER(CeProblem), vp, vp, ctypes.c_int64, ctypes.c_int32, vp, vp, ctypes.c_float,
+        ctypes.c_float, ctypes.c_float, vp, vp, vp, vp,
+    ]
+    lib.ce_fused_distill.restype = ctypes.c_int
     lib.ce_status_string.argtypes = [ctypes.c_int]
     lib.ce_status_string.restype = ctypes.c_char_p
     return lib
@@ -178,3 +183,11 @@ def lmhead_raw(problem, hidden, weight, targets, mask, z_alpha, grad_scale, loss
         ctypes.byref(problem), hidden or None, weight or None, targets or None, mask or None,
         float(z_alpha), float(grad_scale), loss_out or None, lse_out or None, dhidden or None,
         dweight or None, workspace or None, int(workspace_bytes_), stream or None))
+
+
+def distill_raw(problem, logits, teacher, ld_teacher, teacher_dtype, targets, mask, z_alpha,
+                kl_beta, grad_scale, loss_out, kl_out, grad_out, stream):
+    return int(LIB.ce_fused_distill(
+        ctypes.byref(problem), logits or None, teacher or None, int(ld_teacher), int(teacher_dtype),
+        targets or None, mask or None, float(z_alpha), float(kl_beta), float(grad_scale),
+        loss_out or None, kl_out or None, grad_out or None, stream or None))

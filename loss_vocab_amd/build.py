@@ -15,7 +15,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "ce_fused.hip"), os.path.join(PKG, "csrc", "lmhead_ce.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("ce_fused.hip", "lmhead_ce.hip", "distill_ce.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libce_fused.so")
 ARCH = "gfx950"

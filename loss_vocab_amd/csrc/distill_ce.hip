@@ -1,0 +1,450 @@
+// Cross-entropy + z-loss with a distillation child on the same softmax pass,
+// for MI355X (gfx950).
+//
+// Fast-LLM PR #552 ("Fuse GSPO into the monolithic compiled loss", PR body,
+// What) lists distillation with CE and z-loss among the losses that share the
+// vocabulary softmax and finish loss and gradient in one pass. Per row, with
+// student logits z (the ones differentiated) and teacher logits y:
+//   loss = NLL + alpha lse_z^2 + beta KL(softmax(y) || softmax(z))
+//   grad = s (1 + 2 alpha lse_z + beta) softmax(z) - s beta softmax(y),
+// the target column taken from the non-target logsumexps as for the NLL
+// (torchtitan #5661, revised PR description, Numerics):
+//   grad_t = s (-pS_nt + 2 alpha lse_z pS_t + beta (pT_nt - pS_nt)).
+//
+// One workgroup per row, both passes streamed. Pass 1 keeps, per lane, the
+// student's non-target (shift, sum), the teacher's non-target (shift, sum)
+// and U = sum 2^d (y_j - z_j) in the teacher's shifted frame; the epilogue
+// forms, in fp64,
+//   KL = pT_t (NLL_z - NLL_y) + 2^(M_y - lse_y log2 e) U + pT_nt (lse_z - lse_y),
+// every piece from the non-target statistics and the two target logits.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "ce_fused.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;
+constexpr float kL2E = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access by dtype: load one element, or 8 consecutive elements of a
+// 16-byte-aligned row (chunk c = elements 8c .. 8c + 7); NT marks a last use
+// (pass 2), whose loads need not stay in the caches.
+template <typename T> struct Ld;
+template <> struct Ld<float> {
+  static constexpr int BYTES = 4;
+  __device__ static float one(const void* row, int64_t j) { return static_cast<const float*>(row)[j]; }
+  template <bool NT>
+  __device__ static void eight(const void* row, int64_t c, float (&x)[8]) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + c * 32);
+    const u32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
+    const u32x4 b = NT ? __builtin_nontemporal_load(q + 1) : q[1];
+    x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+    x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+    x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+    x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+  }
+  __device__ static void put_one(void* row, int64_t j, float g) { static_cast<float*>(row)[j] = g; }
+  __device__ static void put_eight(void* row, int64_t c, const float (&g)[8]) {
+    u32x4* q = reinterpret_cast<u32x4*>(static_cast<char*>(row) + c * 32);
+    const u32x4 a = {__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]),
+                     __float_as_uint(g[3])};
+    const u32x4 b = {__float_as_uint(g[4]), __float_as_uint(g[5]), __float_as_uint(g[6]),
+                     __float_as_uint(g[7])};
+    __builtin_nontemporal_store(a, q);
+    __builtin_nontemporal_store(b, q + 1);
+  }
+};
+template <> struct Ld<uint16_t> {   // bf16
+  static constexpr int BYTES = 2;
+  __device__ static float one(const void* row, int64_t j) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[j]) << 16);
+  }
+  template <bool NT>
+  __device__ static void eight(const void* row, int64_t c, float (&x)[8]) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const char*>(row) + c * 16);
+    const u32x4 a = NT ? __builtin_nontemporal_load(q) : q[0];
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void put_one(void* row, int64_t j, float g) {
+    static_cast<uint16_t*>(row)[j] = to_bf16(g);
+  }
+  __device__ static void put_eight(void* row, int64_t c, const float (&g)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(to_bf16(g[2 * i])) |
+             (static_cast<uint32_t>(to_bf16(g[2 * i + 1])) << 16);
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<char*>(row) + c * 16));
+  }
+};
+
+struct DistillParams {
+  const void* logits;
+  const void* teacher;
+  void* grad;
+  const int64_t* targets;
+  const uint8_t* mask;
+  float* loss_out;
+  float* kl_out;
+  int64_t T, V, ld_s, ld_t, ld_g, ignore_index;
+  float z_alpha, kl_beta, grad_scale;
+};
+
+// Running (shift, sum) in log2 units plus the teacher's U.
+struct Part {
+  float ms, ss;      // student non-target
+  float mt, st, u;   // teacher non-target, sum 2^d (y - z)
+};
+
+// s_old 2^(m - M) + add: the one update of a (shift, sum) pair, used for the
+// student and the teacher alike (the same arithmetic on equal inputs gives
+// equal statistics, so a teacher equal to the student has KL exactly 0).
+__device__ __forceinline__ float rescale(float m, float s, float M) {
+  return (m == kNegInf || s == 0.f) ? 0.f : fexp2(m - M);
+}
+__device__ __forceinline__ void upd(float& m, float& s, float M, float add) {
+  s = __builtin_fmaf(s, rescale(m, s, M), add);
+  m = M;
+}
+
+// Fold N elements into the part: xs / xt with the target element at -inf,
+// ws / wt the raw values for the teacher's weight y - z.
+template <int N>
+__device__ __forceinline__ void fold(Part& p, const float (&xs)[N], const float (&xt)[N],
+                                     const float (&ws)[N], const float (&wt)[N]) {
+  float gs = kNegInf, gt = kNegInf;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    gs = fmaxf(gs, xs[k]);
+    gt = fmaxf(gt, xt[k]);
+  }
+  const float ns = fmaxf(p.ms, gs * kL2E);
+  if (ns != kNegInf) {
+    float a = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) a += fexp2(__builtin_fmaf(xs[k], kL2E, -ns));
+    upd(p.ms, p.ss, ns, a);
+  }
+  const float nt = fmaxf(p.mt, gt * kL2E);
+  if (nt != kNegInf) {
+    float a = 0.f, au = 0.f;
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const float e = fexp2(__builtin_fmaf(xt[k], kL2E, -nt));
+      a += e;
+      au += (e > 0.f) ? e * (wt[k] - ws[k]) : 0.f;
+    }
+    p.u = __builtin_fmaf(p.u, rescale(p.mt, p.st, nt), au);
+    upd(p.mt, p.st, nt, a);
+  }
+}
+
+__device__ __forceinline__ void merge(Part& a, const Part& b) {
+  const float ns = fmaxf(a.ms, b.ms);
+  if (ns != kNegInf) upd(a.ms, a.ss, ns, b.ss * rescale(b.ms, b.ss, ns));
+  const float nt = fmaxf(a.mt, b.mt);
+  if (nt != kNegInf) {
+    a.u = __builtin_fmaf(a.u, rescale(a.mt, a.st, nt), b.u * rescale(b.mt, b.st, nt));
+    upd(a.mt, a.st, nt, b.st * rescale(b.mt, b.st, nt));
+  }
+}
+
+__device__ __forceinline__ Part shfl_xor(const Part& p, int off) {
+  Part q;
+  q.ms = __shfl_xor(p.ms, off, 64);
+  q.ss = __shfl_xor(p.ss, off, 64);
+  q.mt = __shfl_xor(p.mt, off, 64);
+  q.st = __shfl_xor(p.st, off, 64);
+  q.u = __shfl_xor(p.u, off, 64);
+  return q;
+}
+
+__device__ __forceinline__ double sigmoid_d(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  const double e = exp(x);
+  return e / (1.0 + e);
+}
+
+struct Side {   // one distribution's row quantities, fp64
+  double lse, nll, p_nt, p_t;
+};
+
+// From a non-target (shift, sum) in log2 units and the target logit.
+__device__ __forceinline__ Side side(float M, float S, float zt) {
+  const double lse_nt = (M == kNegInf || S == 0.f)
+                            ? -HUGE_VAL
+                            : static_cast<double>(M) / static_cast<double>(kL2E) + log(static_cast<double>(S));
+  const double z = static_cast<double>(zt);
+  const double x = lse_nt - z;
+  const double l1p = log1p(exp(-fabs(x)));
+  Side o;
+  o.nll = (x > 0.0 ? x : 0.0) + l1p;
+  o.lse = (lse_nt > z ? lse_nt : z) + l1p;
+  o.p_nt = sigmoid_d(x);
+  o.p_t = sigmoid_d(-x);
+  return o;
+}
+
+struct RowOut {
+  float cs, ct, ks, kt, gt;   // student / teacher factors, lse in log2 units, target grad
+};
+
+template <typename TS, typename TT, typename TO, bool VEC>
+__global__ __launch_bounds__(kBlock) void distill_rows_kernel(DistillParams p) {
+  __shared__ Part red[kBlock / 64];
+  __shared__ RowOut out_sh;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t V = p.V;
+  const int64_t nch = VEC ? V / 8 : 0;            // full 8-element chunks
+  const int64_t tail0 = nch * 8;                  // first element of the tail
+  for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x) {
+    const int64_t t = p.targets[r];
+    const bool valid = (t != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+    const bool owned = t >= 0 && t < V;
+    void* grow = p.grad ? static_cast<char*>(p.grad) + r * p.ld_g * Ld<TO>::BYTES : nullptr;
+    if (!valid || !owned) {
+      const float fill = valid ? __builtin_nanf("") : 0.f;
+      if (tid == 0) {
+        p.loss_out[r] = fill;
+        if (p.kl_out) p.kl_out[r] = fill;
+      }
+      if (grow) {
+        const float f8[8] = {fill, fill, fill, fill, fill, fill, fill, fill};
+        for (int64_t c = tid; c < nch; c += kBlock) Ld<TO>::put_eight(grow, c, f8);
+        for (int64_t j = tail0 + tid; j < V; j += kBlock) Ld<TO>::put_one(grow, j, fill);
+      }
+      continue;
+    }
+    const void* srow = static_cast<const char*>(p.logits) + r * p.ld_s * Ld<TS>::BYTES;
+    const void* trow = static_cast<const char*>(p.teacher) + r * p.ld_t * Ld<TT>::BYTES;
+    const float zs_t = Ld<TS>::one(srow, t), zt_t = Ld<TT>::one(trow, t);
+
+    // ---- pass 1 ----
+    Part pa{kNegInf, 0.f, kNegInf, 0.f, 0.f};
+    for (int64_t c = tid; c < nch; c += kBlock) {
+      float ws[8], wt[8], xs[8], xt[8];
+      Ld<TS>::template eight<false>(srow, c, ws);
+      Ld<TT>::template eight<false>(trow, c, wt);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool tgt = c * 8 + k == t;
+        xs[k] = tgt ? kNegInf : ws[k];
+        xt[k] = tgt ? kNegInf : wt[k];
+      }
+      fold<8>(pa, xs, xt, ws, wt);
+    }
+    for (int64_t j = tail0 + tid; j < V; j += kBlock) {
+      float ws[1] = {Ld<TS>::one(srow, j)}, wt[1] = {Ld<TT>::one(trow, j)};
+      float xs[1] = {j == t ? kNegInf : ws[0]}, xt[1] = {j == t ? kNegInf : wt[0]};
+      fold<1>(pa, xs, xt, ws, wt);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) merge(pa, shfl_xor(pa, off));
+    if (lane == 0) red[wid] = pa;
+    __syncthreads();
+    if (tid == 0) {
+      Part tot = red[0];
+#pragma unroll
+      for (int w = 1; w < kBlock / 64; ++w) merge(tot, red[w]);
+      // ---- fp64 epilogue ----
+      const Side S = side(tot.ms, tot.ss, zs_t);
+      const Side Tt = side(tot.mt, tot.st, zt_t);
+      const double alpha = p.z_alpha, beta = p.kl_beta, sc = p.grad_scale;
+      double kl = (Tt.p_t > 0.0) ? Tt.p_t * (S.nll - Tt.nll) : 0.0;
+      if (tot.mt != kNegInf && tot.st > 0.f) {
+        const double l2t = static_cast<double>(kL2E) * Tt.lse;
+        kl += exp2(static_cast<double>(tot.mt) - l2t) * static_cast<double>(tot.u);
+        kl += Tt.p_nt * (S.lse - Tt.lse);
+      }
+      const double zl = (alpha == 0.0) ? 0.0 : 2.0 * alpha * S.lse;
+      p.loss_out[r] = static_cast<float>(S.nll + ((alpha == 0.0) ? 0.0 : alpha * S.lse * S.lse) +
+                                         beta * kl);
+      if (p.kl_out) p.kl_out[r] = static_cast<float>(kl);
+      RowOut o;
+      o.cs = static_cast<float>(sc * (1.0 + zl + beta));
+      o.ct = static_cast<float>(sc * beta);
+      o.ks = static_cast<float>(static_cast<double>(kL2E) * S.lse);
+      o.kt = static_cast<float>(static_cast<double>(kL2E) * Tt.lse);
+      o.gt = static_cast<float>(sc * (-S.p_nt + zl * S.p_t + beta * (Tt.p_nt - S.p_nt)));
+      out_sh = o;
+    }
+    __syncthreads();
+    const RowOut o = out_sh;
+
+    // ---- pass 2 ----
+    if (grow) {
+      const bool teach = o.ct != 0.f;
+      for (int64_t c = tid; c < nch; c += kBlock) {
+        float ws[8], wt[8], g[8];
+        Ld<TS>::template eight<true>(srow, c, ws);
+        if (teach) Ld<TT>::template eight<true>(trow, c, wt);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          float v = o.cs * fexp2(__builtin_fmaf(ws[k], kL2E, -o.ks));
+          if (teach) v -= o.ct * fexp2(__builtin_fmaf(wt[k], kL2E, -o.kt));
+          g[k] = (c * 8 + k == t) ? o.gt : v;
+        }
+        Ld<TO>::put_eight(grow, c, g);
+      }
+      for (int64_t j = tail0 + tid; j < V; j += kBlock) {
+        float v = o.cs * fexp2(__builtin_fmaf(Ld<TS>::one(srow, j), kL2E, -o.ks));
+        if (teach) v -= o.ct * fexp2(__builtin_fmaf(Ld<TT>::one(trow, j), kL2E, -o.kt));
+        Ld<TO>::put_one(grow, j, j == t ? o.gt : v);
+      }
+    }
+    __syncthreads();   // out_sh and red are rewritten by the next row
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+int device_cus_distill() {
+  static std::atomic<int> cus{0};
+  int c = cus.load();
+  if (c == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      c = 256;
+    cus.store(c);
+  }
+  return c;
+}
+
+template <typename TS, typename TT, typename TO, bool VEC>
+ce_status launch_distill(const DistillParams& dp, hipStream_t st) {
+  const int64_t grid = std::min<int64_t>(dp.T, 16LL * device_cus_distill());
+  if (grid <= 0) return CE_OK;
+  hipLaunchKernelGGL((distill_rows_kernel<TS, TT, TO, VEC>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kBlock), 0, st, dp);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+template <typename TS, typename TT>
+ce_status dispatch_o(const DistillParams& dp, int32_t grad_dtype, bool vec, hipStream_t st) {
+  if (grad_dtype == CE_DTYPE_F32)
+    return vec ? launch_distill<TS, TT, float, true>(dp, st) : launch_distill<TS, TT, float, false>(dp, st);
+  return vec ? launch_distill<TS, TT, uint16_t, true>(dp, st)
+             : launch_distill<TS, TT, uint16_t, false>(dp, st);
+}
+
+template <typename TS>
+ce_status dispatch_t(const DistillParams& dp, int32_t teacher_dtype, int32_t grad_dtype, bool vec,
+                     hipStream_t st) {
+  return teacher_dtype == CE_DTYPE_F32 ? dispatch_o<TS, float>(dp, grad_dtype, vec, st)
+                                       : dispatch_o<TS, uint16_t>(dp, grad_dtype, vec, st);
+}
+
+int dbytes(int32_t dt) { return dt == CE_DTYPE_F32 ? 4 : 2; }
+
+bool span(int64_t T, int64_t V, int64_t ld, int b, size_t* out) {
+  if (T == 0) {
+    *out = 0;
+    return true;
+  }
+  if (ld > (INT64_MAX - V) / T) return false;
+  *out = static_cast<size_t>(((T - 1) * ld + V) * b);
+  return true;
+}
+
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a && b && an && bn && a0 < b0 + bn && b0 < a0 + an;
+}
+
+bool rows16(const void* ptr, int64_t ld, int b) {
+  return ptr == nullptr || ((reinterpret_cast<uintptr_t>(ptr) % 16 == 0) && (ld * b) % 16 == 0);
+}
+
+}  // namespace
+
+extern "C" ce_status ce_fused_distill(const ce_problem* p, const void* logits, const void* teacher,
+                                      int64_t ld_teacher, int32_t teacher_dtype,
+                                      const int64_t* targets, const uint8_t* mask, float z_alpha,
+                                      float kl_beta, float grad_scale, float* loss_out,
+                                      float* kl_out, void* grad_out, void* stream_ptr) {
+  if (p == nullptr) return CE_ERR_INVALID_ARG;
+  const int64_t T = p->T, V = p->V;
+  if (T < 0 || V < 1 || p->ld_logits < V || ld_teacher < V) return CE_ERR_INVALID_ARG;
+  const bool dt_ok = [](int32_t d) { return d == CE_DTYPE_F32 || d == CE_DTYPE_BF16; }(p->logits_dtype);
+  if (!dt_ok || (teacher_dtype != CE_DTYPE_F32 && teacher_dtype != CE_DTYPE_BF16))
+    return CE_ERR_INVALID_ARG;
+  if (grad_out && ((p->grad_dtype != CE_DTYPE_F32 && p->grad_dtype != CE_DTYPE_BF16) ||
+                   p->ld_grad < V))
+    return CE_ERR_INVALID_ARG;
+  if (p->flags != 0) return CE_ERR_INVALID_ARG;
+  if (p->num_segments != 0) return CE_ERR_UNSUPPORTED;   // no segment sums on this child
+  if (!std::isfinite(z_alpha) || !std::isfinite(kl_beta) || !std::isfinite(grad_scale))
+    return CE_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !teacher || !targets || !loss_out)) return CE_ERR_INVALID_ARG;
+  const int bs = dbytes(p->logits_dtype), bt = dbytes(teacher_dtype);
+  const int bo = grad_out ? dbytes(p->grad_dtype) : bs;
+  size_t ns = 0, nt = 0, no = 0;
+  if (!span(T, V, p->ld_logits, bs, &ns) || !span(T, V, ld_teacher, bt, &nt) ||
+      (grad_out && !span(T, V, p->ld_grad, bo, &no)))
+    return CE_ERR_INVALID_ARG;
+  // The gradient may replace the student logits exactly (same dtype and
+  // stride); it may not touch the teacher; the row outputs touch neither.
+  if (grad_out) {
+    const bool same = grad_out == logits && p->grad_dtype == p->logits_dtype &&
+                      p->ld_grad == p->ld_logits;
+    if ((!same && overlap(grad_out, no, logits, ns)) || overlap(grad_out, no, teacher, nt))
+      return CE_ERR_ALIAS;
+  }
+  for (const float* o : {static_cast<const float*>(loss_out), static_cast<const float*>(kl_out)})
+    if (overlap(o, static_cast<size_t>(T) * 4, logits, ns) ||
+        overlap(o, static_cast<size_t>(T) * 4, teacher, nt) ||
+        overlap(o, static_cast<size_t>(T) * 4, grad_out, no))
+      return CE_ERR_ALIAS;
+  if (T == 0) return CE_OK;
+
+  DistillParams dp{};
+  dp.logits = logits;
+  dp.teacher = teacher;
+  dp.grad = grad_out;
+  dp.targets = targets;
+  dp.mask = mask;
+  dp.loss_out = loss_out;
+  dp.kl_out = kl_out;
+  dp.T = T;
+  dp.V = V;
+  dp.ld_s = p->ld_logits;
+  dp.ld_t = ld_teacher;
+  dp.ld_g = grad_out ? p->ld_grad : p->ld_logits;
+  dp.ignore_index = p->ignore_index;
+  dp.z_alpha = z_alpha;
+  dp.kl_beta = kl_beta;
+  dp.grad_scale = grad_scale;
+  const bool vec = rows16(logits, p->ld_logits, bs) && rows16(teacher, ld_teacher, bt) &&
+                   rows16(grad_out, p->ld_grad, bo);
+  hipStream_t st = static_cast<hipStream_t>(stream_ptr);
+  (void)hipGetLastError();
+  return p->logits_dtype == CE_DTYPE_F32
+             ? dispatch_t<float>(dp, teacher_dtype, p->grad_dtype, vec, st)
+             : dispatch_t<uint16_t>(dp, teacher_dtype, p->grad_dtype, vec, st);
+}

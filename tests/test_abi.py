@@ -325,3 +325,37 @@ def test_lmhead_workspace_grows_with_backward_and_chunk():
     p.dhidden_dtype = 1      # a bf16 dX adds an fp32 accumulator
     assert L.lmhead_workspace_bytes(p, True) > bwd
     assert L.LIB.ce_lmhead_workspace_bytes(None, 1) == 0
+
+
+A_TEACH = 0xA0000000
+A_KL = 0xB0000000
+
+
+def _dcall(p, logits=A_LOGITS, teacher=A_TEACH, ldt=None, tdt=0, targets=A_TGT, loss=A_LOSS,
+           kl=0, grad=A_GRAD, za=0.0, kb=1.0, gs=1.0):
+    return _lib().distill_raw(p, logits, teacher, p.V if ldt is None else ldt, tdt, targets, 0, za,
+                              kb, gs, loss, kl, grad, 0)
+
+
+@pytest.mark.parametrize("case,pkw,kw,expect", [
+    ("segments are not supported", dict(S=2), {}, 2),
+    ("flags", dict(flags=1), {}, 1),
+    ("bad teacher dtype", {}, dict(tdt=5), 1),
+    ("teacher stride < V", {}, dict(ldt=50), 1),
+    ("null teacher", {}, dict(teacher=0), 1),
+    ("null loss", {}, dict(loss=0), 1),
+    ("non-finite beta", {}, dict(kb=float("nan")), 1),
+    ("grad over the teacher", {}, dict(grad=A_TEACH + 64), 3),
+    ("grad overlapping logits (shifted)", {}, dict(grad=A_LOGITS + 4), 3),
+    ("kl inside the logits", {}, dict(kl=A_LOGITS + 16), 3),
+    ("loss inside the teacher", {}, dict(loss=A_TEACH), 3),
+])
+def test_distill_validation(case, pkw, kw, expect):
+    st = _dcall(_problem(**pkw), **kw)
+    assert st == expect, (case, _lib().status_string(st))
+
+
+def test_distill_in_place_allowed():
+    """grad_out == logits with the same dtype and stride passes validation
+    (checked with T = 0 so nothing is launched)."""
+    assert _dcall(_problem(T=0), grad=A_LOGITS) == 0

@@ -1,0 +1,213 @@
+"""Distillation child on the shared softmax vs the fp64 oracle.
+
+Tolerances (derived from the arithmetic):
+* the CE part of the loss and of the gradient keeps the fused path's bars
+  (loss relative 1e-5; fp32 gradient absolute 1e-6; bf16 gradient 2 ulp);
+* KL is assembled from fp32 row statistics whose relative error is ~1e-6, in
+  pieces of size up to pT_nt (|lse_z| + |lse_y| + max|y - z|) + |pT_t (NLL_z -
+  NLL_y)|; its error is held to 1e-5 |KL| + 4e-6 times that size;
+* each gradient element s ((1 + 2 alpha lse + beta) pS - beta pT) carries
+  relative error ~1e-6 in each of its two terms: 4e-6 s ((1 + 2 alpha lse +
+  beta) pS + beta pT) is added to the element's bar.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import distill_oracle
+from parity_utils import bf16_ulp, to_np64
+from workloads import WORKLOADS, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU parity tests need a GPU"
+    import loss_vocab_amd  # noqa: F401
+    yield
+    torch.cuda.empty_cache()
+
+
+def _np(t):
+    return None if t is None else t.detach().cpu().numpy()
+
+
+def _lse(z):
+    m = z.max(axis=1, keepdims=True)
+    m = np.where(np.isfinite(m), m, 0.0)
+    with np.errstate(divide="ignore"):
+        return (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def kl_bound(zs64, zt64, ref):
+    """1e-5 |KL| + 4e-6 (|lse_z| + |lse_y| + max|y - z| + NLL) per row, and
+    the two logsumexps."""
+    ls, lt = _lse(zs64), _lse(zt64)
+    with np.errstate(invalid="ignore"):
+        w = np.where(np.isfinite(zt64) & np.isfinite(zs64), np.abs(zt64 - zs64), 0.0)
+    size = np.abs(ls) + np.abs(lt) + w.max(axis=1) + np.abs(ref["ce"]["nll"])
+    return 1e-5 * np.abs(ref["kl"]) + 4e-6 * size, ls, lt
+
+
+def compare(zs, zt, t, *, mask=None, alpha=0.0, beta=1.0, gamma=1.0, grad_dtype=None,
+            in_place=False, what=""):
+    import loss_vocab_amd as L
+    zs64, zt64, t_np = to_np64(zs), to_np64(zt), _np(t)
+    gdt = grad_dtype or zs.dtype
+    loss, kl, grad = L.ce_distill(zs, zt, t, mask=mask, z_alpha=alpha, kl_beta=beta,
+                                  grad_scale=gamma, grad_dtype=gdt, in_place=in_place)
+    torch.cuda.synchronize()
+    ref = distill_oracle(zs64, zt64, t_np, mask=_np(mask), z_alpha=alpha, kl_beta=beta,
+                         grad_scale=gamma)
+    valid = ref["valid"]
+    V = zs64.shape[1]
+    live = valid & (t_np >= 0) & (t_np < V)
+    kb, ls, lt = kl_bound(zs64, zt64, ref)
+    with np.errstate(invalid="ignore", over="ignore"):
+        pt = np.exp(zt64 - lt[:, None])
+    got_kl, got_loss = _np(kl).astype(np.float64), _np(loss).astype(np.float64)
+    assert np.array_equal(np.isnan(got_kl), np.isnan(ref["kl"])), what + " kl NaN pattern"
+    assert np.array_equal(np.isnan(got_loss), np.isnan(ref["loss"])), what + " loss NaN pattern"
+    m = live
+    bad = np.abs(got_kl[m] - ref["kl"][m]) > kb[m]
+    assert not bad.any(), (what + " kl", got_kl[m][bad][:3], ref["kl"][m][bad][:3])
+    lb = 1e-5 * np.abs(ref["loss"][m]) + beta * kb[m]
+    bad = np.abs(got_loss[m] - ref["loss"][m]) > lb
+    assert not bad.any(), (what + " loss", got_loss[m][bad][:3], ref["loss"][m][bad][:3])
+    # ignored rows +0.0 bit for bit
+    inv = torch.as_tensor(~valid, device=zs.device)
+    for x in (loss, kl):
+        assert bool((x[inv].cpu().view(torch.int32) == 0).all()), what + " ignored row"
+    # gradient
+    g = to_np64(grad)
+    r = ref["grad"]
+    with np.errstate(invalid="ignore", over="ignore"):
+        ps = np.exp(zs64 - ls[:, None])
+    fac = gamma * ((1 + 2 * alpha * np.abs(ls)[:, None] + beta) * ps + beta * pt)
+    fac = np.where(live[:, None], fac, 0.0)
+    if gdt == torch.float32:
+        gb = 1e-6 + 4e-6 * fac
+    else:
+        gb = 2 * bf16_ulp(r) + 4e-6 * fac + (np.abs(r) < 2.0 ** -126) * 2.0 ** -126
+    assert np.array_equal(np.isnan(g), np.isnan(r)), what + " grad NaN pattern"
+    mm = ~np.isnan(r)
+    err = np.abs(g[mm] - r[mm])
+    bad = err > gb[mm]
+    if bad.any():
+        i = np.argmax(err / gb[mm])
+        raise AssertionError(f"{what} grad: {bad.sum()} off; got {g[mm][i]!r} ref {r[mm][i]!r} "
+                             f"bound {gb[mm][i]:.3e}")
+    return loss, kl, grad, ref
+
+
+def _pair(T, V, dtype, tdtype=None, seed=0, sz=2.0, st=2.0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    zs = (torch.randn(T, V, generator=g, device=DEV) * sz).to(dtype)
+    zt = (torch.randn(T, V, generator=g, device=DEV) * st).to(tdtype or dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    return zs, zt, t
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("V", [1, 2, 7, 8, 9, 513, 4099, 32000])
+def test_vocab_sizes(dtype, V):
+    print(f"[distill] V={V} {dtype}", flush=True)
+    zs, zt, t = _pair(6, V, dtype, seed=V)
+    t[2] = -100
+    compare(zs, zt, t, alpha=1e-3, beta=0.7, gamma=0.2, what=f"V={V}")
+
+
+@pytest.mark.parametrize("sd,td,gd", [(torch.float32, torch.bfloat16, torch.float32),
+                                      (torch.bfloat16, torch.float32, torch.bfloat16),
+                                      (torch.bfloat16, torch.bfloat16, torch.float32)])
+def test_mixed_dtypes(sd, td, gd):
+    zs, zt, t = _pair(9, 3001, sd, td, seed=3)
+    compare(zs, zt, t, alpha=1e-4, beta=1.5, gamma=0.1, grad_dtype=gd, what="mixed")
+
+
+def test_unaligned_rows_take_the_element_path():
+    g = torch.Generator(device=DEV).manual_seed(5)
+    base = torch.randn(7, 2001 + 3, generator=g, device=DEV)
+    zs = base[:, 1:2002]
+    zt = torch.randn(7, 2001, generator=g, device=DEV).to(torch.bfloat16)
+    t = torch.randint(0, 2001, (7,), generator=g, device=DEV)
+    compare(zs, zt, t, beta=0.5, gamma=1.0, what="unaligned")
+
+
+def test_teacher_equal_to_student():
+    """KL is 0 and the gradient is the CE gradient: the two statistics are
+    computed identically, so the KL pieces cancel exactly."""
+    zs, _, t = _pair(8, 5000, torch.bfloat16, seed=7)
+    loss, kl, grad, ref = compare(zs, zs.clone(), t, alpha=1e-3, beta=2.0, gamma=0.5, what="same")
+    assert bool((kl == 0).all())
+
+
+def test_beta_zero_skips_the_teacher_in_the_gradient():
+    import loss_vocab_amd as L
+    zs, zt, t = _pair(8, 5000, torch.bfloat16, seed=8)
+    _, kl, grad, ref = compare(zs, zt, t, alpha=1e-3, beta=0.0, gamma=0.5, what="beta0")
+    g2 = L.ce_fused(zs, t, z_alpha=1e-3, grad_scale=0.5)[1]
+    torch.cuda.synchronize()
+    r = ref["grad"]
+    d = np.abs(to_np64(grad) - to_np64(g2))
+    assert np.all(d <= 2 * bf16_ulp(r) + 2.0 ** -126)
+
+
+def test_confident_rows_and_infinities():
+    g = torch.Generator(device=DEV).manual_seed(9)
+    T, V = 12, 3000
+    zs = torch.randn(T, V, generator=g, device=DEV) * 2
+    zt = torch.randn(T, V, generator=g, device=DEV) * 2
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    ar = torch.arange(T, device=DEV)
+    zs[ar[:6], t[:6]] = zs[ar[:6]].amax(1) + torch.linspace(18, 40, 6, device=DEV)
+    zt[ar[:6], t[:6]] = zt[ar[:6]].amax(1) + torch.linspace(20, 36, 6, device=DEV)
+    zt[6, :100] = float("-inf")            # teacher rules columns out
+    zs[7, 5] = float("-inf")
+    zs[7, t[7]] = 3.0
+    t[8] = -100
+    t[9] = V + 4                           # out of range: NaN row
+    compare(zs, zt, t, alpha=1e-4, beta=0.8, gamma=0.3, what="confident")
+
+
+def test_in_place_and_mask():
+    zs, zt, t = _pair(64, 8192, torch.bfloat16, seed=11)
+    mask = (torch.arange(64, device=DEV) % 3 != 0).to(torch.uint8)
+    compare(zs.clone(), zt, t, mask=mask, alpha=1e-4, beta=0.5, gamma=1 / 40, in_place=True,
+            what="in place")
+
+
+def test_full_shape_sampled():
+    """The 8192 x 32000 bf16 recipe as student, a second draw of it as
+    teacher: sampled rows against the oracle, every loss finite."""
+    import loss_vocab_amd as L
+    wl = WORKLOADS["cez_bf16_T8192_V32000_collapse"]
+    s = make_inputs(wl, device=DEV)
+    te = make_inputs(wl, device=DEV, seed_offset=1)["logits"]
+    zs, t = s["logits"], s["targets"]
+    loss, kl, grad = L.ce_distill(zs, te, t, z_alpha=s["z_alpha"], kl_beta=0.5,
+                                  grad_scale=s["grad_scale"])
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(1).choice(wl.T, size=24, replace=False))
+    ri = torch.as_tensor(rows, device=DEV)
+    t_np = _np(t)
+    ref = distill_oracle(to_np64(zs[ri]), to_np64(te[ri]), t_np[rows], z_alpha=s["z_alpha"],
+                         kl_beta=0.5, grad_scale=s["grad_scale"])
+    live = ref["valid"]
+    kb, _, _ = kl_bound(to_np64(zs[ri]), to_np64(te[ri]), ref)
+    got = _np(kl)[rows].astype(np.float64)
+    assert np.all(np.abs(got[live] - ref["kl"][live]) <= kb[live])
+    r = ref["grad"]
+    assert np.all(np.abs(to_np64(grad[ri]) - r) <= 2 * bf16_ulp(r) + 1e-7 + (np.abs(r) < 2.0 ** -126)
+                  * 2.0 ** -126)
+    valid = torch.as_tensor(t_np != -100, device=DEV)
+    assert bool(torch.isfinite(loss[valid]).all()) and bool((kl[valid] > -1e-3).all())
+    assert math.isfinite(float(loss.sum()))
