@@ -78,12 +78,12 @@ class CeError(RuntimeError):
         super().__init__(f"{where} failed: {status_string(status)} ({status})")
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python loss_vocab_amd/build.py` "
+            f"{path} is not built; run `python loss_vocab_amd/build.py` "
             "(the fused CE has no CPU fallback)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp = ctypes.c_void_p
     lib.ce_workspace_bytes.argtypes = [ctypes.POINTER(CeProblem)]
     lib.ce_workspace_bytes.restype = ctypes.c_size_t

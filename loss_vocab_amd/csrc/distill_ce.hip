@@ -11,18 +11,32 @@
 // (torchtitan #5661, revised PR description, Numerics):
 //   grad_t = s (-pS_nt + 2 alpha lse_z pS_t + beta (pT_nt - pS_nt)).
 //
-// One workgroup per row, both passes streamed. Pass 1 keeps, per lane, the
-// student's non-target (shift, sum), the teacher's non-target (shift, sum)
-// and U = sum 2^d (y_j - z_j) in the teacher's shifted frame; the epilogue
-// forms, in fp64,
+// One workgroup per row. Pass 1 keeps, per lane, the student's non-target
+// (shift, sum), the teacher's non-target (shift, sum) and
+// U = sum 2^d (y_j - z_j) in the teacher's shifted frame; the epilogue forms,
+// in fp64,
 //   KL = pT_t (NLL_z - NLL_y) + 2^(M_y - lse_y log2 e) U + pT_nt (lse_z - lse_y),
 // every piece from the non-target statistics and the two target logits.
+//
+// Two kernels:
+//  * distill_chunk_kernel (student and teacher of one dtype, 16-byte aligned
+//    rows): a row is cut into 16-byte chunks, chunk i * BLOCK + tid being slot
+//    i of thread tid. The first NRAW slots of both matrices stay in registers
+//    and the next NLDS in LDS (copied there straight from HBM), so they are
+//    read once; later slots are streamed U at a time, and pass 2 walks them
+//    backwards so the re-reads find the most recently read lines still in the
+//    caches. The target element is set to -inf in the one slot that holds it
+//    (the slot index is the same for the whole workgroup), so the hot loops
+//    carry no per-element test;
+//  * distill_rows_kernel (any dtype mix, any alignment): 8 elements per lane
+//    and step, both passes streamed.
 
 #include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "ce_fused.h"
 
@@ -212,6 +226,32 @@ struct RowOut {
   float cs, ct, ks, kt, gt;   // student / teacher factors, lse in log2 units, target grad
 };
 
+// The row's loss and KL from the block-reduced partial and the two target
+// logits (written to the outputs), and the factors pass 2 needs.
+__device__ __forceinline__ RowOut finish_row(const DistillParams& p, int64_t r, const Part& tot,
+                                          float zs_t, float zt_t) {
+  const Side S = side(tot.ms, tot.ss, zs_t);
+  const Side Tt = side(tot.mt, tot.st, zt_t);
+  const double alpha = p.z_alpha, beta = p.kl_beta, sc = p.grad_scale;
+  double kl = (Tt.p_t > 0.0) ? Tt.p_t * (S.nll - Tt.nll) : 0.0;
+  if (tot.mt != kNegInf && tot.st > 0.f) {
+    const double l2t = static_cast<double>(kL2E) * Tt.lse;
+    kl += exp2(static_cast<double>(tot.mt) - l2t) * static_cast<double>(tot.u);
+    kl += Tt.p_nt * (S.lse - Tt.lse);
+  }
+  const double zl = (alpha == 0.0) ? 0.0 : 2.0 * alpha * S.lse;
+  p.loss_out[r] = static_cast<float>(S.nll + ((alpha == 0.0) ? 0.0 : alpha * S.lse * S.lse) +
+                                     beta * kl);
+  if (p.kl_out) p.kl_out[r] = static_cast<float>(kl);
+  RowOut o;
+  o.cs = static_cast<float>(sc * (1.0 + zl + beta));
+  o.ct = static_cast<float>(sc * beta);
+  o.ks = static_cast<float>(static_cast<double>(kL2E) * S.lse);
+  o.kt = static_cast<float>(static_cast<double>(kL2E) * Tt.lse);
+  o.gt = static_cast<float>(sc * (-S.p_nt + zl * S.p_t + beta * (Tt.p_nt - S.p_nt)));
+  return o;
+}
+
 template <typename TS, typename TT, typename TO, bool VEC>
 __global__ __launch_bounds__(kBlock) void distill_rows_kernel(DistillParams p) {
   __shared__ Part red[kBlock / 64];
@@ -270,25 +310,7 @@ __global__ __launch_bounds__(kBlock) void distill_rows_kernel(DistillParams p) {
 #pragma unroll
       for (int w = 1; w < kBlock / 64; ++w) merge(tot, red[w]);
       // ---- fp64 epilogue ----
-      const Side S = side(tot.ms, tot.ss, zs_t);
-      const Side Tt = side(tot.mt, tot.st, zt_t);
-      const double alpha = p.z_alpha, beta = p.kl_beta, sc = p.grad_scale;
-      double kl = (Tt.p_t > 0.0) ? Tt.p_t * (S.nll - Tt.nll) : 0.0;
-      if (tot.mt != kNegInf && tot.st > 0.f) {
-        const double l2t = static_cast<double>(kL2E) * Tt.lse;
-        kl += exp2(static_cast<double>(tot.mt) - l2t) * static_cast<double>(tot.u);
-        kl += Tt.p_nt * (S.lse - Tt.lse);
-      }
-      const double zl = (alpha == 0.0) ? 0.0 : 2.0 * alpha * S.lse;
-      p.loss_out[r] = static_cast<float>(S.nll + ((alpha == 0.0) ? 0.0 : alpha * S.lse * S.lse) +
-                                         beta * kl);
-      if (p.kl_out) p.kl_out[r] = static_cast<float>(kl);
-      RowOut o;
-      o.cs = static_cast<float>(sc * (1.0 + zl + beta));
-      o.ct = static_cast<float>(sc * beta);
-      o.ks = static_cast<float>(static_cast<double>(kL2E) * S.lse);
-      o.kt = static_cast<float>(static_cast<double>(kL2E) * Tt.lse);
-      o.gt = static_cast<float>(sc * (-S.p_nt + zl * S.p_t + beta * (Tt.p_nt - S.p_nt)));
+      const RowOut o = finish_row(p, r, tot, zs_t, zt_t);
       out_sh = o;
     }
     __syncthreads();
@@ -320,6 +342,393 @@ __global__ __launch_bounds__(kBlock) void distill_rows_kernel(DistillParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Chunk kernel: student and teacher of one dtype, 16-byte aligned rows
+// ---------------------------------------------------------------------------
+
+constexpr int kNT = 2;                   // cache policy bits: non-temporal
+constexpr int kBufWord3 = 0x00020000;    // buffer descriptor word 3 (raw buffer)
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 f = {a, b};
+  const bf16x2 h = __builtin_convertvector(f, bf16x2);   // round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// A 16-byte chunk of input: W elements; NEG is a word of -inf elements.
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+  static constexpr int W = 4;
+  static constexpr uint32_t NEG = 0xff800000u;
+  __device__ static void unpack(const u32x4 v, float* x) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+  }
+};
+template <> struct Chunk<uint16_t> {
+  static constexpr int W = 8;
+  static constexpr uint32_t NEG = 0xff80ff80u;
+  __device__ static void unpack(const u32x4 v, float* x) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+// The gradient of one chunk (W values) at byte offset vo of the row's window.
+template <typename TO, int W>
+__device__ __forceinline__ void put_chunk(__amdgpu_buffer_rsrc_t rg, uint32_t vo, const float* g) {
+  if constexpr (sizeof(TO) == 2 && W == 8) {
+    const u32x4 q = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                     pack_bf16x2(g[6], g[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(q, rg, vo, 0, kNT);
+  } else if constexpr (sizeof(TO) == 2) {   // 4 fp32 in -> 4 bf16 out
+    const u32x2 q = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(q, rg, vo, 0, kNT);
+  } else {
+#pragma unroll
+    for (int h = 0; h < W / 4; ++h) {
+      const u32x4 q = {__float_as_uint(g[4 * h]), __float_as_uint(g[4 * h + 1]),
+                       __float_as_uint(g[4 * h + 2]), __float_as_uint(g[4 * h + 3])};
+      __builtin_amdgcn_raw_buffer_store_b128(q, rg, vo + 16u * h, 0, kNT);
+    }
+  }
+}
+
+template <int POL>
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t rr, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, POL);
+}
+
+// The window [off, bytes) of a row, off < bytes, formed with scalar
+// arithmetic: lanes index it from 0, and the hardware range check returns 0
+// for loads past its end and drops stores there.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t window(const void* row, uint32_t off,
+                                                         uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(row)) + off,
+                                           0, bytes - off, kBufWord3);
+}
+
+// The empty asm marks the registers as rewritten (no instruction is emitted),
+// so floats unpacked from a resident chunk in pass 1 are not kept alive for
+// pass 2: a resident chunk costs 4 registers between the passes.
+__device__ __forceinline__ void touch(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Fold N values of each side into the part: xs / xt hold -inf where a value
+// is absent (the target column, lanes past the row end). One shift update per
+// call; the teacher's U term takes e (y - z) with y - z clamped below at
+// -FLT_MAX, so absent pairs (-inf - -inf) and teacher zeros add 0, and a
+// student zero under a live teacher value adds +inf.
+template <int N>
+__device__ __forceinline__ void fold_group(Part& p, const float* xs, const float* xt) {
+  float gs = kNegInf, gt = kNegInf;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    gs = fmaxf(gs, xs[k]);
+    gt = fmaxf(gt, xt[k]);
+  }
+  const float ns = fmaxf(p.ms, gs * kL2E);
+  const float hs = ns == kNegInf ? 0.f : ns;
+  float as = 0.f;
+#pragma unroll
+  for (int k = 0; k < N; ++k) as += fexp2(__builtin_fmaf(xs[k], kL2E, -hs));
+  p.ss = __builtin_fmaf(p.ss, fexp2(p.ms - hs), as);
+  p.ms = ns;
+  const float nt = fmaxf(p.mt, gt * kL2E);
+  const float ht = nt == kNegInf ? 0.f : nt;
+  float at = 0.f, au = 0.f;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const float e = fexp2(__builtin_fmaf(xt[k], kL2E, -ht));
+    at += e;
+    au = __builtin_fmaf(e, fmaxf(xt[k] - xs[k], -__FLT_MAX__), au);
+  }
+  const float f = fexp2(p.mt - ht);
+  p.st = __builtin_fmaf(p.st, f, at);
+  p.u = __builtin_fmaf(p.u, f, au);
+  p.mt = nt;
+}
+
+//   TI     : student and teacher element type
+//   TO     : gradient element type
+//   BLOCK  : threads per workgroup
+//   NRAW   : slots per thread of each matrix kept in registers between passes
+//   NLDS   : slots per thread of each matrix kept in LDS (HBM -> LDS directly)
+//   U      : streamed slots per thread and step
+template <typename TI, typename TO, int BLOCK, int NRAW, int NLDS, int U>
+__global__ __launch_bounds__(BLOCK) void distill_chunk_kernel(DistillParams p) {
+  constexpr int W = Chunk<TI>::W;
+  constexpr uint32_t OB = W * sizeof(TO);          // gradient bytes per chunk
+  constexpr uint32_t NON = NRAW + NLDS;            // on-chip slots per thread
+  static_assert(BLOCK % 64 == 0 && BLOCK <= 1024, "whole waves");
+  __shared__ Part red[2][BLOCK / 64];
+  __shared__ RowOut outs[2];
+  __shared__ u32x4 stS[NLDS > 0 ? NLDS : 1][NLDS > 0 ? BLOCK : 1];
+  __shared__ u32x4 stT[NLDS > 0 ? NLDS : 1][NLDS > 0 ? BLOCK : 1];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63u, wid = tid >> 6;
+  // In-row byte offsets are 32-bit (the host bounds a row below 2 GiB).
+  const uint32_t V = static_cast<uint32_t>(p.V);
+  const uint32_t nchunk = V / W;
+  const uint32_t c16_last = (nchunk > 0 ? nchunk - 1 : 0) * 16u;
+  const uint32_t tail_begin = nchunk * W;
+  const uint32_t nslot = (nchunk + BLOCK - 1) / BLOCK;
+  const u32x4 neg4 = {Chunk<TI>::NEG, Chunk<TI>::NEG, Chunk<TI>::NEG, Chunk<TI>::NEG};
+  int par = 0;
+  for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
+    const int64_t t64 = p.targets[r];
+    const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+    const bool owned = t64 >= 0 && t64 < static_cast<int64_t>(V);
+    void* grow = p.grad ? static_cast<char*>(p.grad) + r * p.ld_g * static_cast<int64_t>(sizeof(TO))
+                        : nullptr;
+    if (!valid || !owned) {
+      // Ignored row: +0.0 everywhere. Valid row with an out-of-range
+      // target: NaN loss, KL and gradient row.
+      const float fill = valid ? __builtin_nanf("") : 0.f;
+      if (tid == 0) {
+        p.loss_out[r] = fill;
+        if (p.kl_out) p.kl_out[r] = fill;
+      }
+      if (grow) {
+        float f[W];
+#pragma unroll
+        for (int k = 0; k < W; ++k) f[k] = fill;
+        const __amdgpu_buffer_rsrc_t rg =
+            __builtin_amdgcn_make_buffer_rsrc(grow, 0, nchunk * OB, kBufWord3);
+        for (uint32_t c = tid; c < nchunk; c += BLOCK) put_chunk<TO, W>(rg, c * OB, f);
+        if (tid < V - tail_begin) Ld<TO>::put_one(grow, tail_begin + tid, fill);
+      }
+      continue;
+    }
+    const uint32_t t = static_cast<uint32_t>(t64);
+    const char* srow = static_cast<const char*>(p.logits) + r * p.ld_s * static_cast<int64_t>(sizeof(TI));
+    const char* trow = static_cast<const char*>(p.teacher) + r * p.ld_t * static_cast<int64_t>(sizeof(TI));
+    const float zs_t = Ld<TI>::one(srow, t), zt_t = Ld<TI>::one(trow, t);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(srow), 0, nchunk * 16u, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rt =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(trow), 0, nchunk * 16u, kBufWord3);
+
+    // The target: chunk ct, element kt, slot st (the same for every thread),
+    // lane `mine`. Word masks put -inf into element kt in that lane only.
+    const uint32_t ct = t / W, kt = t - ct * W;
+    const bool in_chunks = t < tail_begin;
+    const uint32_t st = in_chunks ? ct / BLOCK : 0xffffffffu;
+    const bool mine = in_chunks && ct - (ct / BLOCK) * BLOCK == tid;
+    const uint32_t kq = (kt * static_cast<uint32_t>(sizeof(TI))) >> 2;
+    const uint32_t ksh = (kt * static_cast<uint32_t>(sizeof(TI)) * 8u) & 31u;
+    const uint32_t kmask = sizeof(TI) == 4 ? 0xffffffffu : (0xffffu << ksh);
+    const uint32_t kput = sizeof(TI) == 4 ? 0xff800000u : (0xff80u << ksh);
+    const u32x4 and_m = {mine && kq == 0 ? ~kmask : ~0u, mine && kq == 1 ? ~kmask : ~0u,
+                         mine && kq == 2 ? ~kmask : ~0u, mine && kq == 3 ? ~kmask : ~0u};
+    const u32x4 or_m = {mine && kq == 0 ? kput : 0u, mine && kq == 1 ? kput : 0u,
+                        mine && kq == 2 ? kput : 0u, mine && kq == 3 ? kput : 0u};
+
+    // On-chip slots: offsets clamped to the last chunk, so every load is in
+    // bounds. Streamed slots: one window per step of U slots starting at slot
+    // i, lane offset (u BLOCK + tid) 16 for its u-th slot.
+    // prep() turns lanes past the row end into -inf (only the row's last slot
+    // has any) and masks the target in its slot.
+    uint32_t vin = tid * 16u;
+    asm volatile("" : "+v"(vin));
+    auto off = [&](uint32_t slot) { return min(vin + slot * (BLOCK * 16u), c16_last); };
+    auto prep = [&](u32x4& v, uint32_t slot) {
+      if (slot * BLOCK + BLOCK > nchunk && slot * BLOCK + tid >= nchunk) v = neg4;
+      if (slot == st) v = (v & and_m) | or_m;
+    };
+    auto sload = [&](const char* row, uint32_t i, int u, auto pol) {
+      return ld16<decltype(pol)::value>(window(row, i * (BLOCK * 16u), nchunk * 16u),
+                                        tid * 16u + u * (BLOCK * 16u));
+    };
+    // A step of U streamed slots needs fix-ups only if it holds the row's
+    // end or the target (the same for the whole workgroup).
+    auto special = [&](uint32_t i) { return (i + U) * BLOCK > nchunk || st - i < U; };
+
+    // ---- issue every on-chip load first ----
+    u32x4 rS[NRAW > 0 ? NRAW : 1], rT[NRAW > 0 ? NRAW : 1];
+    if (nchunk > 0) {
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) {
+        rS[i] = ld16<kNT>(rs, off(i));
+        rT[i] = ld16<kNT>(rt, off(i));
+      }
+#pragma unroll
+      for (int i = 0; i < NLDS; ++i) {
+        // lane l of a wave lands at base + 16 l: slot i of thread tid is st*[i][tid]
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(srow + off(NRAW + i)),
+            (__attribute__((address_space(3))) void*)(&stS[i][tid & ~63u]), 16, 0, kNT);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(trow + off(NRAW + i)),
+            (__attribute__((address_space(3))) void*)(&stT[i][tid & ~63u]), 16, 0, kNT);
+      }
+    }
+
+    // ---- pass 1 ----
+    Part pa{kNegInf, 0.f, kNegInf, 0.f, 0.f};
+    if (NRAW > 0 && nchunk > 0) {
+      float xs[NRAW > 0 ? NRAW * W : 1], xt[NRAW > 0 ? NRAW * W : 1];
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) {
+        prep(rS[i], i);
+        prep(rT[i], i);
+        Chunk<TI>::unpack(rS[i], xs + i * W);
+        Chunk<TI>::unpack(rT[i], xt + i * W);
+      }
+      fold_group<NRAW * W>(pa, xs, xt);
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) {
+        touch(rS[i]);
+        touch(rT[i]);
+      }
+    }
+    if (NLDS > 0 && nchunk > 0) {
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's HBM -> LDS copies have landed
+      constexpr int G = NLDS < 4 ? NLDS : 4;
+#pragma unroll
+      for (int i0 = 0; i0 < NLDS; i0 += G) {
+        float xs[G * W], xt[G * W];
+#pragma unroll
+        for (int i = i0; i < i0 + G && i < NLDS; ++i) {
+          u32x4 a = stS[i][tid], b = stT[i][tid];
+          prep(a, NRAW + i);
+          prep(b, NRAW + i);
+          Chunk<TI>::unpack(a, xs + (i - i0) * W);
+          Chunk<TI>::unpack(b, xt + (i - i0) * W);
+        }
+        fold_group<G * W>(pa, xs, xt);
+      }
+    }
+    for (uint32_t i = NON; i < nslot; i += U) {
+      u32x4 a[U], b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        a[u] = sload(srow, i, u, std::integral_constant<int, 0>{});
+        b[u] = sload(trow, i, u, std::integral_constant<int, 0>{});
+      }
+      if (special(i)) {
+        // a real branch (not selects): the fix-ups cost nothing elsewhere
+        asm volatile("");
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          prep(a[u], i + u);
+          prep(b[u], i + u);
+        }
+      }
+      float xs[U * W], xt[U * W];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        Chunk<TI>::unpack(a[u], xs + u * W);
+        Chunk<TI>::unpack(b[u], xt + u * W);
+      }
+      fold_group<U * W>(pa, xs, xt);
+    }
+    if (tid < V - tail_begin) {
+      const uint32_t j = tail_begin + tid;
+      const float xs[1] = {j == t ? kNegInf : Ld<TI>::one(srow, j)};
+      const float xt[1] = {j == t ? kNegInf : Ld<TI>::one(trow, j)};
+      fold_group<1>(pa, xs, xt);
+    }
+
+    // ---- reduction and fp64 epilogue ----
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) merge(pa, shfl_xor(pa, o));
+    if (lane == 0) red[par][wid] = pa;
+    __syncthreads();
+    if (tid == 0) {
+      Part tot = red[par][0];
+#pragma unroll
+      for (int w = 1; w < BLOCK / 64; ++w) merge(tot, red[par][w]);
+      outs[par] = finish_row(p, r, tot, zs_t, zt_t);
+    }
+    __syncthreads();
+    const RowOut o = outs[par];
+    if (grow == nullptr) continue;
+
+    // ---- pass 2: gradient; streamed slots newest first, then on-chip ----
+    // Stores go through windows like the loads: those past the row end are
+    // dropped.
+    auto store = [&](uint32_t i, int u, const float* g) {
+      put_chunk<TO, W>(window(grow, i * (BLOCK * OB), nchunk * OB), tid * OB + u * (BLOCK * OB), g);
+    };
+    auto pass2 = [&](auto teach_c) {
+      constexpr bool TEACH = decltype(teach_c)::value;
+      auto grad = [&](const u32x4 a, const u32x4 b, float* g) {
+        float xs[W];
+        Chunk<TI>::unpack(a, xs);
+        if constexpr (TEACH) {
+          float xt[W];
+          Chunk<TI>::unpack(b, xt);
+#pragma unroll
+          for (int k = 0; k < W; ++k)
+            g[k] = __builtin_fmaf(o.cs, fexp2(__builtin_fmaf(xs[k], kL2E, -o.ks)),
+                                  -o.ct * fexp2(__builtin_fmaf(xt[k], kL2E, -o.kt)));
+        } else {
+#pragma unroll
+          for (int k = 0; k < W; ++k) g[k] = o.cs * fexp2(__builtin_fmaf(xs[k], kL2E, -o.ks));
+        }
+      };
+      if (nslot > NON) {
+        for (uint32_t gi = (nslot - NON + U - 1) / U; gi-- > 0;) {
+          const uint32_t i = NON + gi * U;
+          u32x4 a[U], b[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            a[u] = sload(srow, i, u, std::integral_constant<int, kNT>{});
+            if constexpr (TEACH) b[u] = sload(trow, i, u, std::integral_constant<int, kNT>{});
+          }
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            float g[W];
+            grad(a[u], b[u], g);
+            store(i, u, g);
+          }
+        }
+      }
+      if (tid < V - tail_begin) {
+        const uint32_t j = tail_begin + tid;
+        float v = o.cs * fexp2(__builtin_fmaf(Ld<TI>::one(srow, j), kL2E, -o.ks));
+        if constexpr (TEACH) v -= o.ct * fexp2(__builtin_fmaf(Ld<TI>::one(trow, j), kL2E, -o.kt));
+        Ld<TO>::put_one(grow, j, j == t ? o.gt : v);
+      }
+#pragma unroll
+      for (int i = 0; i < NLDS; ++i) {
+        float g[W];
+        grad(stS[i][tid], stT[i][tid], g);
+        store(0, NRAW + i, g);
+      }
+#pragma unroll
+      for (int i = 0; i < NRAW; ++i) {
+        float g[W];
+        grad(rS[i], rT[i], g);
+        store(0, i, g);
+      }
+    };
+    if (o.ct != 0.f) {
+      pass2(std::integral_constant<bool, true>{});
+    } else {
+      pass2(std::integral_constant<bool, false>{});
+    }
+    // The target column: written after its chunk by the same lane, so this
+    // store lands last (a lane's stores to one address stay in order).
+    if (mine) Ld<TO>::put_one(grow, t, o.gt);
+    if constexpr (NLDS > 0) {
+      // The next row's HBM -> LDS copies overwrite the staging slots: this
+      // wave's reads of them must have returned first.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 
@@ -334,6 +743,41 @@ int device_cus_distill() {
     cus.store(c);
   }
   return c;
+}
+
+template <typename TI, typename TO, int B, int NRAW, int NLDS, int U>
+ce_status launch_chunk(const DistillParams& dp, hipStream_t st) {
+  auto kern = distill_chunk_kernel<TI, TO, B, NRAW, NLDS, U>;
+  // One resident wave of workgroups: as many per CU as fit.
+  static std::atomic<int> per_cu{0};
+  int n = per_cu.load();
+  if (n == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, B, 0) != hipSuccess || n < 1) n = 1;
+    per_cu.store(n);
+  }
+  const int64_t grid = std::min<int64_t>(dp.T, static_cast<int64_t>(n) * device_cus_distill());
+  if (grid <= 0) return CE_OK;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(B), 0, st, dp);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+// Shapes measured on MI355X (one call, both passes, beta != 0):
+//  * bf16 rows up to 64 K columns: 256 threads, 4 LDS slots, no register
+//    slots -- three workgroups per CU hide each other's row epilogues;
+//  * longer bf16 rows: 256 threads, 4 register + 8 LDS slots, two per CU;
+//  * fp32 rows: 1024 threads, 2 register + 4 LDS slots, 2 slots per step
+//    (512 threads, 4 + 4 slots when the gradient is bf16: the wider shape
+//    spills there).
+template <typename TI, typename TO>
+ce_status dispatch_chunk(const DistillParams& dp, hipStream_t st) {
+  if constexpr (sizeof(TI) == 2) {
+    if (dp.V <= 65536) return launch_chunk<TI, TO, 256, 0, 4, 4>(dp, st);
+    return launch_chunk<TI, TO, 256, 4, 8, 4>(dp, st);
+  } else if constexpr (sizeof(TO) == 4) {
+    return launch_chunk<TI, TO, 1024, 2, 4, 2>(dp, st);
+  } else {
+    return launch_chunk<TI, TO, 512, 4, 4, 4>(dp, st);
+  }
 }
 
 template <typename TS, typename TT, typename TO, bool VEC>
@@ -444,6 +888,14 @@ extern "C" ce_status ce_fused_distill(const ce_problem* p, const void* logits, c
                    rows16(grad_out, p->ld_grad, bo);
   hipStream_t st = static_cast<hipStream_t>(stream_ptr);
   (void)hipGetLastError();
+  // One dtype for both matrices, 16-byte rows and row windows below 2 GiB:
+  // the chunk kernel.
+  if (vec && teacher_dtype == p->logits_dtype && V <= (int64_t{1} << 31) / 4 - 1) {
+    const bool gf = !grad_out || p->grad_dtype == CE_DTYPE_F32;
+    if (p->logits_dtype == CE_DTYPE_F32)
+      return gf ? dispatch_chunk<float, float>(dp, st) : dispatch_chunk<float, uint16_t>(dp, st);
+    return gf ? dispatch_chunk<uint16_t, float>(dp, st) : dispatch_chunk<uint16_t, uint16_t>(dp, st);
+  }
   return p->logits_dtype == CE_DTYPE_F32
              ? dispatch_t<float>(dp, teacher_dtype, p->grad_dtype, vec, st)
              : dispatch_t<uint16_t>(dp, teacher_dtype, p->grad_dtype, vec, st);

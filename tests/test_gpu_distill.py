@@ -211,3 +211,23 @@ def test_full_shape_sampled():
     valid = torch.as_tensor(t_np != -100, device=DEV)
     assert bool(torch.isfinite(loss[valid]).all()) and bool((kl[valid] > -1e-3).all())
     assert math.isfinite(float(loss.sum()))
+
+
+@pytest.mark.parametrize("dtype,gdt,V", [(torch.bfloat16, torch.bfloat16, 32003),
+                                         (torch.bfloat16, torch.bfloat16, 128259),
+                                         (torch.bfloat16, torch.float32, 70001),
+                                         (torch.float32, torch.float32, 151937),
+                                         (torch.float32, torch.bfloat16, 20001)])
+def test_target_positions(dtype, gdt, V):
+    """One row per target position: the first chunks (kept on chip), each
+    later step of streamed chunks, the row's last whole chunk and its tail,
+    for every row-length and dtype shape of the chunked kernel."""
+    W = 16 // (4 if dtype == torch.float32 else 2)
+    nchunk = V // W
+    pos = sorted({0, W - 1, W * 256 + 3, W * 1024 * 3 + 5, W * 256 * 9 + 1, W * 4096 + 2,
+                  V // 2, (nchunk - 1) * W, (nchunk - 1) * W + W - 1, V - 1})
+    pos = [q for q in pos if q < V]
+    print(f"[distill positions] V={V} {dtype} -> {gdt}: {pos}", flush=True)
+    zs, zt, _ = _pair(len(pos), V, dtype, seed=V % 97)
+    t = torch.as_tensor(pos, device=DEV)
+    compare(zs, zt, t, alpha=1e-4, beta=0.6, gamma=0.05, grad_dtype=gdt, what=f"pos V={V}")
