@@ -32,20 +32,20 @@ METRIC_DISTILL = "fused CE + distillation (KL to a teacher matrix) fwd+bwd logit
 METRIC_FORWARD_LSE = "CE forward + logsumexp logit elems/sec + achieved HBM GB/s (% of peak)"
 
 
-def kernel_source_sha():
-    with open(os.path.join(ROOT, "loss_vocab_amd", "csrc", "ce_fused.hip"), "rb") as f:
+def kernel_source_sha(src="ce_fused.hip"):
+    with open(os.path.join(ROOT, "loss_vocab_amd", "csrc", src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profiles(workload):
+def traffic_from_profiles(workload, prefix="traffic", src="ce_fused.hip"):
     """HBM bytes per launch from committed rocprofv3 counter summaries, or None
     when none exists or the kernel source changed since they were taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"{prefix}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha") != kernel_source_sha():
+    if d.get("kernel_source_sha") != kernel_source_sha(src):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -445,7 +445,7 @@ def main():
         b_out = 4 if wl.grad_torch_dtype == torch.float32 else 2
         nbytes = wl.n_valid * wl.V * 2 * b_in + wl.T * wl.V * b_out + wl.T * (8 + 2 * 4)
         achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
-        traffic = None
+        traffic = traffic_from_profiles(wl.name, "traffic_distill", "distill_ce.hip")
         metric = METRIC_DISTILL
     if args.path == "forward":
         # Valid rows read once; targets read, loss / lse / entropy written
