@@ -69,6 +69,16 @@ typedef enum ce_status {
  * id (ignored rows included). Requires S > 0. */
 #define CE_FLAG_SEGMENT_MEAN 0x1u
 
+/* Debug check, for ce_fused_fwd_bwd and ce_fused_forward only. Before any
+ * output is written, a device scan checks that every target is ignore_index
+ * or in [0, V) and that segment ids are non-decreasing and in [0, S); the
+ * call then waits for the stream (so it cannot be captured in a graph) and
+ * returns CE_ERR_INVALID_ARG, with nothing else enqueued, if any check fails.
+ * Without the flag an out-of-range target gives a NaN row and unsorted ids
+ * are undefined. The scan's per-block results take 4096 bytes of workspace
+ * (counted by ce_workspace_bytes). */
+#define CE_FLAG_VALIDATE 0x2u
+
 /* Shape and options of one call. */
 typedef struct ce_problem {
   int64_t T;              /* rows (T >= 0; T == 0 only writes seg_loss_out zeros) */
@@ -82,9 +92,10 @@ typedef struct ce_problem {
   uint32_t flags;         /* CE_FLAG_* */
 } ce_problem;
 
-/* Device workspace (bytes) a call with this problem needs: zero without
- * segments, else room for a [T] float NLL staging array and [S+1] segment
- * offsets. Returns 0 for a null or invalid problem. */
+/* Device workspace (bytes) a call with this problem needs: room for a [T]
+ * float NLL staging array and [S+1] segment offsets when S > 0, plus 4096
+ * bytes under CE_FLAG_VALIDATE; zero otherwise. Returns 0 for a null or
+ * invalid problem. */
 size_t ce_workspace_bytes(const ce_problem* p);
 
 /*

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     CE_DTYPE_BF16,
     CE_DTYPE_F32,
     CE_FLAG_SEGMENT_MEAN,
+    CE_FLAG_VALIDATE,
     CE_OK,
     CeError,
     CeLmhead,
@@ -38,7 +39,7 @@ def _rows(t, name):
 
 
 def make_problem(logits, grad_out=None, *, num_segments=0, segment_mean=False,
-                 ignore_index=IGNORE_INDEX):
+                 ignore_index=IGNORE_INDEX, validate=False):
     if logits.dtype not in _DTYPES:
         raise TypeError(f"logits dtype {logits.dtype} is not float32/bfloat16")
     T, V = logits.shape
@@ -58,18 +59,18 @@ def make_problem(logits, grad_out=None, *, num_segments=0, segment_mean=False,
         p.grad_dtype = p.logits_dtype
     p.ignore_index = int(ignore_index)
     p.num_segments = int(num_segments)
-    p.flags = CE_FLAG_SEGMENT_MEAN if segment_mean else 0
+    p.flags = (CE_FLAG_SEGMENT_MEAN if segment_mean else 0) | (CE_FLAG_VALIDATE if validate else 0)
     return p
 
 
-def workspace_bytes(logits, *, num_segments=0):
-    return _lib.workspace_bytes(make_problem(logits, num_segments=num_segments))
+def workspace_bytes(logits, *, num_segments=0, validate=False):
+    return _lib.workspace_bytes(make_problem(logits, num_segments=num_segments, validate=validate))
 
 
 def ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale,
                      loss_out, seg_loss_out, grad_out, *, num_segments=0,
                      segment_mean=False, ignore_index=IGNORE_INDEX, workspace=None,
-                     stream=None):
+                     stream=None, validate=False):
     """Same-named wrapper of the C entry point on torch tensors.
 
     logits [T, V] f32/bf16 (row stride free, unit column stride); targets [T]
@@ -78,10 +79,13 @@ def ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale,
     itself (in place) or None (forward only); workspace: a uint8 device tensor
     of at least ``workspace_bytes`` bytes when segments are used (allocated
     here when None). The call is asynchronous on ``stream`` (default: torch's
-    current stream). Raises CeError on a non-OK status.
+    current stream). ``validate`` sets CE_FLAG_VALIDATE: a device scan of the
+    targets and segment ids, after which the call waits for the stream and
+    raises CeError(CE_ERR_INVALID_ARG) before writing anything if one is out of
+    range or the ids are unsorted. Raises CeError on a non-OK status.
     """
     p = make_problem(logits, grad_out, num_segments=num_segments,
-                     segment_mean=segment_mean, ignore_index=ignore_index)
+                     segment_mean=segment_mean, ignore_index=ignore_index, validate=validate)
     for name, t, dt in (("targets", targets, torch.int64), ("mask", mask, torch.uint8),
                         ("segment_ids", segment_ids, torch.int32),
                         ("loss_out", loss_out, torch.float32),
@@ -103,7 +107,7 @@ def ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale,
 
 def ce_fused(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
              z_alpha=0.0, grad_scale=1.0, segment_mean=False, grad_dtype=None,
-             in_place=False, want_grad=True, ignore_index=IGNORE_INDEX):
+             in_place=False, want_grad=True, ignore_index=IGNORE_INDEX, validate=False):
     """Allocate the outputs and run one fused call.
 
     Returns ``(loss[T] f32, grad[T, V] or None, seg_loss[S] f32 or None)``.
@@ -121,16 +125,18 @@ def ce_fused(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
         grad = torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
     ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale, loss, seg, grad,
                      num_segments=num_segments, segment_mean=segment_mean,
-                     ignore_index=ignore_index)
+                     ignore_index=ignore_index, validate=validate)
     return loss, grad, seg
 
 
 def ce_fused_forward(logits, targets, mask, segment_ids, z_alpha, loss_out, seg_loss_out,
                      lse_out, entropy_out, *, num_segments=0, ignore_index=IGNORE_INDEX,
-                     workspace=None, stream=None):
+                     workspace=None, stream=None, validate=False):
     """Same-named wrapper of the forward-only C entry point: loss_out [T] f32,
-    seg_loss_out [S] f32 or None, lse_out / entropy_out [T] f32 or None."""
-    p = make_problem(logits, num_segments=num_segments, ignore_index=ignore_index)
+    seg_loss_out [S] f32 or None, lse_out / entropy_out [T] f32 or None;
+    ``validate`` as for ``ce_fused_fwd_bwd``."""
+    p = make_problem(logits, num_segments=num_segments, ignore_index=ignore_index,
+                     validate=validate)
     for name, t, dt in (("targets", targets, torch.int64), ("mask", mask, torch.uint8),
                         ("segment_ids", segment_ids, torch.int32),
                         ("loss_out", loss_out, torch.float32),
@@ -151,7 +157,7 @@ def ce_fused_forward(logits, targets, mask, segment_ids, z_alpha, loss_out, seg_
 
 
 def ce_forward(logits, targets, *, mask=None, segment_ids=None, num_segments=0, z_alpha=0.0,
-               entropy=True, ignore_index=IGNORE_INDEX):
+               entropy=True, ignore_index=IGNORE_INDEX, validate=False):
     """Allocate and run the forward-only call.
 
     Returns ``(loss[T], lse[T], entropy[T] or None, seg_loss[S] or None)``.
@@ -164,7 +170,7 @@ def ce_forward(logits, targets, *, mask=None, segment_ids=None, num_segments=0, 
     seg = (torch.empty(num_segments, dtype=torch.float32, device=dev)
            if segment_ids is not None else None)
     ce_fused_forward(logits, targets, mask, segment_ids, z_alpha, loss, seg, lse, ent,
-                     num_segments=num_segments, ignore_index=ignore_index)
+                     num_segments=num_segments, ignore_index=ignore_index, validate=validate)
     return loss, lse, ent, seg
 
 

@@ -23,6 +23,7 @@ CE_ERR_WORKSPACE = 4
 CE_ERR_HIP = 5
 
 CE_FLAG_SEGMENT_MEAN = 0x1
+CE_FLAG_VALIDATE = 0x2
 
 ROW_STATE = 8   # floats of saved state per row (ce_rows_finish)
 

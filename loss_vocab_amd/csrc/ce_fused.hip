@@ -951,6 +951,34 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   }
 }
 
+// Debug scan (CE_FLAG_VALIDATE): block b writes to words[b] the OR over its
+// rows of 1 (target neither ignored nor in [0, V)), 2 (segment id outside
+// [0, S)) and 4 (segment id below the previous row's). Grid-stride over rows;
+// every block writes its word, so the words need no clearing.
+constexpr int kValidateBlocks = 1024;
+
+__global__ __launch_bounds__(256) void ce_validate_kernel(const int64_t* __restrict__ targets,
+                                                          int64_t T, int64_t V, int64_t ignore,
+                                                          const int32_t* __restrict__ seg_ids,
+                                                          int32_t S, uint32_t* __restrict__ words) {
+  __shared__ uint32_t part[256 / 64];
+  uint32_t b = 0;
+  for (int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; r < T;
+       r += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t t = targets[r];
+    if (t != ignore && (t < 0 || t >= V)) b |= 1u;
+    if (seg_ids) {
+      const int32_t s = seg_ids[r];
+      if (s < 0 || s >= S) b |= 2u;
+      if (r > 0 && seg_ids[r - 1] > s) b |= 4u;
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) b |= __shfl_xor(b, off, 64);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = b;
+  __syncthreads();
+  if (threadIdx.x == 0) words[blockIdx.x] = part[0] | part[1] | part[2] | part[3];
+}
+
 // seg_start[s] = first row whose id is >= s, for s in [0, S]; ids sorted.
 __global__ __launch_bounds__(256) void ce_seg_bounds_kernel(const int32_t* __restrict__ ids,
                                                             int64_t T, int32_t S,
@@ -1244,6 +1272,14 @@ RowParams shard_params(const ce_shard* s, const void* logits, const int64_t* tar
   return rp;
 }
 
+// Workspace bytes of the segment sums: the [T] NLL staging array and the
+// [S + 1] segment offsets (none without segments).
+size_t segment_ws_bytes(const ce_problem* p) {
+  if (p->num_segments == 0) return 0;
+  return align_up(static_cast<size_t>(p->T) * sizeof(float)) +
+         align_up((static_cast<size_t>(p->num_segments) + 1) * sizeof(int32_t));
+}
+
 // Validation and launches shared by the fused entry points. grad_out null
 // is a forward; lse_out / ent_out (forward only) are optional [T] outputs.
 ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targets,
@@ -1258,7 +1294,7 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
   if (p->logits_dtype != CE_DTYPE_F32 && p->logits_dtype != CE_DTYPE_BF16) return CE_ERR_INVALID_ARG;
   if (grad_out && p->grad_dtype != CE_DTYPE_F32 && p->grad_dtype != CE_DTYPE_BF16)
     return CE_ERR_INVALID_ARG;
-  if ((p->flags & ~CE_FLAG_SEGMENT_MEAN) != 0) return CE_ERR_INVALID_ARG;
+  if ((p->flags & ~(CE_FLAG_SEGMENT_MEAN | CE_FLAG_VALIDATE)) != 0) return CE_ERR_INVALID_ARG;
   if (p->ld_logits < V) return CE_ERR_INVALID_ARG;
   if (grad_out && p->ld_grad < V) return CE_ERR_INVALID_ARG;
   if (p->num_segments < 0) return CE_ERR_INVALID_ARG;
@@ -1309,6 +1345,23 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const int32_t S = p->num_segments;
+  if ((p->flags & CE_FLAG_VALIDATE) && T > 0) {
+    // Scan, wait, and refuse before anything else is enqueued.
+    uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p));
+    const int64_t nb = std::min<int64_t>(kValidateBlocks, (T + 255) / 256);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(ce_validate_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, stream,
+                       targets, T, V, p->ignore_index, segment_ids, S, words);
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+    uint32_t host[kValidateBlocks];
+    if (hipMemcpyAsync(host, words, static_cast<size_t>(nb) * sizeof(uint32_t),
+                       hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return CE_ERR_HIP;
+    uint32_t bad = 0;
+    for (int64_t i = 0; i < nb; ++i) bad |= host[i];
+    if (bad != 0) return CE_ERR_INVALID_ARG;
+  }
   float* nll_ws = nullptr;
   int32_t* seg_start = nullptr;
   if (S > 0) {
@@ -1375,9 +1428,8 @@ extern "C" {
 
 size_t ce_workspace_bytes(const ce_problem* p) {
   if (p == nullptr || p->T < 0 || p->num_segments < 0) return 0;
-  if (p->num_segments == 0) return 0;
-  return align_up(static_cast<size_t>(p->T) * sizeof(float)) +
-         align_up((static_cast<size_t>(p->num_segments) + 1) * sizeof(int32_t));
+  return segment_ws_bytes(p) +
+         ((p->flags & CE_FLAG_VALIDATE) ? align_up(kValidateBlocks * sizeof(uint32_t)) : 0);
 }
 
 const char* ce_status_string(int status) {

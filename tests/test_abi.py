@@ -91,6 +91,9 @@ def test_workspace_bytes():
     assert L.workspace_bytes(_problem(T=1000, S=7)) == 4096 + 256
     assert L.workspace_bytes(_problem(T=65536, S=512)) == 262144 + 2304
     assert L.LIB.ce_workspace_bytes(None) == 0
+    # the debug scan's per-block words come after the segment arrays
+    assert L.workspace_bytes(_problem(flags=2)) == 4096
+    assert L.workspace_bytes(_problem(T=1000, S=7, flags=3)) == 4096 + 256 + 4096
 
 
 # Fake device addresses: validation compares them, never dereferences them.
@@ -132,6 +135,9 @@ def _call(p, logits=A_LOGITS, targets=A_TGT, mask=0, seg=0, za=0.0, gs=1.0, loss
     ("in place with another stride", dict(grad=A_LOGITS), dict(ldg=128, ld=100), 3),
     ("workspace missing", dict(seg=A_SEG), dict(S=4), 4),
     ("workspace too small", dict(seg=A_SEG, ws=A_WS, ws_bytes=100), dict(S=4), 4),
+    ("validate without workspace", {}, dict(flags=2), 4),
+    ("validate, workspace for segments only", dict(seg=A_SEG, ws=A_WS, ws_bytes=4096 + 256),
+     dict(T=1000, S=7, flags=2), 4),
 ])
 def test_validation_errors(case, kwargs, pkw, expect):
     p = None if pkw is None else _problem(**pkw)
@@ -219,6 +225,7 @@ def test_shard_grad_nonfinite_scale():
     ("segments without ids", dict(S=3), {}, 1),
     ("workspace missing", dict(S=3), dict(seg=A_SEG), 4),
     ("bad flag", dict(flags=4), {}, 1),
+    ("validate is for the fused calls", dict(flags=2), {}, 1),
 ])
 def test_rows_finish_validation(case, pkw, kw, expect):
     p = _problem(**pkw)

@@ -433,3 +433,51 @@ def test_full_size(name):
             check_loss([float(seg[s])], [ref_s], f"{name} segment {s}")
     del inp, loss, grad, seg
     torch.cuda.empty_cache()
+
+
+def test_validate_flag():
+    """CE_FLAG_VALIDATE: clean inputs give exactly the unchecked outputs; an
+    out-of-range target, an id outside [0, S) or a decreasing id is refused
+    with CE_ERR_INVALID_ARG before any output is written."""
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(33)
+    T, V, S = 700, 1001, 9
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[::7] = -100
+    seg = (torch.arange(T, device=DEV) * S // T).to(torch.int32)
+    kw = dict(segment_ids=seg, num_segments=S, z_alpha=1e-4, grad_scale=0.5)
+    ref = L.ce_fused(z, t, **kw)
+    got = L.ce_fused(z, t, validate=True, **kw)
+    fwd_ref = L.ce_forward(z, t, segment_ids=seg, num_segments=S, z_alpha=1e-4)
+    fwd = L.ce_forward(z, t, segment_ids=seg, num_segments=S, z_alpha=1e-4, validate=True)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    for a, b in zip(fwd_ref, fwd):
+        assert torch.equal(a, b)
+
+    def refused(targets, ids):
+        loss = torch.full((T,), 7.0, device=DEV)
+        grad = torch.full((T, V), 3.0, device=DEV, dtype=torch.bfloat16)
+        segl = torch.full((S,), 5.0, device=DEV)
+        with pytest.raises(L.CeError) as e:
+            L.ce_fused_fwd_bwd(z, targets, None, ids, 0.0, 1.0, loss, segl, grad, num_segments=S,
+                               validate=True)
+        assert e.value.status == 1
+        torch.cuda.synchronize()
+        assert bool((loss == 7.0).all()) and bool((grad == 3.0).all()) and bool((segl == 5.0).all())
+
+    bad_t = t.clone()
+    bad_t[T - 1] = V
+    refused(bad_t, seg)
+    bad_t = t.clone()
+    bad_t[300] = -5
+    refused(bad_t, seg)
+    bad_s = seg.clone()
+    bad_s[T - 1] = S
+    refused(t, bad_s)
+    bad_s = seg.clone()
+    bad_s[400] = 0                      # decreasing once
+    refused(t, bad_s)
