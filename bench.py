@@ -50,6 +50,18 @@ def traffic_from_profiles(workload, prefix="traffic", src="ce_fused.hip"):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0, kl_beta=None):
     """Time the fp64 oracle on ``rows`` rows of the workload recipe (generated
     on the host), split in 256-row blocks over a thread pool, repeating the
@@ -104,7 +116,7 @@ def cpu_baseline(wl, rows, threads, forward=False, min_seconds=10.0, kl_beta=Non
     if teacher is not None:
         what, segs = "CE+KL loss and gradient against a second draw as teacher", ""
     return {"value": passes * rows * wl.V / dt, "unit": "logit elems/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3),
+            "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(dt, 3),
             "sample": f"{rows} rows x V={wl.V} of the same recipe{segs} generated on the host, "
                       f"{passes} passes; fp64 numpy {what} in 256-row blocks on {threads} threads"}
 
@@ -145,7 +157,7 @@ def cpu_baseline_lmhead(wl, rows, threads, min_seconds):
             if dt >= min_seconds:
                 break
     return {"value": passes * rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 3),
+            "cpu_model": cpu_model(), "seconds": round(dt, 3),
             "sample": f"{rows} rows of the recipe (whole weight V={wl.V} x H={wl.H}) generated on "
                       f"the host, {passes} passes; fp64 numpy logits, loss, dX and dW in 8-row "
                       f"blocks on {threads} threads"}
