@@ -1,0 +1,104 @@
+"""The entry points under HIP graph capture.
+
+A captured call enqueues only this library's kernels on the capturing
+stream (no allocation, no memset: the workspace comes from the caller), so a
+graph of it replays to the eager result. Each graph is replayed several times
+with other device work and synchronisation between the replays, and every
+replay is compared with the eager call bit for bit.
+"""
+
+from __future__ import annotations
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import loss_vocab_amd  # noqa: F401
+    yield
+    torch.cuda.empty_cache()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _replay_matches(g, outs, ref, what):
+    for rep in range(3):
+        for o in outs:
+            o.fill_(-7.0)                               # stale values must be rewritten
+        junk = torch.randn(1 << 20, device=DEV).sum()   # other eager work in between
+        g.replay()
+        torch.cuda.synchronize()
+        float(junk)
+        for o, r in zip(outs, ref):
+            assert torch.equal(_bits(o), _bits(r)), f"{what}: replay {rep} differs"
+
+
+def test_fused_call_with_segments_replays():
+    import loss_vocab_amd as L
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    T, V, S = 640, 20011, 11
+    z = (torch.randn(T, V, generator=gen, device=DEV) * 2).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=gen, device=DEV)
+    t[::9] = -100
+    seg = (torch.arange(T, device=DEV) * S // T).to(torch.int32)
+    loss = torch.empty(T, device=DEV)
+    segl = torch.empty(S, device=DEV)
+    grad = torch.empty(T, V, device=DEV, dtype=torch.bfloat16)
+    ws = torch.empty(L.workspace_bytes(z, num_segments=S), dtype=torch.uint8, device=DEV)
+
+    def call():
+        L.ce_fused_fwd_bwd(z, t, None, seg, 1e-4, 1.0, loss, segl, grad, num_segments=S,
+                           segment_mean=True, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (loss.clone(), segl.clone(), grad.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                                          # warm the launch paths off-capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    _replay_matches(g, (loss, segl, grad), ref, "fused")
+
+
+def test_forward_and_distill_calls_replay():
+    import loss_vocab_amd as L
+    gen = torch.Generator(device=DEV).manual_seed(6)
+    T, V = 300, 50021
+    z = (torch.randn(T, V, generator=gen, device=DEV) * 2).to(torch.bfloat16)
+    y = (torch.randn(T, V, generator=gen, device=DEV) * 2).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=gen, device=DEV)
+    t[::5] = -100
+    loss, lse, ent = (torch.empty(T, device=DEV) for _ in range(3))
+    dl, kl = torch.empty(T, device=DEV), torch.empty(T, device=DEV)
+    grad = torch.empty(T, V, device=DEV, dtype=torch.bfloat16)
+
+    def call():
+        L.ce_fused_forward(z, t, None, None, 1e-4, loss, None, lse, ent)
+        L.ce_fused_distill(z, y, t, None, 1e-4, 0.5, 1.0 / T, dl, kl, grad)
+
+    call()
+    torch.cuda.synchronize()
+    ref = tuple(x.clone() for x in (loss, lse, ent, dl, kl, grad))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    _replay_matches(g, (loss, lse, ent, dl, kl, grad), ref, "forward + distill")
