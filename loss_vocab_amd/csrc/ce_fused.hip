@@ -747,13 +747,23 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 
     // ---- pass 1d: streamed slots, online (shift, sum) ----------------------
     auto stream1 = [&](u32x4 (&raw)[U], uint32_t b) {
+      // Only a step that holds the row's end or the target's slot needs the
+      // fix-ups. The test is the same for the whole workgroup, and the empty
+      // asm keeps it a branch (the compiler would otherwise turn the fix-ups
+      // into selects that run in every step).
+      if (b + U * BLOCK > nchunk || (in_chunks && st * BLOCK - b < U * BLOCK)) {
+        asm volatile("");
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          fix_slot(b + u * BLOCK, raw[u]);
+          if (mine && b + u * BLOCK == st * BLOCK) raw[u] = (raw[u] & and_m) | or_m;
+        }
+      }
 #pragma unroll
       for (int g0 = 0; g0 < U; g0 += OG) {
         float x[OG * W];
 #pragma unroll
         for (int u = g0; u < g0 + OG; ++u) {
-          fix_slot(b + u * BLOCK, raw[u]);
-          if (mine && b + u * BLOCK == st * BLOCK) raw[u] = (raw[u] & and_m) | or_m;
           float xu[W];
           Elem<TI>::unpack(raw[u], xu);
 #pragma unroll
