@@ -1152,21 +1152,23 @@ ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
 }
 
 // Pick a kernel variant for (input type, output type, vector path or not).
-// Kernel shape by row length (chunks of 16 bytes), measured on MI355X:
-//  * short rows: 256 lanes, both passes streamed (the second read of a row
-//    hits the on-die caches), two load groups in flight per lane;
-//  * medium rows: 512 lanes, 8 slots per lane kept on chip (4 in VGPRs, 4
-//    in LDS), the rest streamed;
-//  * long rows: 1024 lanes, 13 slots per lane on chip (4 VGPR + 9 LDS:
+// Kernel shape by row length (chunks of 16 bytes), measured on MI355X; the
+// more of a row stays on chip, the less of it pass 2 reads again:
+//  * up to 8192 chunks: 512 lanes, 8 slots per lane in LDS (64 KiB: all of
+//    a row of up to 4096 chunks), the rest streamed 2 slots per step;
+//  * up to 16384 chunks: 1024 lanes, 9 LDS slots per lane (144 KiB), the
+//    rest streamed 2 slots per step;
+//  * longer rows: 1024 lanes, 13 slots per lane on chip (4 VGPR + 9 LDS:
 //    208 KiB of a row), the rest streamed with one online update per slot.
-// All use one workgroup per row until the grid reaches 64 per compute unit.
+// All use one workgroup per row until the grid reaches 64 per compute unit
+// (in practice the LDS footprint bounds the workgroups per CU first).
 template <typename TI, typename TO, bool WRITE>
 ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   if (!vec) return launch_rows_scalar<TI, TO, WRITE>(rp, stream);
   const int64_t nchunk = rp.V / Elem<TI>::VEC;
-  if (nchunk <= 8192) return launch_rows<TI, TO, 256, 0, 0, 0, 4, WRITE, true, true>(rp, stream, 64);
+  if (nchunk <= 8192) return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
   if (nchunk <= 16384)
-    return launch_rows<TI, TO, 512, 0, 4, 4, 2, WRITE, true, true>(rp, stream, 64);
+    return launch_rows<TI, TO, 1024, 0, 0, 9, 2, WRITE, true, true>(rp, stream, 64);
   return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
 }
 

@@ -244,8 +244,15 @@ def test_in_place_equals_out_of_place_and_forward_only(V):
     torch.cuda.synchronize()
     assert none is None
     assert grad_b.data_ptr() == zc.data_ptr()
-    assert torch.equal(loss_a, loss_b) and torch.equal(loss_a, loss_f)
+    # in place and out of place run one kernel: bit for bit
+    assert torch.equal(loss_a, loss_b)
     assert torch.equal(grad_a.view(torch.int16), grad_b.view(torch.int16))
+    # the forward-only call keeps nothing on chip and runs another workgroup
+    # shape, so its partial sums merge in another order: equal up to the
+    # fp32 rounding of the row statistics (the loss bar, rel 1e-5, holds)
+    rel = ((loss_f - loss_a).abs() / loss_a.abs().clamp_min(1e-30)).max()
+    assert float(rel) <= 2e-6
+    assert float(loss_f[5]) == 0.0 and float(loss_a[5]) == 0.0
 
 
 def test_z_alpha_zero_loss_is_nll():
@@ -299,14 +306,15 @@ def test_deterministic():
 
 
 # ---------------------------------------------------------------------------
-# Kernel tiers by row length in 16-byte chunks: up to 8192 chunks (256 lanes,
-# both passes streamed), up to 16384 (512 lanes, 4 VGPR + 4 LDS slots per
-# lane), beyond (1024 lanes, 4 VGPR + 9 LDS slots, rest streamed). Targets
+# Kernel tiers by row length in 16-byte chunks: up to 8192 chunks (512 lanes,
+# 8 LDS slots per lane, rest streamed), up to 16384 (1024 lanes, 9 LDS slots),
+# beyond (1024 lanes, 4 VGPR + 9 LDS slots, rest streamed). Targets
 # are placed in each kind of slot: register, LDS, streamed, the row's partial
 # last slot and the tail past the last whole chunk.
 # ---------------------------------------------------------------------------
 
 TIER_CASES = [
+    (torch.bfloat16, 4096 * 8), (torch.bfloat16, 4096 * 8 + 9), (torch.float32, 4096 * 4 - 3),
     (torch.bfloat16, 8192 * 8), (torch.bfloat16, 8192 * 8 + 8), (torch.bfloat16, 70001),
     (torch.bfloat16, 16384 * 8), (torch.bfloat16, 16384 * 8 + 3), (torch.bfloat16, 150000),
     (torch.float32, 8192 * 4 + 1), (torch.float32, 40000), (torch.float32, 70003),
@@ -315,7 +323,7 @@ TIER_CASES = [
 
 def _tier_targets(V, W):
     nchunk = V // W
-    lanes = 256 if nchunk <= 8192 else (512 if nchunk <= 16384 else 1024)
+    lanes = 512 if nchunk <= 8192 else 1024
     marks = [0, 1, lanes - 1, lanes, 4 * lanes - 1, 4 * lanes, 8 * lanes - 1, 8 * lanes,
              13 * lanes - 1, 13 * lanes, 17 * lanes + 5, nchunk - 1]
     elems = sorted({min(V - 1, c * W + (c % W)) for c in marks if c < max(nchunk, 1)})
