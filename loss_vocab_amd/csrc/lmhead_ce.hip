@@ -345,18 +345,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   }
 }
 
-// Tile order of the one-tile-per-workgroup kernels: blocks are dealt to the 8
-// XCDs in turn, so XCD x gets blocks x, x + 8, ...; those are mapped to one
-// contiguous run of tiles, M fastest, so the workgroups of an XCD share the B
-// tile they work on (and its L2).
+// Tile order of the one-tile-per-workgroup kernels. Tiles are grouped 8 along
+// M by 4 along N (32 tiles: the workgroups an XCD runs at once), groups M
+// fastest; blocks are dealt to the 8 XCDs in turn (XCD x gets blocks x,
+// x + 8, ...), and each XCD gets one contiguous run of groups. The 32
+// workgroups of an XCD then read 8 A and 4 B tile slices per K stage, each
+// shared through its L2 by 4 or 8 of them (M-fastest runs of single tiles
+// shared one B slice but read 32 different A slices).
+constexpr int kGM = 8, kGN = 4;
+
+__host__ __device__ inline int64_t tile_slots(int64_t tiles_m, int64_t tiles_n) {
+  return (tiles_m + kGM - 1) / kGM * kGM * ((tiles_n + kGN - 1) / kGN * kGN);
+}
+
 __device__ __forceinline__ void tile_of_block(const GemmParams& p, int64_t& m0, int64_t& n0,
                                               bool& live) {
-  const int64_t ntiles = static_cast<int64_t>(p.tiles_m) * p.tiles_n;
-  const int64_t per = (ntiles + 7) / 8;
+  const int64_t slots = tile_slots(p.tiles_m, p.tiles_n);
+  const int64_t per = (slots + 7) / 8;
   const int64_t id = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  live = id < ntiles;
-  m0 = (id % p.tiles_m) * kBM;
-  n0 = (id / p.tiles_m) * kBN;
+  const int64_t gms = (p.tiles_m + kGM - 1) / kGM;
+  const int64_t g = id / (kGM * kGN), r = id % (kGM * kGN);
+  const int64_t mt = (g % gms) * kGM + r % kGM, nt = (g / gms) * kGN + r / kGM;
+  live = id < slots && mt < p.tiles_m && nt < p.tiles_n;
+  m0 = mt * kBM;
+  n0 = nt * kBN;
 }
 
 // Gradient tiles of one column chunk: G = dL/dz for all rows and the chunk's
@@ -548,10 +560,14 @@ LmLayout layout(const ce_lmhead* p, bool backward, bool dx32) {
   L.t_pad = round_up(std::max<int64_t>(p->T, 1), kBM);
   L.tiles_n = (p->V + kBN - 1) / kBN;
   L.tiles_m_all = (p->T + kBM - 1) / kBM;
-  // one workgroup per compute unit (256), in a power-of-two number of ranges
-  // so that the workgroups of an XCD (block % 8) share one range
+  // A power-of-two number of ranges, about eight workgroups per compute unit
+  // in all (2048 = 8 x 256 CUs, run one at a time per CU): the 32 workgroups
+  // an XCD runs at once (block % 8) then cover 32 / (n_ranges / 8) row tiles
+  // of n_ranges / 8 ranges, sharing both operands' slices through L2 (with
+  // one range per XCD they read 32 row tiles' slices; 32 ranges measured 9%
+  // faster at T = 16384).
   const int64_t tm = std::max<int64_t>(L.tiles_m_all, 1);
-  const int64_t want = (256 + tm - 1) / tm;
+  const int64_t want = (2048 + tm - 1) / tm;
   int64_t nr = 1;
   while (nr < want && nr < L.tiles_n) nr *= 2;
   L.n_ranges = std::min<int64_t>(nr, L.tiles_n);
@@ -586,9 +602,12 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a && b && an && bn && a0 < b0 + bn && b0 < a0 + an;
 }
 
-// One-tile-per-workgroup kernels get 8 * ceil(tiles / 8) blocks: the XCD
-// mapping of tile_of_block covers every tile only then (the extra blocks exit).
-int64_t tile_blocks(int64_t tiles) { return (tiles + 7) / 8 * 8; }
+// One-tile-per-workgroup kernels get 8 * ceil(slots / 8) blocks: the grouped
+// XCD mapping of tile_of_block covers every tile only then (blocks of padding
+// slots exit).
+int64_t tile_blocks(int64_t tiles_m, int64_t tiles_n) {
+  return (tile_slots(tiles_m, tiles_n) + 7) / 8 * 8;
+}
 
 ce_status launch(void (*kern)(GemmParams), int64_t blocks, const GemmParams& gp, hipStream_t st) {
   if (blocks <= 0) return CE_OK;
@@ -764,7 +783,7 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
       gp.gt = gt;
       gp.ld_gt = L.t_pad;
       gp.zero_rows = T;
-      const ce_status s3 = launch_k<GradSel>(tile_blocks(L.tiles_m_all * tiles_c), gp, st);
+      const ce_status s3 = launch_k<GradSel>(tile_blocks(L.tiles_m_all, tiles_c), gp, st);
       if (s3 != CE_OK) return s3;
     }
     if (dhidden) {
@@ -782,7 +801,7 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
       gp.c = dx;
       gp.ld_c = H;
       gp.accumulate = v0 > 0 ? 1 : 0;
-      const ce_status s4 = launch_k<StoreSel>(tile_blocks(L.tiles_m_all * tiles_h), gp, st);
+      const ce_status s4 = launch_k<StoreSel>(tile_blocks(L.tiles_m_all, tiles_h), gp, st);
       if (s4 != CE_OK) return s4;
     }
     if (dweight) {
@@ -796,7 +815,7 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
       gp.tiles_n = static_cast<int32_t>(tiles_h);
       gp.c = dweight + v0 * H;
       gp.ld_c = H;
-      const ce_status s5 = launch_k<StoreSel>(tile_blocks(tiles_c * tiles_h), gp, st);
+      const ce_status s5 = launch_k<StoreSel>(tile_blocks(tiles_c, tiles_h), gp, st);
       if (s5 != CE_OK) return s5;
     }
   }
