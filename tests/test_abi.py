@@ -135,6 +135,7 @@ def _call(p, logits=A_LOGITS, targets=A_TGT, mask=0, seg=0, za=0.0, gs=1.0, loss
     ("in place with another stride", dict(grad=A_LOGITS), dict(ldg=128, ld=100), 3),
     ("workspace missing", dict(seg=A_SEG), dict(S=4), 4),
     ("workspace too small", dict(seg=A_SEG, ws=A_WS, ws_bytes=100), dict(S=4), 4),
+    ("V past the 2^28 in-row offset bound", {}, dict(V=(1 << 28) + 1), 2),
     ("validate without workspace", {}, dict(flags=2), 4),
     ("validate, workspace for segments only", dict(seg=A_SEG, ws=A_WS, ws_bytes=4096 + 256),
      dict(T=1000, S=7, flags=2), 4),

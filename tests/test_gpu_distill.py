@@ -217,7 +217,8 @@ def test_full_shape_sampled():
                                          (torch.bfloat16, torch.bfloat16, 128259),
                                          (torch.bfloat16, torch.float32, 70001),
                                          (torch.float32, torch.float32, 151937),
-                                         (torch.float32, torch.bfloat16, 20001)])
+                                         (torch.float32, torch.bfloat16, 20001),
+                                         (torch.bfloat16, torch.bfloat16, (1 << 21) + 5)])
 def test_target_positions(dtype, gdt, V):
     """One row per target position: the first chunks (kept on chip), each
     later step of streamed chunks, the row's last whole chunk and its tail,

@@ -173,7 +173,7 @@ def test_forward_without_entropy():
 
 
 SHAPES = [(torch.float32, 50001), (torch.bfloat16, 100003), (torch.float32, 170003),
-          (torch.bfloat16, 170003)]
+          (torch.bfloat16, 170003), (torch.bfloat16, (1 << 22) + 3), (torch.float32, (1 << 21) + 1)]
 
 
 @pytest.mark.parametrize("dtype,V", SHAPES, ids=[f"{str(d)[6:]}-{v}" for d, v in SHAPES])

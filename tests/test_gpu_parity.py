@@ -350,6 +350,18 @@ def test_kernel_tiers(dtype, V):
                 what=f"tier V={V} mixed")
 
 
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, (1 << 22) + 3), (torch.float32, (1 << 21) + 1)])
+def test_very_long_rows(dtype, V):
+    """Rows of millions of columns: hundreds of streamed slots per lane in
+    the long-row tier, targets at the start, the middle and the last column."""
+    print(f"[parity] long rows V={V} {dtype}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V % 1000)
+    z = (torch.randn(4, V, generator=g, device=DEV) * 2).to(dtype)
+    t = torch.tensor([0, V // 2 + 1, V - 1, -100], device=DEV)
+    z[1, V // 2 + 1] = float(z[1].float().max()) + 30.0
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / 3), what=f"long V={V}")
+
+
 def test_many_rows_per_workgroup():
     """More rows than workgroups: every workgroup loops over several rows."""
     g = torch.Generator(device=DEV).manual_seed(99)
