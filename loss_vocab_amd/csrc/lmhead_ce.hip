@@ -84,6 +84,16 @@ static_assert(sizeof(float) * kBand * kCRow <= sizeof(Stages), "band fits in the
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// (a, b) rounded to bf16 (nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 f = {a, b};
+  const bf16x2 h = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   // round to nearest even; NaN stays NaN
   uint32_t u = __float_as_uint(f);
@@ -414,27 +424,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
       uint16_t* dst = gr < p.M ? p.g + gr * p.ld_g + c0 : nullptr;
 #pragma unroll
       for (int j0 = 0; j0 < kCPT; j0 += 8) {
-        uint32_t w[4];
+        float gv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int j = j0 + e;
           const int64_t col = c0 + j;
-          float gv;
           if (col >= p.N) {
-            gv = 0.f;
+            gv[e] = 0.f;
           } else if (!live) {
-            gv = fill;
+            gv[e] = fill;
           } else if (col + p.v0 == t) {
-            gv = gtv;
+            gv[e] = gtv;
           } else {
-            gv = cnt * fexp2(__builtin_fmaf(crow[j], kL2E, -kl));
+            gv[e] = cnt * fexp2(__builtin_fmaf(crow[j], kL2E, -kl));
           }
-          const uint16_t h = to_bf16(gv);
-          crow[j] = __uint_as_float(static_cast<uint32_t>(h) << 16);
-          if (e & 1)
-            w[e >> 1] |= static_cast<uint32_t>(h) << 16;
-          else
-            w[e >> 1] = h;
+        }
+        // round to bf16 in pairs (v_cvt_pk_bf16_f32, RNE); the band keeps the
+        // rounded values for the transposed stores
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
+          crow[j0 + 2 * e] = __uint_as_float(w[e] << 16);
+          crow[j0 + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
         }
         if (dst) {
           const u32x4 v = {w[0], w[1], w[2], w[3]};
