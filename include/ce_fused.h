@@ -93,9 +93,10 @@ typedef struct ce_problem {
 } ce_problem;
 
 /* Device workspace (bytes) a call with this problem needs: room for a [T]
- * float NLL staging array and [S+1] segment offsets when S > 0, plus 4096
- * bytes under CE_FLAG_VALIDATE; zero otherwise. Returns 0 for a null or
- * invalid problem. */
+ * float NLL staging array and [S+1] segment offsets when S > 0; for fp32
+ * logits of more than 65536 columns, 32 bytes per row for the two-workgroup
+ * row mode (its per-row flags and partial statistics); plus 4096 bytes under
+ * CE_FLAG_VALIDATE; zero otherwise. Returns 0 for a null or invalid problem. */
 size_t ce_workspace_bytes(const ce_problem* p);
 
 /*
@@ -275,8 +276,9 @@ ce_status ce_shard_stats(const ce_shard* s, const void* logits, const int64_t* t
  *   [4] f_r = 1 / segment length under CE_FLAG_SEGMENT_MEAN, else 1
  *   [5] kind: 0 valid, 1 ignored, 2 poisoned (target outside [0, V): NaN loss)
  *   [6..7] 0.
- * The merge runs in fp64 in shard order (deterministic). workspace as for
- * ce_fused_fwd_bwd with the same p.
+ * The merge runs in fp64 in shard order (deterministic). workspace: with
+ * segments, the [T] NLL staging array and [S+1] offsets (ce_workspace_bytes
+ * of the same p is always enough); may be NULL without segments.
  */
 ce_status ce_rows_finish(const ce_problem* p, int32_t num_shards, const float* stats,
                          const int64_t* targets, const uint8_t* mask,

@@ -210,19 +210,28 @@ struct RowParams {
   const float* row_weight;   // gradient mode: [T] weights of the NLL term, or null
   float* lse_out;            // optional [T] full logsumexp
   float* ent_out;            // optional [T] softmax entropy (entropy variant only)
+  // pair mode: [T][2] slots of two 64-bit words per half, (shift, sum) and
+  // (target logit, 0), set to all-ones before the launch; columns
+  // [0, pair_split) are half 0, [pair_split, V) half 1
+  uint32_t* pair_part;
+  int64_t pair_split;
 };
 
 // What a row-kernel launch does.
 enum RowMode : int {
   kFused = 0,   // both passes, loss and gradient
   kStats = 1,   // pass 1 only: per-row (shift, sum, target logit) of a shard
-  kGrad = 2     // pass 2 only, from a saved per-row state
+  kGrad = 2,    // pass 2 only, from a saved per-row state
+  kPair = 3     // both passes over half a row; the two halves exchange statistics
 };
 
 // Saved per-row state: kRowState floats per row,
 //   [0] lse log2(e)   [1] p_nt = sigmoid(LSE_nt - z_t)   [2] p_t = sigmoid(z_t - LSE_nt)
 //   [3] 2 alpha lse   [4] segment factor (1 / length, or 1)   [5] kind   [6..7] zero
 constexpr int kRowState = 8;
+// Pair mode: polls of a partner's flag (each after s_sleep 2, ~128 cycles)
+// before the wait is given up (~0.1 s).
+constexpr uint32_t kPairSpin = 1u << 21;
 constexpr float kRowValid = 0.f, kRowIgnored = 1.f, kRowPoisoned = 2.f;
 
 
@@ -530,6 +539,8 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
                 "the entropy variant is a forward with streamed or LDS-staged slots");
   static_assert(MODE != kGrad || (NRES + NRAW + NLDS == 0 && WRITE), "gradient mode streams");
   static_assert(MODE != kStats || !WRITE, "statistics mode writes no gradient");
+  static_assert(MODE != kPair || (WRITE && !ENT), "pair mode is the fused call");
+  constexpr bool PAIR = MODE == kPair;
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
   constexpr uint32_t OB = W * Elem<TO>::BYTES;     // gradient bytes per chunk
   constexpr int NON = NRES + NRAW + NLDS;          // on-chip slots per thread
@@ -543,8 +554,17 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
   const uint32_t wid = tid >> 6;
+  // Pair mode: blocks b and b + 8 (same XCD, same L2) take the two halves of
+  // one row; half 0 holds columns [0, pair_split), half 1 the rest.
+  const uint32_t half = PAIR ? (blockIdx.x >> 3) & 1u : 0u;
+  const int64_t row0 = PAIR ? static_cast<int64_t>(blockIdx.x >> 4) * 8 + (blockIdx.x & 7u)
+                            : static_cast<int64_t>(blockIdx.x);
+  const int64_t row_step = PAIR ? gridDim.x / 2 : gridDim.x;
+  const int64_t c0 = (PAIR && half) ? p.pair_split : 0;
+  [[maybe_unused]] __shared__ float pair_sh[2][4];
+  [[maybe_unused]] bool pair_broken = false;   // thread 0: a partner once failed to arrive
   // In-row offsets are 32-bit (the host bounds a row below 2 GiB).
-  const uint32_t V = static_cast<uint32_t>(p.V);
+  const uint32_t V = static_cast<uint32_t>(PAIR ? (half ? p.V - p.pair_split : p.pair_split) : p.V);
   const uint32_t nchunk = V / W;
   const uint32_t clast = nchunk > 0 ? nchunk - 1 : 0;
   const uint32_t tail_begin = nchunk * W;
@@ -556,12 +576,15 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   [[maybe_unused]] const u32x4 neg4 = {neg_w, neg_w, neg_w, neg_w};
 
   int par = 0;
-  for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
+  for (int64_t r = row0; r < p.T; r += row_step, par ^= 1) {
     const int64_t t64 = p.targets[r];
-    void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes : nullptr;
+    void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes + c0 * Elem<TO>::BYTES
+                       : nullptr;
     // The target's column within these rows (t_local = V: not among them).
-    const int64_t tl = t64 - p.v0;
+    const int64_t tl = t64 - p.v0 - c0;
     const bool owned = tl >= 0 && tl < static_cast<int64_t>(V);
+    // Whether the target lies in the row at all (in pair mode, in either half).
+    const bool in_row = PAIR ? (t64 - p.v0 >= 0 && t64 - p.v0 < p.V) : owned;
     RowOut saved{};
     if constexpr (MODE == kGrad) {
       // The saved state says whether the row is ignored (+0.0), poisoned
@@ -585,16 +608,18 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
           }
           continue;
         }
-      } else if (!valid || !owned) {
+      } else if (!valid || !in_row) {
         // Ignored row: +0.0 everywhere, logits never read. Valid row with an
-        // out-of-range target: NaN loss and gradient row.
-        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
+        // out-of-range target: NaN loss and gradient row. (Both halves of a
+        // pair decide alike; half 0 writes the row's loss.)
+        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE,
+                            !PAIR || half == 0);
         continue;
       }
     }
 
     const uint32_t t = owned ? static_cast<uint32_t>(tl) : V;
-    const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes;
+    const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes + c0 * Elem<TI>::BYTES;
     const float zt = (MODE != kGrad && owned) ? Elem<TI>::load1(zrow, t) : kNegInf;
     const __amdgpu_buffer_rsrc_t rin =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(zrow), 0, nchunk * 16u, kBufWord3);
@@ -827,6 +852,59 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       }
       continue;
     }
+    float ztm = zt;   // the row's target logit (pair mode: from whichever half holds it)
+    if constexpr (PAIR) {
+      // Publish this half's partial, then take the partner's. Each half's slot
+      // is two 64-bit words, (shift, sum) and (target logit, 0), filled with
+      // all-ones before the launch; each word is stored and polled as one
+      // relaxed device-scope atomic, so a word that differs from all-ones is
+      // complete and no fence is needed (a fence at device scope would write
+      // back and invalidate this XCD's L2, which pass 2 re-reads from). The
+      // merge is symmetric, so both halves hold the same row statistics. A
+      // partner that never arrives (it cannot: the launch is cooperative)
+      // gives a NaN row after a bounded wait instead of a hang.
+      uint64_t* slot = reinterpret_cast<uint64_t*>(p.pair_part) + 4 * r;
+      if (tid == 0) {
+        const uint64_t ms = (static_cast<uint64_t>(__float_as_uint(s)) << 32) | __float_as_uint(mL);
+        __hip_atomic_store(slot + 2 * half, ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(slot + 2 * half + 1, static_cast<uint64_t>(__float_as_uint(zt)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float pm = __builtin_nanf(""), ps = __builtin_nanf(""), pz = __builtin_nanf("");
+        if (!pair_broken) {
+          uint64_t w0 = ~0ull, w1 = ~0ull;
+          uint32_t n = 0;
+          while (n < kPairSpin) {
+            if (w0 == ~0ull)
+              w0 = __hip_atomic_load(slot + 2 * (half ^ 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (w1 == ~0ull)
+              w1 = __hip_atomic_load(slot + 2 * (half ^ 1u) + 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+            if (w0 != ~0ull && w1 != ~0ull) break;
+            __builtin_amdgcn_s_sleep(2);
+            ++n;
+          }
+          if (n < kPairSpin) {
+            pm = __uint_as_float(static_cast<uint32_t>(w0));
+            ps = __uint_as_float(static_cast<uint32_t>(w0 >> 32));
+            pz = __uint_as_float(static_cast<uint32_t>(w1));
+          } else {
+            pair_broken = true;
+          }
+        }
+        pair_sh[par][0] = pm;
+        pair_sh[par][1] = ps;
+        pair_sh[par][2] = pz;
+      }
+      __syncthreads();
+      const float pm = pair_sh[par][0], ps = pair_sh[par][1], pz = pair_sh[par][2];
+      if (pm != pm) {
+        mL = __builtin_nanf("");
+        s = __builtin_nanf("");
+      } else {
+        merge(mL, s, pm, ps);
+      }
+      ztm = fmaxf(zt, pz);
+    }
     RowOut o;
     if constexpr (MODE == kGrad) {
       o = saved;
@@ -834,7 +912,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       // Wave 0 alone runs the fp64 epilogue; the others wait at the barrier,
       // leaving the SIMDs to other workgroups.
       if (wid == 0) {
-        o = row_epilogue(p, r, mL, s, zt, tid == 0);
+        o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0));
         if (lane == 0) {
           epi[par][0] = o.g_t;
           epi[par][1] = o.cnt;
@@ -850,7 +928,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       o.cnt = epi[par][1];
       o.kl = epi[par][2];
     } else {
-      o = row_epilogue(p, r, mL, s, zt, tid == 0);
+      o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0));
       if constexpr (ENT) {
         if (tid == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
       }
@@ -1144,6 +1222,43 @@ ce_status launch_rows(const RowParams& rp, hipStream_t stream, int per_cu_cap = 
       occ, rp, stream, per_cu_cap);
 }
 
+__global__ __launch_bounds__(256) void ce_fill_u32_kernel(uint32_t* __restrict__ p, int64_t n,
+                                                          uint32_t v) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = v;
+}
+
+// Pair mode for long rows: the long-row shape on half rows, two workgroups
+// of one XCD per row. The launch is cooperative (every workgroup resident, so
+// a partner always arrives) on a grid of whole XCD pairs; when the runtime
+// refuses it, the whole-row kernel runs instead.
+template <typename TI, typename TO>
+ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
+  auto kern = ce_rows_kernel<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1, kPair>;
+  static std::atomic<int> occ{0};
+  int per_cu = occ.load(std::memory_order_relaxed);
+  if (per_cu <= 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 1024, 0) != hipSuccess)
+      per_cu = 0;
+    occ.store(per_cu > 0 ? per_cu : -1, std::memory_order_relaxed);
+  }
+  const int64_t grid = static_cast<int64_t>(device_cus()) * (per_cu > 0 ? per_cu : 0) / 16 * 16;
+  if (grid >= 16) {
+    const int64_t n = 8 * rp.T;
+    const unsigned nb = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024));
+    hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(nb), dim3(256), 0, stream, rp.pair_part, n, ~0u);
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+    RowParams arg = rp;
+    void* args[] = {&arg};
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(static_cast<unsigned>(grid)),
+                                   dim3(1024), args, 0, stream) == hipSuccess)
+      return CE_OK;
+    (void)hipGetLastError();
+  }
+  return launch_rows<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1>(rp, stream, 64);
+}
+
 template <typename TI, typename TO, bool WRITE, int MODE = kFused, bool ENT = false>
 ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
   static std::atomic<int> occ{0};
@@ -1169,6 +1284,11 @@ ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   if (nchunk <= 8192) return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
   if (nchunk <= 16384)
     return launch_rows<TI, TO, 1024, 0, 0, 9, 2, WRITE, true, true>(rp, stream, 64);
+  if constexpr (WRITE && Elem<TI>::BYTES == 4) {
+    // fp32 rows this long: two workgroups per row keep twice the share of
+    // each row on chip (the pass-2 re-reads fall by half)
+    if (rp.pair_part != nullptr) return launch_rows_pair<TI, TO>(rp, stream);
+  }
   return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
 }
 
@@ -1292,6 +1412,14 @@ size_t segment_ws_bytes(const ce_problem* p) {
          align_up((static_cast<size_t>(p->num_segments) + 1) * sizeof(int32_t));
 }
 
+// fp32 rows of more than 16384 16-byte chunks run in pair mode, which needs
+// 32 bytes of exchange slots per row (placed after the segment arrays).
+bool pair_rows(const ce_problem* p) { return p->logits_dtype == CE_DTYPE_F32 && p->V / 4 > 16384; }
+size_t pair_ws_bytes(const ce_problem* p) {
+  if (!pair_rows(p)) return 0;
+  return align_up(static_cast<size_t>(p->T) * 8 * sizeof(uint32_t));
+}
+
 // Validation and launches shared by the fused entry points. grad_out null
 // is a forward; lse_out / ent_out (forward only) are optional [T] outputs.
 ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targets,
@@ -1359,7 +1487,8 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
   const int32_t S = p->num_segments;
   if ((p->flags & CE_FLAG_VALIDATE) && T > 0) {
     // Scan, wait, and refuse before anything else is enqueued.
-    uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p));
+    uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p) +
+                                                  pair_ws_bytes(p));
     const int64_t nb = std::min<int64_t>(kValidateBlocks, (T + 255) / 256);
     (void)hipGetLastError();
     hipLaunchKernelGGL(ce_validate_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, stream,
@@ -1408,6 +1537,10 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
     rp.grad_scale = grad_scale;
     rp.lse_out = lse_out;
     rp.ent_out = ent_out;
+    if (grad_out && pair_rows(p)) {
+      rp.pair_part = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p));
+      rp.pair_split = (V / 4 / 2) * 4;   // a chunk boundary
+    }
 
     const bool vec_in = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) &&
                         ((p->ld_logits * bi) % 16 == 0);
@@ -1440,7 +1573,7 @@ extern "C" {
 
 size_t ce_workspace_bytes(const ce_problem* p) {
   if (p == nullptr || p->T < 0 || p->num_segments < 0) return 0;
-  return segment_ws_bytes(p) +
+  return segment_ws_bytes(p) + pair_ws_bytes(p) +
          ((p->flags & CE_FLAG_VALIDATE) ? align_up(kValidateBlocks * sizeof(uint32_t)) : 0);
 }
 
@@ -1507,7 +1640,7 @@ ce_status ce_rows_finish(const ce_problem* p, int32_t num_shards, const float* s
   if (T > INT32_MAX) return CE_ERR_UNSUPPORTED;
   if (T > 0 && (!stats || !targets || !loss_out || !row_state)) return CE_ERR_INVALID_ARG;
   if (!std::isfinite(z_alpha)) return CE_ERR_INVALID_ARG;
-  const size_t need = ce_workspace_bytes(p);
+  const size_t need = segment_ws_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CE_ERR_WORKSPACE;
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0) return CE_ERR_WORKSPACE;
 

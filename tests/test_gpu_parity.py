@@ -362,6 +362,34 @@ def test_very_long_rows(dtype, V):
     compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / 3), what=f"long V={V}")
 
 
+def test_long_fp32_rows_two_workgroups_per_row():
+    """fp32 rows past 16384 chunks run two workgroups per row that exchange
+    their halves' statistics: segments, a mask, ignored and out-of-range rows,
+    targets in either half and at the split, in place equal to out of place."""
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(71)
+    T, V, S = 40, 70001, 3
+    split = (V // 4 // 2) * 4
+    z = torch.randn(T, V, generator=g, device=DEV) * 2
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[0], t[1], t[2], t[3] = split - 1, split, 0, V - 1
+    t[5] = -100
+    t[6] = V + 3                                  # out of range: NaN row
+    z[7, t[7]] = z[7].max() + 35.0                # confident row
+    mask = (torch.arange(T, device=DEV) % 9 != 4).to(torch.uint8)
+    seg = (torch.arange(T, device=DEV) * S // T).to(torch.int32)
+    inp = _inp(z, t, alpha=1e-4, gamma=1.0, seg=seg, S=S, seg_mean=True)
+    loss_a, grad_a, seg_a, _ = compare_all(inp, mask=mask, what="pair rows")
+    zc = z.clone()
+    loss_b, grad_b, seg_b = L.ce_fused(zc, t, mask=mask, segment_ids=seg, num_segments=S,
+                                       z_alpha=1e-4, grad_scale=1.0, segment_mean=True,
+                                       in_place=True)
+    torch.cuda.synchronize()
+    assert torch.equal(loss_a.nan_to_num(7.0), loss_b.nan_to_num(7.0))
+    assert torch.equal(grad_a.nan_to_num(7.0), grad_b.nan_to_num(7.0))
+    assert torch.equal(seg_a.nan_to_num(7.0), seg_b.nan_to_num(7.0))   # a NaN row poisons its segment
+
+
 def test_many_rows_per_workgroup():
     """More rows than workgroups: every workgroup loops over several rows."""
     g = torch.Generator(device=DEV).manual_seed(99)
