@@ -45,6 +45,11 @@ CASES = [
     (torch.bfloat16, 25, 1003, 3, 1, 1e-4, 0),    # unaligned shard starts: one-element kernel
     (torch.float32, 25, 777, 5, 1, 0.0, 4),
     (torch.bfloat16, 12, 70001, 2, 8, 1e-4, 0),
+    # shard rows on both sides of the 4096-chunk shape boundary in one call
+    (torch.bfloat16, 20, 65537, 2, 8, 1e-4, 0),
+    # shard rows past 14000 chunks (the deepest statistics shape)
+    (torch.bfloat16, 12, 230011, 2, 8, 1e-4, 0),
+    (torch.float32, 10, 120001, 2, 4, 1e-4, 3),
 ]
 
 
@@ -171,18 +176,19 @@ def test_split_pages_share_full_size():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("dtype,shards", [(torch.bfloat16, 2), (torch.float32, 3)])
-def test_weighted_backward(dtype, shards):
+@pytest.mark.parametrize("dtype,shards,V", [(torch.bfloat16, 2, 5003), (torch.float32, 3, 5003),
+                                            (torch.bfloat16, 2, 70001)])
+def test_weighted_backward(dtype, shards, V):
     """A deferred child sharing the softmax: forward (statistics + finish with
     per-segment NLL sums), then per-row weights fixed between forward and
     backward (here seeded per-segment weights broadcast to their rows, as a
     GSPO-style seam would produce), then the weighted gradient."""
     import loss_vocab_amd as L
     g = torch.Generator(device=DEV).manual_seed(31 + shards)
-    T, V, S = 200, 5003, 8
+    T, S = (200 if V < 10000 else 40), 8
     z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(dtype)
     t = torch.randint(0, V, (T,), generator=g, device=DEV)
-    t[[3, 50, 51]] = -100
+    t[[3, T // 4, T // 4 + 1]] = -100
     seg = torch.sort(torch.randint(0, S, (T,), generator=g, device=DEV)).values.to(torch.int32)
     w_seg = torch.randn(S, generator=torch.Generator().manual_seed(7), dtype=torch.float32)
     w_row = w_seg.to(DEV)[seg.long()].contiguous()
