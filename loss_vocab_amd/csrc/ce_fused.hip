@@ -44,6 +44,9 @@ namespace {
 constexpr float kL2E = 1.44269504088896340736f;  // log2(e), rounded to float
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kNT = 2;                           // cache policy bits: non-temporal
+// Read-only int64 in the constant address space: uniform loads become scalar
+// loads through the scalar cache.
+typedef const __attribute__((address_space(4))) int64_t kconst_i64;
 constexpr int kBufWord3 = 0x00020000;            // buffer descriptor word 3 (gfx9 raw buffer)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -575,9 +578,16 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   const uint32_t neg_w = Elem<TI>::NEG_INF_WORD;
   [[maybe_unused]] const u32x4 neg4 = {neg_w, neg_w, neg_w, neg_w};
 
+  // Labels are read through the scalar cache (the constant address space: the
+  // kernel never writes them), one row ahead: the load waits on the LDS
+  // counter, so neither its latency nor the previous row's gradient stores
+  // still in flight hold up the start of a row.
+  const kconst_i64* labels = (const kconst_i64*)p.targets;
+  int64_t t_next = row0 < p.T ? labels[row0] : 0;
   int par = 0;
   for (int64_t r = row0; r < p.T; r += row_step, par ^= 1) {
-    const int64_t t64 = p.targets[r];
+    const int64_t t64 = t_next;
+    if (r + row_step < p.T) t_next = labels[r + row_step];
     void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes + c0 * Elem<TO>::BYTES
                        : nullptr;
     // The target's column within these rows (t_local = V: not among them).
@@ -771,6 +781,40 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
     }
 
     // ---- pass 1d: streamed slots, online (shift, sum) ----------------------
+    // A step's slots at b + u BLOCK. In the long-row shapes (one online update
+    // per slot, OG = 1) slots wholly past the row end are neither loaded nor
+    // reduced nor stored (the tests are uniform over the workgroup and only
+    // the row's last steps take the slow branch; a skipped slot holds -inf, a
+    // constant, so no register stays live from the previous step). With two
+    // slots per update the tail wastes at most one group, and the extra
+    // branches measured slower there (3% on 16032-chunk rows), so those shapes
+    // load and reduce every slot of a step; lanes past the end load the last
+    // chunk again (one broadcast line) and fix_slot makes them -inf.
+    constexpr bool SKIP_TAIL = OG == 1;
+    auto load_group = [&](u32x4 (&raw)[U], uint32_t b, auto load) {
+      if (!SKIP_TAIL || b + (U - 1) * BLOCK < nchunk) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = load(b + u * BLOCK);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = b + u * BLOCK < nchunk ? load(b + u * BLOCK) : neg4;
+      }
+    };
+    auto reduce_group = [&](const u32x4 (&raw)[U], int g0) {
+      float x[OG * W];
+#pragma unroll
+      for (int u = g0; u < g0 + OG; ++u) {
+        float xu[W];
+        Elem<TI>::unpack(raw[u], xu);
+#pragma unroll
+        for (int k = 0; k < W; ++k) x[(u - g0) * W + k] = xu[k];
+      }
+      if constexpr (ENT) {
+        online_group3<OG * W>(mL, s, hs, x);
+      } else {
+        online_group<OG * W>(mL, s, x);
+      }
+    };
     auto stream1 = [&](u32x4 (&raw)[U], uint32_t b) {
       // Only a step that holds the row's end or the target's slot needs the
       // fix-ups. The test is the same for the whole workgroup, and the empty
@@ -783,48 +827,34 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
           fix_slot(b + u * BLOCK, raw[u]);
           if (mine && b + u * BLOCK == st * BLOCK) raw[u] = (raw[u] & and_m) | or_m;
         }
-      }
 #pragma unroll
-      for (int g0 = 0; g0 < U; g0 += OG) {
-        float x[OG * W];
-#pragma unroll
-        for (int u = g0; u < g0 + OG; ++u) {
-          float xu[W];
-          Elem<TI>::unpack(raw[u], xu);
-#pragma unroll
-          for (int k = 0; k < W; ++k) x[(u - g0) * W + k] = xu[k];
+        for (int g0 = 0; g0 < U; g0 += OG) {
+          if (SKIP_TAIL && b + g0 * BLOCK >= nchunk) break;
+          reduce_group(raw, g0);
         }
-        if constexpr (ENT) {
-          online_group3<OG * W>(mL, s, hs, x);
-        } else {
-          online_group<OG * W>(mL, s, x);
-        }
+      } else {
+#pragma unroll
+        for (int g0 = 0; g0 < U; g0 += OG) reduce_group(raw, g0);
       }
     };
     if constexpr (MODE == kGrad) {
       // no pass 1
     } else if constexpr (PF) {
       // Two groups in flight: group B's loads run while group A is reduced.
-      // Loads past the row end are clamped to its last chunk (one broadcast
-      // line) and their lanes are -inf, so a trailing empty group is harmless.
       if (NON * BLOCK < nchunk) {
         u32x4 ra[U], rb[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) ra[u] = load_slot(NON * BLOCK + u * BLOCK);
+        load_group(ra, NON * BLOCK, load_slot);
         for (uint32_t b = NON * BLOCK; b < nchunk; b += 2 * U * BLOCK) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) rb[u] = load_slot(b + (U + u) * BLOCK);
+          load_group(rb, b + U * BLOCK, load_slot);
           stream1(ra, b);
-#pragma unroll
-          for (int u = 0; u < U; ++u) ra[u] = load_slot(b + (2 * U + u) * BLOCK);
+          load_group(ra, b + 2 * U * BLOCK, load_slot);
           stream1(rb, b + U * BLOCK);
         }
       }
     } else {
       for (uint32_t b = NON * BLOCK; b < nchunk; b += U * BLOCK) {
         u32x4 raw[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = load_slot(b + u * BLOCK);
+        load_group(raw, b, load_slot);
         stream1(raw, b);
       }
     }
@@ -992,32 +1022,39 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
         store_slot((NRES + NRAW + i) * BLOCK, g);
       }
       auto stream2 = [&](const u32x4 (&raw)[U], uint32_t b) {
+        if (SKIP_TAIL && b + U * BLOCK > nchunk) {
+          // the row's last step: slots wholly past the end are skipped
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          float g[W];
-          grad_of(raw[u], g);
-          store_slot(b + u * BLOCK, g);
+          for (int u = 0; u < U; ++u) {
+            if (b + u * BLOCK >= nchunk) break;
+            float g[W];
+            grad_of(raw[u], g);
+            store_slot(b + u * BLOCK, g);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            float g[W];
+            grad_of(raw[u], g);
+            store_slot(b + u * BLOCK, g);
+          }
         }
       };
       if constexpr (PF) {
         if (NON * BLOCK < nchunk) {
           u32x4 ra[U], rb[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) ra[u] = load_slot_last_use(NON * BLOCK + u * BLOCK);
+          load_group(ra, NON * BLOCK, load_slot_last_use);
           for (uint32_t b = NON * BLOCK; b < nchunk; b += 2 * U * BLOCK) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) rb[u] = load_slot_last_use(b + (U + u) * BLOCK);
+            load_group(rb, b + U * BLOCK, load_slot_last_use);
             stream2(ra, b);
-#pragma unroll
-            for (int u = 0; u < U; ++u) ra[u] = load_slot_last_use(b + (2 * U + u) * BLOCK);
+            load_group(ra, b + 2 * U * BLOCK, load_slot_last_use);
             stream2(rb, b + U * BLOCK);
           }
         }
       } else {
         for (uint32_t b = NON * BLOCK; b < nchunk; b += U * BLOCK) {
           u32x4 raw[U];
-#pragma unroll
-          for (int u = 0; u < U; ++u) raw[u] = load_slot_last_use(b + u * BLOCK);
+          load_group(raw, b, load_slot_last_use);
           stream2(raw, b);
         }
       }
@@ -1033,8 +1070,10 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
     }
     if constexpr (NLDS > 0) {
       // The next row's HBM -> LDS copies overwrite the staging slots: every
-      // read of them by this wave must have returned first.
-      __builtin_amdgcn_s_waitcnt(0);
+      // LDS read of them by this wave must have returned first. (Pass 2 has
+      // consumed each one before its store; the gradient stores themselves
+      // need not land before the next row's loads go out.)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
 }
