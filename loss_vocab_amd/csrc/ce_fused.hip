@@ -47,6 +47,7 @@ constexpr int kNT = 2;                           // cache policy bits: non-tempo
 // Read-only int64 in the constant address space: uniform loads become scalar
 // loads through the scalar cache.
 typedef const __attribute__((address_space(4))) int64_t kconst_i64;
+typedef const __attribute__((address_space(4))) int32_t kconst_i32;
 constexpr int kBufWord3 = 0x00020000;            // buffer descriptor word 3 (gfx9 raw buffer)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -188,12 +189,6 @@ __device__ __forceinline__ void online_group3(float& mL, float& s, float& u, con
   mL = (mn == kNegInf) ? kNegInf : sh;
 }
 
-__device__ __forceinline__ double sigmoid_d(double x) {
-  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
-  const double e = exp(x);
-  return e / (1.0 + e);
-}
-
 struct RowParams {
   const void* logits;
   void* grad;
@@ -271,14 +266,19 @@ struct RowLoss {
   double p_t;   // sigmoid(z_t - LSE_nt): target probability
 };
 
+// One exponential serves all four: with e = exp(-|x|), softplus(x) =
+// max(x, 0) + log1p(e), and sigmoid(+-x) is 1 / (1 + e) on the side where
+// the argument is >= 0 and e / (1 + e) on the other (the stable forms).
 __device__ __forceinline__ RowLoss row_loss(double lse_nt, double zt_d) {
   RowLoss o;
   const double xx = lse_nt - zt_d;                       // LSE_nt - z_t
-  const double l1p = log1p(exp(-fabs(xx)));
+  const double e = exp(-fabs(xx));
+  const double l1p = log1p(e);
   o.nll = (xx > 0.0 ? xx : 0.0) + l1p;                   // softplus
   o.lse = (lse_nt > zt_d ? lse_nt : zt_d) + l1p;         // logaddexp
-  o.p_nt = sigmoid_d(xx);
-  o.p_t = sigmoid_d(-xx);
+  const double d = 1.0 + e;
+  o.p_nt = (xx >= 0.0) ? 1.0 / d : e / d;                // sigmoid(x)
+  o.p_t = (xx <= 0.0) ? 1.0 / d : e / d;                 // sigmoid(-x)
   return o;
 }
 
@@ -296,15 +296,15 @@ __device__ __forceinline__ double segment_factor(const int32_t* seg_ids, const i
   return 1.0 / static_cast<double>(len > 0 ? len : 1);
 }
 
+// seg_f: the row's segment factor (1 / segment length, or 1).
 __device__ __forceinline__ RowOut row_epilogue(const RowParams& p, int64_t r, float M, float S,
-                                               float zt, bool write_loss) {
+                                               float zt, bool write_loss, double seg_f) {
   const double l2e = static_cast<double>(kL2E);
   const RowLoss L = row_loss(lse_from_partial(M == kNegInf ? -HUGE_VAL : static_cast<double>(M),
                                               static_cast<double>(S)),
                              static_cast<double>(zt));
   const double nll = L.nll, lse = L.lse, p_nt = L.p_nt, p_t = L.p_t;
-  double scale = static_cast<double>(p.grad_scale);
-  if (p.seg_mean) scale *= segment_factor(p.seg_ids, p.seg_start, p.num_segments, r);
+  const double scale = static_cast<double>(p.grad_scale) * seg_f;
   const double alpha = static_cast<double>(p.z_alpha);
   const double zfac = (alpha == 0.0) ? 0.0 : 2.0 * alpha * lse;
   if (write_loss) {
@@ -488,7 +488,9 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_scalar_kernel(RowParams p) {
         }
         continue;
       } else {
-        o = row_epilogue(p, r, mL, s, zt, tid == 0);
+        o = row_epilogue(p, r, mL, s, zt, tid == 0,
+                         p.seg_mean ? segment_factor(p.seg_ids, p.seg_start, p.num_segments, r)
+                                    : 1.0);
       }
     }
     if constexpr (WRITE) {
@@ -583,6 +585,8 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   // counter, so neither its latency nor the previous row's gradient stores
   // still in flight hold up the start of a row.
   const kconst_i64* labels = (const kconst_i64*)p.targets;
+  const kconst_i32* seg_ids = (const kconst_i32*)p.seg_ids;
+  const kconst_i32* seg_start = (const kconst_i32*)p.seg_start;
   int64_t t_next = row0 < p.T ? labels[row0] : 0;
   int par = 0;
   for (int64_t r = row0; r < p.T; r += row_step, par ^= 1) {
@@ -675,6 +679,11 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       v.w = out ? neg_w : v.w;
     };
 
+    // The row's segment id goes out now (scalar load); its length is read
+    // once the on-chip loads are in flight, so the epilogue waits on neither.
+    [[maybe_unused]] int32_t sid = 0;
+    if (MODE != kGrad && p.seg_mean) sid = seg_ids[r];
+
     // ---- issue every on-chip load first ------------------------------------
     u32x4 rawe[NRES > 0 ? NRES : 1];
     u32x4 rawv[NRAW > 0 ? NRAW : 1];
@@ -694,6 +703,13 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
               (__attribute__((address_space(3))) void*)(&stage[i][tid & ~63u]), 16, 0, kNT);
         }
       }
+    }
+
+    [[maybe_unused]] int32_t seg_len = 1;   // uniform: stays in scalar registers
+    if (MODE != kGrad && p.seg_mean) {
+      sid = sid < 0 ? 0 : (sid >= p.num_segments ? p.num_segments - 1 : sid);
+      const int32_t len = seg_start[sid + 1] - seg_start[sid];
+      seg_len = len > 0 ? len : 1;
     }
 
     float mL = kNegInf, s = 0.f;
@@ -936,13 +952,14 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       ztm = fmaxf(zt, pz);
     }
     RowOut o;
+    [[maybe_unused]] const double seg_f = 1.0 / static_cast<double>(seg_len);
     if constexpr (MODE == kGrad) {
       o = saved;
     } else if constexpr (EPI1) {
       // Wave 0 alone runs the fp64 epilogue; the others wait at the barrier,
       // leaving the SIMDs to other workgroups.
       if (wid == 0) {
-        o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0));
+        o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0), seg_f);
         if (lane == 0) {
           epi[par][0] = o.g_t;
           epi[par][1] = o.cnt;
@@ -958,7 +975,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       o.cnt = epi[par][1];
       o.kl = epi[par][2];
     } else {
-      o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0));
+      o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0), seg_f);
       if constexpr (ENT) {
         if (tid == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
       }
