@@ -482,9 +482,16 @@ __global__ __launch_bounds__(BLOCK) void distill_chunk_kernel(DistillParams p) {
   const uint32_t tail_begin = nchunk * W;
   const uint32_t nslot = (nchunk + BLOCK - 1) / BLOCK;
   const u32x4 neg4 = {Chunk<TI>::NEG, Chunk<TI>::NEG, Chunk<TI>::NEG, Chunk<TI>::NEG};
+  // Labels are read through the scalar cache (constant address space: the
+  // kernel never writes them), one row ahead, so a row does not open by
+  // waiting on a vector load (and with it on the previous row's stores).
+  typedef const __attribute__((address_space(4))) int64_t label_t;
+  const label_t* labels = (const label_t*)p.targets;
+  int64_t t_next = static_cast<int64_t>(blockIdx.x) < p.T ? labels[blockIdx.x] : 0;
   int par = 0;
   for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
-    const int64_t t64 = p.targets[r];
+    const int64_t t64 = t_next;
+    if (r + gridDim.x < p.T) t_next = labels[r + gridDim.x];
     const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
     const bool owned = t64 >= 0 && t64 < static_cast<int64_t>(V);
     void* grow = p.grad ? static_cast<char*>(p.grad) + r * p.ld_g * static_cast<int64_t>(sizeof(TO))

@@ -318,6 +318,14 @@ TIER_CASES = [
     (torch.bfloat16, 8192 * 8), (torch.bfloat16, 8192 * 8 + 8), (torch.bfloat16, 70001),
     (torch.bfloat16, 16384 * 8), (torch.bfloat16, 16384 * 8 + 3), (torch.bfloat16, 150000),
     (torch.float32, 8192 * 4 + 1), (torch.float32, 40000), (torch.float32, 70003),
+    # long-row shapes (13 on-chip slots of 1024 chunks per lane, then steps of
+    # 4 streamed slots, two steps per loop turn): streamed parts of 3 slots and
+    # one chunk, exactly 2 and 3 steps (a step and a turn wholly past the end)
+    (torch.bfloat16, 16385 * 8 + 5), (torch.bfloat16, (13312 + 8192) * 8),
+    (torch.bfloat16, (13312 + 12288) * 8),
+    # two workgroups per fp32 row: halves with one streamed chunk and with
+    # exactly one step of streamed slots
+    (torch.float32, 2 * (13312 + 1) * 4), (torch.float32, 2 * (13312 + 4096) * 4),
 ]
 
 
