@@ -1328,7 +1328,7 @@ ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
 //  * up to 8192 chunks: 512 lanes, 8 slots per lane in LDS (64 KiB: all of
 //    a row of up to 4096 chunks), the rest streamed 2 slots per step;
 //  * up to 16384 chunks: 1024 lanes, 9 LDS slots per lane (144 KiB), the
-//    rest streamed 2 slots per step;
+//    rest streamed 4 slots per step with one online update per slot;
 //  * longer rows: 1024 lanes, 13 slots per lane on chip (4 VGPR + 9 LDS:
 //    208 KiB of a row), the rest streamed with one online update per slot.
 // All use one workgroup per row until the grid reaches 64 per compute unit
@@ -1339,7 +1339,7 @@ ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   const int64_t nchunk = rp.V / Elem<TI>::VEC;
   if (nchunk <= 8192) return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
   if (nchunk <= 16384)
-    return launch_rows<TI, TO, 1024, 0, 0, 9, 2, WRITE, true, true>(rp, stream, 64);
+    return launch_rows<TI, TO, 1024, 0, 0, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
   if constexpr (WRITE && Elem<TI>::BYTES == 4) {
     // fp32 rows this long: two workgroups per row keep twice the share of
     // each row on chip (the pass-2 re-reads fall by half)
