@@ -111,6 +111,10 @@ size_t ce_workspace_bytes(const ce_problem* p);
  *                ignore_index test).
  *  segment_ids   [T] int32, non-decreasing, values in [0, S); NULL iff S == 0
  *                (with T == 0 it is never read and may be NULL).
+ *                targets, mask and segment_ids must stay unchanged until the
+ *                call completes and must not overlap an output or the
+ *                workspace (the kernels read them through the scalar cache);
+ *                such an overlap is not detected.
  *  z_alpha       z-loss weight (0 disables it).
  *  grad_scale    upstream factor of the gradient (e.g. 1 / number of valid
  *                rows for a token mean).
