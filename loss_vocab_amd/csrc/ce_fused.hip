@@ -581,9 +581,11 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   [[maybe_unused]] const u32x4 neg4 = {neg_w, neg_w, neg_w, neg_w};
 
   // Labels are read through the scalar cache (the constant address space: the
-  // kernel never writes them), one row ahead: the load waits on the LDS
-  // counter, so neither its latency nor the previous row's gradient stores
-  // still in flight hold up the start of a row.
+  // kernel never writes them), one row ahead. A scalar load is counted with
+  // the LDS operations, not with the vector memory ones, so neither its
+  // latency nor the previous row's gradient stores still in flight hold up
+  // the start of a row. (Segment bounds come from an earlier launch; each
+  // dispatch starts with the scalar cache invalidated.)
   const kconst_i64* labels = (const kconst_i64*)p.targets;
   const kconst_i32* seg_ids = (const kconst_i32*)p.seg_ids;
   const kconst_i32* seg_start = (const kconst_i32*)p.seg_start;
