@@ -476,7 +476,8 @@ def main():
         if wl.num_segments:
             nbytes += wl.T * (4 + 8) + wl.num_segments * 4
         achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
-        traffic = None
+        # counters were taken on the default (entropy) forward kernel
+        traffic = None if args.no_entropy else traffic_from_profiles(wl.name, "traffic_forward")
         metric = METRIC_FORWARD_LSE if args.no_entropy else METRIC_FORWARD
     out = {
         "metric": metric,
