@@ -1290,9 +1290,18 @@ __global__ __launch_bounds__(256) void ce_fill_u32_kernel(uint32_t* __restrict__
 // Pair mode for long rows: the long-row shape on half rows, two workgroups
 // of one XCD per row. The launch is cooperative (every workgroup resident, so
 // a partner always arrives) on a grid of whole XCD pairs; when the runtime
-// refuses it, the whole-row kernel runs instead.
+// refuses it, or the stream is being captured into a graph (whose replay
+// need not keep the co-residency a cooperative launch guarantees), the
+// whole-row kernel runs instead.
 template <typename TI, typename TO>
 ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    cap = hipStreamCaptureStatusActive;
+  }
+  if (cap != hipStreamCaptureStatusNone)
+    return launch_rows<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1>(rp, stream, 64);
   auto kern = ce_rows_kernel<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1, kPair>;
   static std::atomic<int> occ{0};
   int per_cu = occ.load(std::memory_order_relaxed);

@@ -102,3 +102,43 @@ def test_forward_and_distill_calls_replay():
     with torch.cuda.graph(g):
         call()
     _replay_matches(g, (loss, lse, ent, dl, kl, grad), ref, "forward + distill")
+
+
+def test_long_fp32_rows_replay():
+    """fp32 rows past 16384 chunks run two workgroups per row through a
+    cooperative launch when called eagerly; under capture the whole-row kernel
+    is recorded instead. Its replays agree with each other bit for bit and with
+    the eager call to the parity tolerances (fp32 losses rel 1e-5, fp32
+    gradients abs 1e-6): the two kernels sum a row's terms in different
+    orders."""
+    import loss_vocab_amd as L
+    gen = torch.Generator(device=DEV).manual_seed(7)
+    T, V = 96, 70003
+    z = torch.randn(T, V, generator=gen, device=DEV) * 2
+    t = torch.randint(0, V, (T,), generator=gen, device=DEV)
+    t[::7] = -100
+    loss = torch.empty(T, device=DEV)
+    grad = torch.empty(T, V, device=DEV)
+    ws = torch.empty(max(1, L.workspace_bytes(z)), dtype=torch.uint8, device=DEV)
+
+    def call():
+        L.ce_fused_fwd_bwd(z, t, None, None, 1e-4, 1.0 / T, loss, None, grad, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = (loss.clone(), grad.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    g.replay()
+    torch.cuda.synchronize()
+    first = (loss.clone(), grad.clone())
+    assert torch.all((first[0] - eager[0]).abs() <= 1e-5 * eager[0].abs()), "loss vs eager"
+    assert torch.all((first[1] - eager[1]).abs() <= 1e-6), "grad vs eager"
+    _replay_matches(g, (loss, grad), first, "long fp32 rows")
