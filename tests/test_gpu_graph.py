@@ -142,3 +142,70 @@ def test_long_fp32_rows_replay():
     assert torch.all((first[0] - eager[0]).abs() <= 1e-5 * eager[0].abs()), "loss vs eager"
     assert torch.all((first[1] - eager[1]).abs() <= 1e-6), "grad vs eager"
     _replay_matches(g, (loss, grad), first, "long fp32 rows")
+
+
+def _capture(call):
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()                                          # warm the launch paths off-capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    return g
+
+
+def test_split_calls_replay():
+    """Per-shard statistics, the finish and per-shard gradients in one graph."""
+    import loss_vocab_amd as L
+    gen = torch.Generator(device=DEV).manual_seed(8)
+    T, V = 200, 20011
+    z = (torch.randn(T, V, generator=gen, device=DEV) * 2).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=gen, device=DEV)
+    t[::6] = -100
+    bounds = L.shard_bounds(V, 2, 8)
+    stats = torch.empty(len(bounds), T, 3, device=DEV)
+    row_state = torch.empty(T, L._lib.ROW_STATE, device=DEV)
+    loss = torch.empty(T, device=DEV)
+    grad = torch.empty(T, V, device=DEV, dtype=torch.bfloat16)
+
+    def call():
+        for k, (a, b) in enumerate(bounds):
+            L.ce_shard_stats(z[:, a:b], t, None, stats[k], v0=a)
+        L.ce_rows_finish(len(bounds), stats, t, None, None, 1e-4, loss, None, row_state, vocab=V)
+        for a, b in bounds:
+            L.ce_shard_grad(z[:, a:b], t, row_state, 1.0 / T, grad[:, a:b], v0=a)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (loss.clone(), row_state.clone(), grad.clone())
+    g = _capture(call)
+    _replay_matches(g, (loss, row_state, grad), ref, "split")
+
+
+def test_lmhead_call_replays():
+    """The LM-head loss (statistics, finish, chunked backward with dX and dW)
+    with a caller-owned workspace."""
+    import loss_vocab_amd as L
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    T, V, H = 256, 1000, 128
+    X = (torch.randn(T, H, generator=gen, device=DEV)).to(torch.bfloat16)
+    W = (torch.randn(V, H, generator=gen, device=DEV) * 0.1).to(torch.bfloat16)
+    t = torch.randint(0, V, (T,), generator=gen, device=DEV)
+    t[::5] = -100
+    loss, lse = torch.empty(T, device=DEV), torch.empty(T, device=DEV)
+    dh = torch.empty(T, H, device=DEV)
+    dw = torch.empty(V, H, device=DEV)
+    p = L.make_lmhead(X, W, dhidden_dtype=torch.float32)
+    ws = torch.empty(max(1, L._lib.lmhead_workspace_bytes(p, True)), dtype=torch.uint8, device=DEV)
+
+    def call():
+        L.ce_lmhead_fwd_bwd(X, W, t, None, 1e-4, 1.0 / T, loss, lse, dh, dw, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (loss.clone(), lse.clone(), dh.clone(), dw.clone())
+    g = _capture(call)
+    _replay_matches(g, (loss, lse, dh, dw), ref, "lmhead")
