@@ -127,7 +127,9 @@ size_t ce_workspace_bytes(const ce_problem* p);
  *                Ignored rows are written as +0.0. May equal logits (in
  *                place); any other overlap with logits is CE_ERR_ALIAS.
  *  workspace     device buffer of at least ce_workspace_bytes(p) bytes (may be
- *                NULL when that is 0). Contents on entry do not matter.
+ *                NULL when that is 0). Contents on entry do not matter. The
+ *                call uses it until it completes on the stream: calls that may
+ *                run concurrently need workspaces of their own.
  *  stream        hipStream_t to enqueue on.
  */
 ce_status ce_fused_fwd_bwd(const ce_problem* p,
