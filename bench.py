@@ -24,7 +24,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-DEFAULT_WORKLOAD = "cez_bf16_T8192_V32000_collapse"
+# The headline: the largest workload (CE + z-loss + segment sums, 65536 x
+# 201088 bf16). Beside it, the shape the pages measure (16384 x 128256 bf16,
+# in place; torchtitan PR #5661, revised PR description, the H100 table).
+DEFAULT_WORKLOAD = "cezseg_bf16_T65536_V201088_seg512"
+EXTRA_WORKLOAD = "ce_bf16_T16384_V128256_zipf_inplace"
 HBM_PEAK_GBPS = 8000.0
 METRIC = "fused CE fwd+bwd logit elems/sec + achieved HBM GB/s (% of peak)"
 METRIC_FORWARD = "CE forward + logsumexp + entropy logit elems/sec + achieved HBM GB/s (% of peak)"
@@ -251,7 +255,11 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input/output buffer sets used in turn (0: 3 below 2 GiB of logits, else 2)")
+    ap.add_argument("--extra-workload", default=EXTRA_WORKLOAD,
+                    help="fused path: a second workload timed after the headline one and "
+                         "reported under 'extra' ('none' to skip)")
     ap.add_argument("--cpu-rows", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -289,25 +297,129 @@ def main():
     # CPU reference first, before the GPU is touched.
     cpu = None
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        avail = len(os.sched_getaffinity(0))
+        threads = max(1, min(16, avail))
         rows = args.cpu_rows or min(wl.T, max(256, int(3e8 // wl.V) // 256 * 256))
         cpu = cpu_baseline(wl, rows, threads, forward=args.path == "forward",
                            min_seconds=args.cpu_seconds,
                            kl_beta=args.kl_beta if args.path == "distill" else None)
+        cpu["cores_available"] = avail
+        cpu["cores_online"] = os.cpu_count()
 
     import torch
 
     import loss_vocab_amd as L
-    from workloads import make_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
 
+    res = bench_workload(wl, args, dev, stream, main=True)
+
+    extra = None
+    if args.path == "fused" and args.extra_workload not in ("", "none") and \
+            args.extra_workload != wl.name:
+        # the pages' measured shape beside the headline, same timing rules
+        ew = WORKLOADS[args.extra_workload]
+        e = bench_workload(ew, args, dev, stream, main=False)
+        extra = {"workload": ew.name, "T": ew.T, "V": ew.V, "value": e["value"],
+                 "unit": "logit elems/s", "ms_per_step": e["ms_per_step"],
+                 "alg_bytes_per_step": e["nbytes"], "alg_GBps": e["achieved"],
+                 "frac": e["achieved"] / HBM_PEAK_GBPS, "timing": e["timing"],
+                 "traffic": e["traffic"]}
+
+    # A plain device-to-device copy of known size, after the timed regions:
+    # the same box's practical read+write ceiling, and the calibration kernel
+    # for the HBM byte counters.
+    copy_probe = None
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        reps = 5
+        c0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cms = c0.elapsed_time(c1) / reps
+        copy_probe = {"bytes_read": n, "bytes_written": n, "ms": cms, "GBps": 2 * n / (cms * 1e-3) / 1e9}
+        del src, dst
+
+    metric = {"fused": METRIC, "split": METRIC, "distill": METRIC_DISTILL,
+              "forward": METRIC_FORWARD_LSE if args.no_entropy else METRIC_FORWARD}[args.path]
+    nbytes, achieved = res["nbytes"], res["achieved"]
+    out = {
+        "metric": metric,
+        "value": res["value"],
+        "unit": "logit elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "T": wl.T, "V": wl.V, "logits_dtype": wl.dtype,
+            "grad_dtype": "bf16" if wl.grad_torch_dtype == torch.bfloat16 else "f32",
+            "in_place": wl.grad == "inplace", "z_alpha": wl.z_alpha,
+            "ignored_rows": wl.n_masked,
+            "segments": 0 if args.path == "distill" else wl.num_segments,
+            "rotating_buffer_sets": res["rotate"], "alg_bytes_per_step": nbytes,
+            "path": args.path, "timing": res["timing"],
+            **({"entropy": not args.no_entropy} if args.path == "forward" else {}),
+            **({"kl_beta": args.kl_beta, "teacher": "second draw of the recipe, seed offset 100"}
+               if args.path == "distill" else {}),
+        },
+        "alg_GBps": nbytes / (res["ms_per_step"] * 1e-3) / 1e9,
+        "pct_of_hbm_peak": 100.0 * nbytes / (res["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": res["traffic"],
+            "kernel_ms_avg": res["avg_call_ms"],
+            "single_call_ms_median_with_events": res["single_call_ms_median"],
+        },
+        "cpu_baseline": cpu,
+        "copy_probe": copy_probe,
+        "split": res["split"],
+        "extra": extra,
+        "wall_s_timed": res["wall"],
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_workload(wl, args, dev, stream, main=True):
+    """Inputs resident in HBM, W warmup steps, K timed steps of the chosen
+    path on ``wl``. Returns the timing and the algorithmic bytes per step.
+
+    Timing: K steps back to back between two events on the launch stream,
+    bracketed by synchronisation, nothing else enqueued between the calls (an
+    event around every call costs ~9 us per call on MI355X: the next kernel
+    waits for the marker). A workload whose gradient overwrites its logits
+    (in place) instead restores each step's logits from a pristine copy
+    before the step, outside two events around the step, so that every step
+    computes on the recipe's logits; its figure is the mean of the per-step
+    event times. One call per step, so the figure is the average launch
+    duration of the fused call."""
+    import torch
+
+    import loss_vocab_amd as L
+    from workloads import alg_bytes, make_inputs
+
+    in_place = wl.grad == "inplace" and args.path != "forward"
+    logit_bytes = wl.T * wl.V * (4 if wl.dtype == "f32" else 2)
+    rotate = args.rotate or (3 if logit_bytes < (2 << 30) else 2)
     sets = []
-    for i in range(args.rotate):
+    for i in range(rotate):
         inp = make_inputs(wl, device=dev, seed_offset=i)
-        in_place = wl.grad == "inplace"
         loss = torch.empty(wl.T, dtype=torch.float32, device=dev)
         if args.path == "forward":
             grad = None
@@ -319,17 +431,17 @@ def main():
                if wl.num_segments else None)
         ws_n = L.workspace_bytes(inp["logits"], num_segments=wl.num_segments)
         ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-        sets.append((inp, loss, grad, seg, ws))
+        pristine = inp["logits"].clone() if in_place else None
+        sets.append((inp, loss, grad, seg, ws, pristine))
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream(dev)
     bounds = L.shard_bounds(wl.V, args.shards, 8 if wl.dtype == "bf16" else 4)
     split_bufs = []
     if args.path == "split":
-        for inp, *_ in sets:
+        for _ in sets:
             split_bufs.append((torch.empty((len(bounds), wl.T, 3), dtype=torch.float32, device=dev),
                                torch.empty((wl.T, 8), dtype=torch.float32, device=dev)))
-    phase_ev = []   # split path: (stats, finish, grad) event triples per step
+    phase_ev = []   # split path: (stats, finish, grad) event quadruples per step
     teachers = []
     if args.path == "distill":
         for i in range(len(sets)):
@@ -342,8 +454,12 @@ def main():
             fwd_bufs.append((torch.empty(wl.T, dtype=torch.float32, device=dev),
                              torch.empty(wl.T, dtype=torch.float32, device=dev)))
 
+    def restore(i):
+        inp, *_, pristine = sets[i % len(sets)]
+        inp["logits"].copy_(pristine)
+
     def step(i):
-        inp, loss, grad, seg, ws = sets[i % len(sets)]
+        inp, loss, grad, seg, ws, _ = sets[i % len(sets)]
         if args.path == "fused":
             L.ce_fused_fwd_bwd(inp["logits"], inp["targets"], None, inp["segment_ids"],
                                inp["z_alpha"], inp["grad_scale"], loss, seg, grad,
@@ -381,62 +497,53 @@ def main():
         phase_ev.append(ev)
 
     for i in range(args.warmup):
+        if in_place:
+            restore(i)
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K steps back to back between two events on the launch
-    # stream, bracketed by synchronisation. Nothing else is enqueued between
-    # the calls: an event recorded around every call costs ~9 us per call on
-    # MI355X (the next kernel waits for the marker), 5% of a 170 us call. One
-    # call per step, so the region average is the average launch duration.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+    if in_place:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for i in range(args.steps):
+            restore(i)
+            ev[i][0].record(stream)
+            step(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        per_step = [a.elapsed_time(b) for a, b in ev]
+        ms_per_step = sum(per_step) / len(per_step)
+        timing = ("per-step events; logits restored from a pristine copy before each step, "
+                  "outside the events")
+        per_call_ms = sorted(per_step)
+    else:
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for i in range(args.steps):
+            step(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        ms_per_step = t_start.elapsed_time(t_end) / args.steps
+        timing = "two events around the K back-to-back steps"
+        # The spread of single calls, after the timed region: events around
+        # each of up to 20 calls (these include the event overhead).
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(20, args.steps))]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            step(args.steps + i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_call_ms = sorted(a.elapsed_time(b) for a, b in ev)
     avg_call_ms = ms_per_step
 
-    # The spread of single calls, after the timed region: events around each
-    # of up to 20 calls (these include the event overhead).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(min(20, args.steps))]
-    for i, (a, b) in enumerate(ev):
-        a.record(stream)
-        step(args.steps + i)
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_call_ms = sorted(a.elapsed_time(b) for a, b in ev)
-
-    # A plain device-to-device copy of known size, after the timed region:
-    # the same box's practical read+write ceiling, and the calibration kernel
-    # for the HBM byte counters.
-    copy_probe = None
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        reps = 5
-        c0.record(stream)
-        for _ in range(reps):
-            dst.copy_(src)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        cms = c0.elapsed_time(c1) / reps
-        copy_probe = {"bytes_read": n, "bytes_written": n, "ms": cms, "GBps": 2 * n / (cms * 1e-3) / 1e9}
-        del src, dst
-
-    elems = wl.T * wl.V
     nbytes = alg_bytes(wl)
     achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
     traffic = traffic_from_profiles(wl.name)
@@ -458,7 +565,6 @@ def main():
         achieved = grad_bytes / (ms[2] * 1e-3) / 1e9
         avg_call_ms = ms[2]
         traffic = None
-    metric = METRIC
     if args.path == "distill":
         # Valid rows of both matrices read once; every gradient row written;
         # targets read, loss and KL written.
@@ -467,7 +573,6 @@ def main():
         nbytes = wl.n_valid * wl.V * 2 * b_in + wl.T * wl.V * b_out + wl.T * (8 + 2 * 4)
         achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
         traffic = traffic_from_profiles(wl.name, "traffic_distill", "distill_ce.hip")
-        metric = METRIC_DISTILL
     if args.path == "forward":
         # Valid rows read once; targets read, loss / lse / entropy written
         # (the segment terms of the fused call stay the same).
@@ -478,46 +583,14 @@ def main():
         achieved = nbytes / (avg_call_ms * 1e-3) / 1e9
         # counters were taken on the default (entropy) forward kernel
         traffic = None if args.no_entropy else traffic_from_profiles(wl.name, "traffic_forward")
-        metric = METRIC_FORWARD_LSE if args.no_entropy else METRIC_FORWARD
-    out = {
-        "metric": metric,
-        "value": elems / (ms_per_step * 1e-3),
-        "unit": "logit elems/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": wl.name, "T": wl.T, "V": wl.V, "logits_dtype": wl.dtype,
-            "grad_dtype": "bf16" if wl.grad_torch_dtype == torch.bfloat16 else "f32",
-            "in_place": wl.grad == "inplace", "z_alpha": wl.z_alpha,
-            "ignored_rows": wl.n_masked,
-            "segments": 0 if args.path == "distill" else wl.num_segments,
-            "rotating_buffer_sets": args.rotate, "alg_bytes_per_step": nbytes,
-            "path": args.path,
-            **({"entropy": not args.no_entropy} if args.path == "forward" else {}),
-            **({"kl_beta": args.kl_beta, "teacher": "second draw of the recipe, seed offset 100"}
-               if args.path == "distill" else {}),
-        },
-        "alg_GBps": nbytes / (ms_per_step * 1e-3) / 1e9,
-        "pct_of_hbm_peak": 100.0 * nbytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel_ms_avg": avg_call_ms,
-            "single_call_ms_median_with_events": per_call_ms[len(per_call_ms) // 2],
-        },
-        "cpu_baseline": cpu,
-        "copy_probe": copy_probe,
-        "split": split_info,
-        "wall_s_timed": wall,
-    }
-    print(json.dumps(out), flush=True)
+    out = {"value": wl.T * wl.V / (ms_per_step * 1e-3), "ms_per_step": ms_per_step,
+           "avg_call_ms": avg_call_ms, "nbytes": nbytes, "achieved": achieved,
+           "traffic": traffic, "split": split_info, "wall": wall, "timing": timing,
+           "rotate": rotate, "single_call_ms_median": per_call_ms[len(per_call_ms) // 2]}
+    del sets, split_bufs, teachers, fwd_bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -95,8 +95,11 @@ typedef struct ce_problem {
 /* Device workspace (bytes) a call with this problem needs: room for a [T]
  * float NLL staging array and [S+1] segment offsets when S > 0; for fp32
  * logits of more than 65536 columns, 32 bytes per row for the two-workgroup
- * row mode (its per-row flags and partial statistics); plus 4096 bytes under
- * CE_FLAG_VALIDATE; zero otherwise. Returns 0 for a null or invalid problem. */
+ * row mode of the gradient pass (its per-row exchange slots); plus 4096
+ * bytes under CE_FLAG_VALIDATE; zero otherwise. This is what a call that
+ * writes a gradient needs; a forward-only call (grad_out NULL, or
+ * ce_fused_forward) needs no exchange slots, so it accepts a workspace
+ * smaller by those bytes. Returns 0 for a null or invalid problem. */
 size_t ce_workspace_bytes(const ce_problem* p);
 
 /*
@@ -126,6 +129,13 @@ size_t ce_workspace_bytes(const ce_problem* p);
  *  grad_out      [T, ld_grad] of grad_dtype, or NULL for a forward-only call.
  *                Ignored rows are written as +0.0. May equal logits (in
  *                place); any other overlap with logits is CE_ERR_ALIAS.
+ *  lse_out       [T] float or NULL: the full logsumexp lse_r of each valid
+ *                row (the per-row statistic a separate backward would save:
+ *                torchtitan PR #5661, revised PR description, Memory/perf),
+ *                +0.0 for ignored rows, NaN for a valid row whose target is
+ *                outside [0, V). Written by the same pass as loss_out (no
+ *                extra read of the logits). May not overlap the logits
+ *                (CE_ERR_ALIAS).
  *  workspace     device buffer of at least ce_workspace_bytes(p) bytes (may be
  *                NULL when that is 0). Contents on entry do not matter. The
  *                call uses it until it completes on the stream: calls that may
@@ -142,6 +152,7 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p,
                            float* loss_out,
                            float* seg_loss_out,
                            void* grad_out,
+                           float* lse_out,
                            void* workspace,
                            size_t workspace_bytes,
                            void* stream);

@@ -67,8 +67,19 @@ def workspace_bytes(logits, *, num_segments=0, validate=False):
     return _lib.workspace_bytes(make_problem(logits, num_segments=num_segments, validate=validate))
 
 
+def _workspace(need, device, stream):
+    """A uint8 workspace of ``need`` bytes for a call enqueued on ``stream``
+    (a hipStream_t as an integer). torch's caching allocator ties a block to
+    the current stream; when the call goes to another stream the block is
+    recorded on it, so it is not handed out again before the call has run."""
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if int(stream) != int(torch.cuda.current_stream(device).cuda_stream):
+        ws.record_stream(torch.cuda.ExternalStream(int(stream), device=device))
+    return ws
+
+
 def ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale,
-                     loss_out, seg_loss_out, grad_out, *, num_segments=0,
+                     loss_out, seg_loss_out, grad_out, *, lse_out=None, num_segments=0,
                      segment_mean=False, ignore_index=IGNORE_INDEX, workspace=None,
                      stream=None, validate=False):
     """Same-named wrapper of the C entry point on torch tensors.
@@ -76,42 +87,45 @@ def ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale,
     logits [T, V] f32/bf16 (row stride free, unit column stride); targets [T]
     int64; mask [T] uint8 or None; segment_ids [T] int32 or None; loss_out [T]
     f32; seg_loss_out [S] f32 or None; grad_out [T, V] f32/bf16, ``logits``
-    itself (in place) or None (forward only); workspace: a uint8 device tensor
-    of at least ``workspace_bytes`` bytes when segments are used (allocated
-    here when None). The call is asynchronous on ``stream`` (default: torch's
-    current stream). ``validate`` sets CE_FLAG_VALIDATE: a device scan of the
-    targets and segment ids, after which the call waits for the stream and
-    raises CeError(CE_ERR_INVALID_ARG) before writing anything if one is out of
-    range or the ids are unsorted. Raises CeError on a non-OK status.
+    itself (in place) or None (forward only); lse_out [T] f32 or None (each
+    row's full logsumexp); workspace: a uint8 device tensor of at least
+    ``workspace_bytes`` bytes when segments are used (allocated here when
+    None). The call is asynchronous on ``stream`` (default: torch's current
+    stream). ``validate`` sets CE_FLAG_VALIDATE: a device scan of the targets
+    and segment ids, after which the call waits for the stream and raises
+    CeError(CE_ERR_INVALID_ARG) before writing anything if one is out of range
+    or the ids are unsorted. Raises CeError on a non-OK status.
     """
     p = make_problem(logits, grad_out, num_segments=num_segments,
                      segment_mean=segment_mean, ignore_index=ignore_index, validate=validate)
     for name, t, dt in (("targets", targets, torch.int64), ("mask", mask, torch.uint8),
                         ("segment_ids", segment_ids, torch.int32),
                         ("loss_out", loss_out, torch.float32),
-                        ("seg_loss_out", seg_loss_out, torch.float32)):
+                        ("seg_loss_out", seg_loss_out, torch.float32),
+                        ("lse_out", lse_out, torch.float32)):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous {dt} tensor")
+    stream = _stream(logits, stream)
     need = _lib.workspace_bytes(p)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        workspace = _workspace(need, logits.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    if stream is None:
-        stream = torch.cuda.current_stream(logits.device).cuda_stream
     st = _lib.call_raw(p, _ptr(logits), _ptr(targets), _ptr(mask), _ptr(segment_ids),
                        z_alpha, grad_scale, _ptr(loss_out), _ptr(seg_loss_out),
-                       _ptr(grad_out), _ptr(workspace), ws_bytes, int(stream or 0))
+                       _ptr(grad_out), _ptr(lse_out), _ptr(workspace), ws_bytes, stream)
     if st != CE_OK:
         raise CeError(st)
 
 
 def ce_fused(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
              z_alpha=0.0, grad_scale=1.0, segment_mean=False, grad_dtype=None,
-             in_place=False, want_grad=True, ignore_index=IGNORE_INDEX, validate=False):
+             in_place=False, want_grad=True, ignore_index=IGNORE_INDEX, validate=False,
+             lse_out=None):
     """Allocate the outputs and run one fused call.
 
     Returns ``(loss[T] f32, grad[T, V] or None, seg_loss[S] f32 or None)``.
-    With ``in_place`` the gradient overwrites ``logits`` and is returned.
+    With ``in_place`` the gradient overwrites ``logits`` and is returned;
+    ``lse_out`` ([T] f32, optional) receives each row's full logsumexp.
     """
     T, V = logits.shape
     dev = logits.device
@@ -124,7 +138,7 @@ def ce_fused(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
     else:
         grad = torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
     ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale, loss, seg, grad,
-                     num_segments=num_segments, segment_mean=segment_mean,
+                     lse_out=lse_out, num_segments=num_segments, segment_mean=segment_mean,
                      ignore_index=ignore_index, validate=validate)
     return loss, grad, seg
 
@@ -145,13 +159,14 @@ def ce_fused_forward(logits, targets, mask, segment_ids, z_alpha, loss_out, seg_
                         ("entropy_out", entropy_out, torch.float32)):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous {dt} tensor")
+    stream = _stream(logits, stream)
     need = _lib.workspace_bytes(p)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=logits.device)
+        workspace = _workspace(need, logits.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.forward_raw(p, _ptr(logits), _ptr(targets), _ptr(mask), _ptr(segment_ids), z_alpha,
                           _ptr(loss_out), _ptr(seg_loss_out), _ptr(lse_out), _ptr(entropy_out),
-                          _ptr(workspace), ws_bytes, _stream(logits, stream))
+                          _ptr(workspace), ws_bytes, stream)
     if st != CE_OK:
         raise CeError(st, "ce_fused_forward")
 
@@ -222,14 +237,14 @@ def ce_rows_finish(num_shards, stats, targets, mask, segment_ids, z_alpha, loss_
     p.ignore_index = int(ignore_index)
     p.num_segments = int(num_segments)
     p.flags = CE_FLAG_SEGMENT_MEAN if segment_mean else 0
+    stream = _stream(targets, stream)
     need = _lib.workspace_bytes(p)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=targets.device)
+        workspace = _workspace(need, targets.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _lib.rows_finish_raw(p, num_shards, _ptr(stats), _ptr(targets), _ptr(mask),
                               _ptr(segment_ids), z_alpha, _ptr(loss_out), _ptr(seg_loss_out),
-                              _ptr(row_state), _ptr(workspace), ws_bytes,
-                              _stream(targets, stream))
+                              _ptr(row_state), _ptr(workspace), ws_bytes, stream)
     if st != CE_OK:
         raise CeError(st, "ce_rows_finish")
 
@@ -318,16 +333,17 @@ def ce_lmhead_fwd_bwd(hidden, weight, targets, mask, z_alpha, grad_scale, loss_o
     p = make_lmhead(hidden, weight, dhidden_dtype=dhidden.dtype if dhidden is not None
                     else torch.float32, chunk_cols=chunk_cols, ignore_index=ignore_index)
     backward = dhidden is not None or dweight is not None
+    stream = _stream(hidden, stream)
     need = _lib.lmhead_workspace_bytes(p, backward)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=hidden.device)
+        workspace = _workspace(max(need, 1), hidden.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     for name, t in (("dhidden", dhidden), ("dweight", dweight)):
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     st = _lib.lmhead_raw(p, _ptr(hidden), _ptr(weight), _ptr(targets), _ptr(mask), z_alpha,
                          grad_scale, _ptr(loss_out), _ptr(lse_out), _ptr(dhidden), _ptr(dweight),
-                         _ptr(workspace), ws_bytes, _stream(hidden, stream))
+                         _ptr(workspace), ws_bytes, stream)
     if st != CE_OK:
         raise CeError(st, "ce_lmhead_fwd_bwd")
 

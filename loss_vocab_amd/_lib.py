@@ -90,7 +90,7 @@ def _load(path=LIB_PATH):
     lib.ce_workspace_bytes.restype = ctypes.c_size_t
     lib.ce_fused_fwd_bwd.argtypes = [
         ctypes.POINTER(CeProblem), vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
-        vp, vp, vp, vp, ctypes.c_size_t, vp,
+        vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
     ]
     lib.ce_fused_fwd_bwd.restype = ctypes.c_int
     lib.ce_fused_forward.argtypes = [
@@ -136,12 +136,12 @@ def workspace_bytes(problem):
 
 
 def call_raw(problem, logits, targets, mask, segment_ids, z_alpha, grad_scale,
-             loss_out, seg_loss_out, grad_out, workspace, workspace_bytes_, stream):
+             loss_out, seg_loss_out, grad_out, lse_out, workspace, workspace_bytes_, stream):
     """Call ce_fused_fwd_bwd with integer addresses (0 = NULL); returns the status."""
     return int(LIB.ce_fused_fwd_bwd(
         ctypes.byref(problem), logits or None, targets or None, mask or None,
         segment_ids or None, float(z_alpha), float(grad_scale), loss_out or None,
-        seg_loss_out or None, grad_out or None, workspace or None,
+        seg_loss_out or None, grad_out or None, lse_out or None, workspace or None,
         int(workspace_bytes_), stream or None))
 
 

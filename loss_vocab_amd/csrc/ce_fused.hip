@@ -224,8 +224,10 @@ enum RowMode : int {
 };
 
 // Saved per-row state: kRowState floats per row,
-//   [0] lse log2(e)   [1] p_nt = sigmoid(LSE_nt - z_t)   [2] p_t = sigmoid(z_t - LSE_nt)
-//   [3] 2 alpha lse   [4] segment factor (1 / length, or 1)   [5] kind   [6..7] zero
+//   [0] lse log2(e) rounded to float   [1] p_nt = sigmoid(LSE_nt - z_t)
+//   [2] p_t = sigmoid(z_t - LSE_nt)    [3] 2 alpha lse
+//   [4] segment factor (1 / length, or 1)   [5] kind
+//   [6] lse log2(e) - [0] (the rounding residue of [0])   [7] zero
 constexpr int kRowState = 8;
 // Pair mode: polls of a partner's flag (each after s_sleep 2, ~128 cycles)
 // before the wait is given up (~0.1 s).
@@ -253,7 +255,8 @@ __device__ __forceinline__ RowOut saved_row(const RowParams& p, const float* rs,
   const float w = p.row_weight ? p.row_weight[r] : zw;
   RowOut o{};
   o.kl = rs[0];
-  o.cnt = w + zw * rs[3];
+  // rs[6] is the rounding residue of rs[0]: folded into the row factor
+  o.cnt = (w + zw * rs[3]) * fexp2(-rs[6]);
   o.g_t = -w * rs[1] + zw * rs[3] * rs[2];
   return o;
 }
@@ -316,9 +319,14 @@ __device__ __forceinline__ RowOut row_epilogue(const RowParams& p, int64_t r, fl
   RowOut o;
   o.cnt_d = scale * (1.0 + zfac);
   o.g_t = static_cast<float>(scale * (-p_nt + zfac * p_t));
-  o.cnt = static_cast<float>(o.cnt_d);
   o.lse_l2 = l2e * lse;
   o.kl = static_cast<float>(o.lse_l2);
+  // kl holds lse log2(e) to half a float ulp (up to ~4e-6 at |lse| ~ 40);
+  // the residue is folded into the per-row factor, so an element's exponent
+  // z log2(e) - kl is exact up to its own rounding: 2^(z log2 e - lse log2 e)
+  // = 2^(-residue) 2^(z log2 e - kl).
+  const double res = isfinite(o.lse_l2) ? o.lse_l2 - static_cast<double>(o.kl) : 0.0;
+  o.cnt = static_cast<float>(o.cnt_d * exp2(-res));
   return o;
 }
 
@@ -1215,13 +1223,14 @@ __global__ __launch_bounds__(256) void ce_finish_kernel(FinishParams f) {
   const double seg = f.seg_mean ? segment_factor(f.seg_ids, f.seg_start, f.num_segments, r) : 1.0;
   f.loss_out[r] = static_cast<float>(L.nll + ((alpha == 0.0) ? 0.0 : alpha * L.lse * L.lse));
   if (f.nll_ws) f.nll_ws[r] = static_cast<float>(L.nll);
-  rs[0] = static_cast<float>(static_cast<double>(kL2E) * L.lse);
+  const double lse_l2 = static_cast<double>(kL2E) * L.lse;
+  rs[0] = static_cast<float>(lse_l2);
   rs[1] = static_cast<float>(L.p_nt);
   rs[2] = static_cast<float>(L.p_t);
   rs[3] = static_cast<float>(zfac);
   rs[4] = static_cast<float>(seg);
   rs[5] = kRowValid;
-  rs[6] = 0.f;
+  rs[6] = isfinite(lse_l2) ? static_cast<float>(lse_l2 - static_cast<double>(rs[0])) : 0.f;
   rs[7] = 0.f;
 }
 
@@ -1494,12 +1503,16 @@ size_t segment_ws_bytes(const ce_problem* p) {
          align_up((static_cast<size_t>(p->num_segments) + 1) * sizeof(int32_t));
 }
 
-// fp32 rows of more than 16384 16-byte chunks run in pair mode, which needs
-// 32 bytes of exchange slots per row (placed after the segment arrays).
+// fp32 rows of more than 16384 16-byte chunks run the gradient pass in pair
+// mode, which needs 32 bytes of exchange slots per row (placed after the
+// segment arrays). A forward-only call runs no pair mode and needs none.
 bool pair_rows(const ce_problem* p) { return p->logits_dtype == CE_DTYPE_F32 && p->V / 4 > 16384; }
-size_t pair_ws_bytes(const ce_problem* p) {
-  if (!pair_rows(p)) return 0;
+size_t pair_ws_bytes(const ce_problem* p, bool grad = true) {
+  if (!grad || !pair_rows(p)) return 0;
   return align_up(static_cast<size_t>(p->T) * 8 * sizeof(uint32_t));
+}
+size_t validate_ws_bytes(const ce_problem* p) {
+  return (p->flags & CE_FLAG_VALIDATE) ? align_up(kValidateBlocks * sizeof(uint32_t)) : 0;
 }
 
 // Validation and launches shared by the fused entry points. grad_out null
@@ -1561,7 +1574,10 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
                        reinterpret_cast<uintptr_t>(o), static_cast<size_t>(T) * sizeof(float)))
       return CE_ERR_ALIAS;
   }
-  const size_t need = ce_workspace_bytes(p);
+  // Workspace: segment arrays, pair-mode slots (gradient calls only), the
+  // debug scan's words, in that order.
+  const bool grad = grad_out != nullptr;
+  const size_t need = segment_ws_bytes(p) + pair_ws_bytes(p, grad) + validate_ws_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CE_ERR_WORKSPACE;
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0) return CE_ERR_WORKSPACE;
 
@@ -1570,7 +1586,7 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
   if ((p->flags & CE_FLAG_VALIDATE) && T > 0) {
     // Scan, wait, and refuse before anything else is enqueued.
     uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p) +
-                                                  pair_ws_bytes(p));
+                                                  pair_ws_bytes(p, grad));
     const int64_t nb = std::min<int64_t>(kValidateBlocks, (T + 255) / 256);
     (void)hipGetLastError();
     hipLaunchKernelGGL(ce_validate_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, stream,
@@ -1655,8 +1671,7 @@ extern "C" {
 
 size_t ce_workspace_bytes(const ce_problem* p) {
   if (p == nullptr || p->T < 0 || p->num_segments < 0) return 0;
-  return segment_ws_bytes(p) + pair_ws_bytes(p) +
-         ((p->flags & CE_FLAG_VALIDATE) ? align_up(kValidateBlocks * sizeof(uint32_t)) : 0);
+  return segment_ws_bytes(p) + pair_ws_bytes(p) + validate_ws_bytes(p);
 }
 
 const char* ce_status_string(int status) {
@@ -1674,10 +1689,10 @@ const char* ce_status_string(int status) {
 ce_status ce_fused_fwd_bwd(const ce_problem* p, const void* logits, const int64_t* targets,
                            const uint8_t* mask, const int32_t* segment_ids, float z_alpha,
                            float grad_scale, float* loss_out, float* seg_loss_out,
-                           void* grad_out, void* workspace, size_t workspace_bytes,
-                           void* stream_ptr) {
+                           void* grad_out, float* lse_out, void* workspace,
+                           size_t workspace_bytes, void* stream_ptr) {
   return run_rows(p, logits, targets, mask, segment_ids, z_alpha, grad_scale, loss_out,
-                  seg_loss_out, grad_out, nullptr, nullptr, workspace, workspace_bytes,
+                  seg_loss_out, grad_out, lse_out, nullptr, workspace, workspace_bytes,
                   stream_ptr);
 }
 

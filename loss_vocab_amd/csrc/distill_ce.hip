@@ -244,10 +244,16 @@ __device__ __forceinline__ RowOut finish_row(const DistillParams& p, int64_t r, 
                                      beta * kl);
   if (p.kl_out) p.kl_out[r] = static_cast<float>(kl);
   RowOut o;
-  o.cs = static_cast<float>(sc * (1.0 + zl + beta));
-  o.ct = static_cast<float>(sc * beta);
-  o.ks = static_cast<float>(static_cast<double>(kL2E) * S.lse);
-  o.kt = static_cast<float>(static_cast<double>(kL2E) * Tt.lse);
+  // ks / kt hold lse log2(e) rounded to float; each residue is folded into
+  // its side's factor, so an element's exponent is exact up to its own
+  // rounding (2^(x - lse log2 e) = 2^(-residue) 2^(x - k)).
+  const double ls2 = static_cast<double>(kL2E) * S.lse, lt2 = static_cast<double>(kL2E) * Tt.lse;
+  o.ks = static_cast<float>(ls2);
+  o.kt = static_cast<float>(lt2);
+  const double rs_ = isfinite(ls2) ? ls2 - static_cast<double>(o.ks) : 0.0;
+  const double rt_ = isfinite(lt2) ? lt2 - static_cast<double>(o.kt) : 0.0;
+  o.cs = static_cast<float>(sc * (1.0 + zl + beta) * exp2(-rs_));
+  o.ct = static_cast<float>(sc * beta * exp2(-rt_));
   o.gt = static_cast<float>(sc * (-S.p_nt + zl * S.p_t + beta * (Tt.p_nt - S.p_nt)));
   return o;
 }

@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
         if (kind == 0.f) {
           const float zw = p.grad_scale * rs[4];
           kl = rs[0];
-          cnt = zw + zw * rs[3];
+          cnt = (zw + zw * rs[3]) * fexp2(-rs[6]);   // rs[6]: rounding residue of rs[0]
           gtv = -zw * rs[1] + zw * rs[3] * rs[2];
           t = p.targets[gr];
           live = true;
@@ -535,14 +535,15 @@ __global__ __launch_bounds__(256) void lm_transpose_kernel(const uint16_t* __res
   }
 }
 
-// lse from the saved state: lse = state[0] / log2(e) for valid rows, 0 for
-// ignored rows, NaN for poisoned ones.
+// lse from the saved state: lse = (state[0] + state[6]) / log2(e) for valid
+// rows, 0 for ignored rows, NaN for poisoned ones.
 __global__ __launch_bounds__(256) void lm_lse_kernel(const float* __restrict__ row_state,
                                                      int64_t T, float* __restrict__ lse) {
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (r >= T) return;
   const float* rs = row_state + kRowState * r;
-  lse[r] = rs[5] == 0.f ? static_cast<float>(static_cast<double>(rs[0]) / static_cast<double>(kL2E))
+  lse[r] = rs[5] == 0.f ? static_cast<float>((static_cast<double>(rs[0]) + static_cast<double>(rs[6])) /
+                                              static_cast<double>(kL2E))
                         : (rs[5] == 1.f ? 0.f : __builtin_nanf(""));
 }
 

@@ -106,8 +106,8 @@ A_WS = 0x60000000
 
 
 def _call(p, logits=A_LOGITS, targets=A_TGT, mask=0, seg=0, za=0.0, gs=1.0, loss=A_LOSS,
-          seg_out=0, grad=A_GRAD, ws=0, ws_bytes=0):
-    return _lib().call_raw(p, logits, targets, mask, seg, za, gs, loss, seg_out, grad, ws,
+          seg_out=0, grad=A_GRAD, lse=0, ws=0, ws_bytes=0):
+    return _lib().call_raw(p, logits, targets, mask, seg, za, gs, loss, seg_out, grad, lse, ws,
                            ws_bytes, 0)
 
 
@@ -131,6 +131,7 @@ def _call(p, logits=A_LOGITS, targets=A_TGT, mask=0, seg=0, za=0.0, gs=1.0, loss
     ("non-finite z_alpha", dict(za=float("nan")), {}, 1),
     ("non-finite grad_scale", dict(gs=float("inf")), {}, 1),
     ("grad overlaps logits (shifted)", dict(grad=A_LOGITS + 64), {}, 3),
+    ("lse_out overlaps logits", dict(lse=A_LOGITS + 32), {}, 3),
     ("in place with another dtype", dict(grad=A_LOGITS), dict(gdt=1), 3),
     ("in place with another stride", dict(grad=A_LOGITS), dict(ldg=128, ld=100), 3),
     ("workspace missing", dict(seg=A_SEG), dict(S=4), 4),
@@ -144,7 +145,7 @@ def test_validation_errors(case, kwargs, pkw, expect):
     p = None if pkw is None else _problem(**pkw)
     if p is None:
         st = _lib().LIB.ce_fused_fwd_bwd(None, None, None, None, None, 0.0, 1.0, None, None,
-                                         None, None, 0, None)
+                                         None, None, None, 0, None)
     else:
         st = _call(p, **kwargs)
     assert st == expect, (case, _lib().status_string(st))
@@ -367,3 +368,65 @@ def test_distill_in_place_allowed():
     """grad_out == logits with the same dtype and stride passes validation
     (checked with T = 0 so nothing is launched)."""
     assert _dcall(_problem(T=0), grad=A_LOGITS) == 0
+
+
+NO_DEVICE_PROBE = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+from loss_vocab_amd import _lib as L
+p = L.CeProblem()
+p.T, p.V, p.ld_logits, p.ld_grad = 8, 100, 100, 100
+p.logits_dtype = p.grad_dtype = 0
+p.ignore_index = -100
+out = {}
+out["fused"] = L.call_raw(p, 0x10000000, 0x20000000, 0, 0, 0.0, 1.0, 0x30000000, 0, 0x40000000,
+                          0x50000000, 0, 0, 0)
+out["forward"] = L.forward_raw(p, 0x10000000, 0x20000000, 0, 0, 0.0, 0x30000000, 0, 0, 0, 0, 0, 0)
+s = L.CeShard()
+s.T, s.V, s.v0, s.ld_logits, s.ld_grad = 8, 100, 0, 100, 100
+s.logits_dtype = s.grad_dtype = 0
+s.ignore_index = -100
+out["shard_stats"] = L.shard_stats_raw(s, 0x10000000, 0x20000000, 0, 0x30000000, 0)
+out["rows_finish"] = L.rows_finish_raw(p, 1, 0x10000000, 0x20000000, 0, 0, 0.0, 0x30000000, 0,
+                                       0x40000000, 0, 0, 0)
+out["shard_grad"] = L.shard_grad_raw(s, 0x10000000, 0x20000000, 0x30000000, 0, 1.0, 0x40000000, 0)
+out["distill"] = L.distill_raw(p, 0x10000000, 0x60000000, 100, 0, 0x20000000, 0, 0.0, 1.0, 1.0,
+                               0x30000000, 0, 0x40000000, 0)
+print(out)
+"""
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU is present: the probe's fake "
+                    "addresses would reach real kernels")
+def test_valid_calls_without_a_device_return_ce_err_hip(tmp_path):
+    """A call that passes every host check, made where no GPU exists, comes
+    back as CE_ERR_HIP from its first HIP call and does not crash the process
+    (a subprocess, so a crash would show as its exit status)."""
+    import ast
+    probe = tmp_path / "nodev.py"
+    probe.write_text(NO_DEVICE_PROBE)
+    res = subprocess.run(["python", str(probe), ROOT], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    got = ast.literal_eval(res.stdout.strip().splitlines()[-1])
+    assert got == {k: 5 for k in ("fused", "forward", "shard_stats", "rows_finish", "shard_grad",
+                                  "distill")}, got
+
+
+def test_forward_only_needs_no_pair_slots():
+    """fp32 rows past 65536 columns reserve pair-mode exchange slots for the
+    gradient pass only: ce_workspace_bytes counts them, a call without a
+    gradient (fused with grad_out NULL, or the forward entry) does not ask for
+    them, while a gradient call still does. T = 0 keeps every call on the
+    host (segment-free, so nothing is enqueued)."""
+    L = _lib()
+    p = _problem(T=1000, V=70000)
+    assert L.workspace_bytes(p) == 1000 * 32
+    p0 = _problem(T=0, V=70000)
+    assert _call(p0, grad=A_GRAD) == 0 and _fwd(p0) == 0
+    # rows present: without the slots a gradient call is refused, a
+    # forward-only call is not refused for the workspace (it fails later, at
+    # its first HIP call, where no device exists; it is not run where one does)
+    assert _call(p, grad=A_GRAD) == 4
+    if not os.path.exists("/dev/kfd"):
+        assert _call(p, grad=0) == 5
+        assert _fwd(p) == 5

@@ -20,6 +20,7 @@ import pytest
 import torch
 
 from oracle import distill_oracle
+from distill_checks import check_rows
 from parity_utils import bf16_ulp, to_np64
 from workloads import WORKLOADS, make_inputs
 
@@ -38,63 +39,6 @@ def _need_gpu():
 
 def _np(t):
     return None if t is None else t.detach().cpu().numpy()
-
-
-def _lse(z):
-    m = z.max(axis=1, keepdims=True)
-    m = np.where(np.isfinite(m), m, 0.0)
-    with np.errstate(divide="ignore"):
-        return (m + np.log(np.exp(z - m).sum(axis=1, keepdims=True)))[:, 0]
-
-
-def kl_bound(zs64, zt64, ref):
-    """1e-5 |KL| + 4e-6 (|lse_z| + |lse_y| + max|y - z| + NLL) per row, and
-    the two logsumexps."""
-    ls, lt = _lse(zs64), _lse(zt64)
-    with np.errstate(invalid="ignore"):
-        w = np.where(np.isfinite(zt64) & np.isfinite(zs64), np.abs(zt64 - zs64), 0.0)
-    size = np.abs(ls) + np.abs(lt) + w.max(axis=1) + np.abs(ref["ce"]["nll"])
-    return 1e-5 * np.abs(ref["kl"]) + 4e-6 * size, ls, lt
-
-
-def check_rows(zs64, zt64, t_np, got_loss, got_kl, g, ref, *, alpha, beta, gamma, gdt, what):
-    """The tolerances above, row by row, on host copies of the outputs."""
-    valid = ref["valid"]
-    V = zs64.shape[1]
-    live = valid & (t_np >= 0) & (t_np < V)
-    kb, ls, lt = kl_bound(zs64, zt64, ref)
-    with np.errstate(invalid="ignore", over="ignore"):
-        pt = np.exp(zt64 - lt[:, None])
-    got_kl, got_loss = got_kl.astype(np.float64), got_loss.astype(np.float64)
-    assert np.array_equal(np.isnan(got_kl), np.isnan(ref["kl"])), what + " kl NaN pattern"
-    assert np.array_equal(np.isnan(got_loss), np.isnan(ref["loss"])), what + " loss NaN pattern"
-    m = live
-    bad = np.abs(got_kl[m] - ref["kl"][m]) > kb[m]
-    assert not bad.any(), (what + " kl", got_kl[m][bad][:3], ref["kl"][m][bad][:3])
-    lb = 1e-5 * np.abs(ref["loss"][m]) + beta * kb[m]
-    bad = np.abs(got_loss[m] - ref["loss"][m]) > lb
-    assert not bad.any(), (what + " loss", got_loss[m][bad][:3], ref["loss"][m][bad][:3])
-    # ignored rows +0.0 bit for bit
-    for x in (got_loss, got_kl):
-        assert np.all(x[~valid].astype(np.float32).view(np.int32) == 0), what + " ignored row"
-    # gradient
-    r = ref["grad"]
-    with np.errstate(invalid="ignore", over="ignore"):
-        ps = np.exp(zs64 - ls[:, None])
-    fac = gamma * ((1 + 2 * alpha * np.abs(ls)[:, None] + beta) * ps + beta * pt)
-    fac = np.where(live[:, None], fac, 0.0)
-    if gdt == torch.float32:
-        gb = 1e-6 + 4e-6 * fac
-    else:
-        gb = 2 * bf16_ulp(r) + 4e-6 * fac + (np.abs(r) < 2.0 ** -126) * 2.0 ** -126
-    assert np.array_equal(np.isnan(g), np.isnan(r)), what + " grad NaN pattern"
-    mm = ~np.isnan(r)
-    err = np.abs(g[mm] - r[mm])
-    bad = err > gb[mm]
-    if bad.any():
-        i = np.argmax(err / gb[mm])
-        raise AssertionError(f"{what} grad: {bad.sum()} off; got {g[mm][i]!r} ref {r[mm][i]!r} "
-                             f"bound {gb[mm][i]:.3e}")
 
 
 def compare(zs, zt, t, *, mask=None, alpha=0.0, beta=1.0, gamma=1.0, grad_dtype=None,

@@ -17,8 +17,8 @@ import numpy as np
 import pytest
 import torch
 
-from parity_utils import (check_grad, check_loss, check_zero_rows, run_hip, run_oracle,
-                          to_np64)
+from parity_utils import (check_grad, check_loss, check_zero_rows, row_scales, run_hip,
+                          run_oracle, to_np64)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,9 @@ def compare_all(inp, *, grad_dtype=None, in_place=False, mask=None, want_grad=Tr
     inv = torch.as_tensor(~ref["valid"], device=DEV)
     check_zero_rows(loss[inv], grad[inv] if grad is not None else None)
     if want_grad:
-        check_grad(to_np64(grad), ref["grad"], gdt, what + " grad")
+        sc = row_scales(logits.shape[0], inp["grad_scale"], _np(inp.get("segment_ids")),
+                        inp.get("num_segments", 0), inp.get("segment_mean", False))
+        check_grad(to_np64(grad), ref["grad"], gdt, what + " grad", scale=sc)
     if seg is not None:
         check_loss(_np(seg), ref["seg_nll"], what + " seg")
         empty = ref["seg_nll"] == 0
@@ -148,7 +150,7 @@ def test_row_stride_larger_than_V(dtype, pad):
     torch.cuda.synchronize()
     ref = run_oracle(to_np64(z), _np(t), z_alpha=1e-4, grad_scale=0.5)
     check_loss(_np(loss), ref["loss"])
-    check_grad(to_np64(gout), ref["grad"], torch.float32)
+    check_grad(to_np64(gout), ref["grad"], torch.float32, scale=0.5)
     assert torch.all(gbig[:, V:] == 5.0), "padding columns of the gradient were written"
     # the padding of the logits is never part of the result
     big[:, V:] = float("nan")
@@ -467,7 +469,7 @@ def test_full_size(name):
     # the oracle ran with scale 1; apply each row's scale (exact in fp64 for
     # the power-of-two-free factors up to rounding far below the tolerance)
     g_ref = ref["grad"] * scale[:, None]
-    check_grad(to_np64(grad[ri]), g_ref, wl.grad_torch_dtype, f"{name} sampled grad")
+    check_grad(to_np64(grad[ri]), g_ref, wl.grad_torch_dtype, f"{name} sampled grad", scale=scale)
     # every ignored row is +0.0, every valid loss finite
     inv = torch.as_tensor(t_all == -100, device=DEV)
     check_zero_rows(loss[inv], grad[inv])
@@ -537,3 +539,71 @@ def test_validate_flag():
     bad_s = seg.clone()
     bad_s[400] = 0                      # decreasing once
     refused(t, bad_s)
+
+
+# ---------------------------------------------------------------------------
+# lse_out on the fused call; fp32 gradients at unit scale with a large lse
+# ---------------------------------------------------------------------------
+
+LSE_CASES = [(torch.float32, 4099), (torch.bfloat16, 3001), (torch.bfloat16, 70001),
+             (torch.bfloat16, 16385 * 8 + 5), (torch.float32, 70003)]
+
+
+@pytest.mark.parametrize("dtype,V", LSE_CASES, ids=[f"{d}-{v}".replace("torch.", "") for d, v in LSE_CASES])
+def test_lse_out_on_fused_call(dtype, V):
+    """The optional lse_out of ce_fused_fwd_bwd: each valid row's full
+    logsumexp (rel 1e-5 against the oracle), +0.0 for ignored rows and NaN for
+    an out-of-range target, from the same pass, on every row-length tier (the
+    last one is the two-workgroup fp32 mode). Loss and gradient are bit for
+    bit those of the call without it."""
+    import loss_vocab_amd as L
+    print(f"[parity] lse_out V={V} {dtype}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V + 1)
+    T = 24
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2.5)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[3] = -100
+    t[7] = V + 2
+    z[5, t[5]] = z[5].max() + 30.0
+    z = z.to(dtype)
+    lse = torch.full((T,), 9.0, device=DEV)
+    loss_a, grad_a, _ = L.ce_fused(z, t, z_alpha=1e-4, grad_scale=0.25, lse_out=lse)
+    loss_b, grad_b, _ = L.ce_fused(z, t, z_alpha=1e-4, grad_scale=0.25)
+    torch.cuda.synchronize()
+    ref = run_oracle(to_np64(z), _np(t), z_alpha=1e-4, grad_scale=0.25)
+    check_loss(_np(lse), ref["lse"], "lse_out")
+    assert float(lse[3]) == 0.0 and math.copysign(1.0, float(lse[3])) == 1.0
+    assert math.isnan(float(lse[7]))
+    assert torch.equal(loss_a.nan_to_num(7.0), loss_b.nan_to_num(7.0))
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(grad_a.view(bits), grad_b.view(bits))
+
+
+FP32_UNIT_CASES = [(torch.float32, 3001), (torch.float32, 40000), (torch.float32, 70003),
+                   (torch.bfloat16, 16385 * 8 + 5), (torch.float32, 8192 * 4 + 1)]
+
+
+@pytest.mark.parametrize("dtype,V", FP32_UNIT_CASES,
+                         ids=[f"{d}-{v}".replace("torch.", "") for d, v in FP32_UNIT_CASES])
+def test_fp32_grad_unit_scale_large_lse(dtype, V):
+    """fp32 gradients at grad_scale 1 on rows whose logits sit near +-50 (so
+    |lse| > 40, where one float carries lse log2(e) only to ~4e-6) and whose
+    largest softmax value, 0.6-0.95, belongs to a non-target column placed in
+    an on-chip slot, a streamed slot or the last chunk: every element within
+    1e-6 absolute (and 2^-16 relative) of the oracle."""
+    print(f"[parity] fp32 unit scale V={V} {dtype}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V + 7)
+    T = 12
+    z = torch.randn(T, V, generator=g, device=DEV) * 2
+    W = 4 if dtype == torch.float32 else 8
+    cols = [5, V // 2 + 3, V - 1 - (V % W) - 2, V - 1, 1100, 9 * 1024 * W + 17]
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    for r in range(T):
+        j = cols[r % len(cols)] % V
+        if int(t[r]) == j:
+            t[r] = (j + 1) % V
+        # dominant non-target: softmax value sigmoid(0.5 + 0.5 (r mod 6)) in 0.62..0.95
+        z[r, j] = float(torch.logsumexp(z[r], 0)) + 0.5 + 0.5 * (r % 6)
+        z[r] += 50.0 if r % 2 == 0 else -55.0
+    z = z.to(dtype)
+    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0), grad_dtype=torch.float32, what=f"unit V={V}")

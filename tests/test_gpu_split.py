@@ -16,7 +16,8 @@ import pytest
 import torch
 
 from oracle import shard_nontarget_lse
-from parity_utils import check_grad, check_loss, check_zero_rows, run_oracle, to_np64
+from parity_utils import (check_grad, check_loss, check_zero_rows, row_scales, run_oracle,
+                          to_np64)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -82,13 +83,19 @@ def test_split_matches_oracle(dtype, T, V, shards, align, alpha, S):
     ref = run_oracle(z64, _np(t), segment_ids=_np(seg), num_segments=S, z_alpha=alpha,
                      grad_scale=gamma, segment_mean=S > 0)
     check_loss(_np(loss), ref["loss"], "split loss")
-    check_grad(to_np64(grad), ref["grad"], dtype, "split grad")
+    check_grad(to_np64(grad), ref["grad"], dtype, "split grad",
+               scale=row_scales(T, gamma, _np(seg), S, S > 0), targets=_np(t))
     inv = torch.as_tensor(~ref["valid"], device=DEV)
     check_zero_rows(loss[inv], grad[inv])
     if S:
         check_loss(_np(segsum), ref["seg_nll"], "split seg")
     rs = _np(row_state)
     assert np.all(rs[~ref["valid"], 5] == 1.0) and np.all(rs[ref["valid"], 5] == 0.0)
+    # [0] + [6]: lse log2(e) as a float and its rounding residue
+    v = ref["valid"]
+    l2 = rs[v, 0].astype(np.float64) + rs[v, 6].astype(np.float64)
+    check_loss(l2 / float(np.float32(L2E_F)), ref["lse"][v], "split row-state lse")
+    assert np.all(np.abs(rs[v, 6]) <= np.spacing(np.abs(rs[v, 0])) / 2)
 
 
 @pytest.mark.parametrize("dtype,align", [(torch.bfloat16, 8), (torch.float32, 4), (torch.bfloat16, 1)])
@@ -204,4 +211,9 @@ def test_weighted_backward(dtype, shards, V):
                                            row_weight=_np(w_row).astype(np.float64))
     check_loss(_np(loss), ref["loss"], "weighted loss")
     check_loss(_np(segsum), ref["seg_nll"], "weighted seg")
-    check_grad(to_np64(grad), ref_w["grad"], dtype, "weighted grad")
+    # unit scale of a row: the larger of its NLL weight and its z-loss weight
+    # unit scale of a row: the larger of its NLL weight and its z-loss weight;
+    # a weight of either sign makes the row factor w + u 2 alpha lse a float
+    # sum that may cancel, so no relative bar here
+    check_grad(to_np64(grad), ref_w["grad"], dtype, "weighted grad",
+               scale=np.maximum(np.abs(_np(w_row).astype(np.float64)), gamma), rel=False)
