@@ -158,6 +158,47 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p,
                            void* stream);
 
 /*
+ * ce_fused_fwd_bwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. It computes exactly what
+ * ce_fused_fwd_bwd computes (the same kernels, bit for bit) and allocates
+ * nothing: the workspace lives in a fixed device array of
+ * CE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, reserved
+ * when the library is loaded and held until the process ends. Its device
+ * address is looked up on the first call on each device.
+ *
+ *  Arguments as for ce_fused_fwd_bwd, minus workspace / workspace_bytes.
+ *  Returns CE_ERR_WORKSPACE when the call would need more than
+ *  CE_NOALLOC_SCRATCH_BYTES (ce_workspace_bytes(p) for a gradient call; less
+ *  without a gradient): with S segments, 4 T + 4 (S + 1) bytes (each rounded
+ *  up to 256); for fp32 logits past 65536 columns with a gradient, 32 T
+ *  bytes more; 4096 more under CE_FLAG_VALIDATE. That is up to about 2
+ *  million rows with segments, or 262144 rows of the two-workgroup fp32
+ *  mode. CE_ERR_INVALID_ARG when the stream belongs to another device than
+ *  the current one.
+ *  Every call on one GPU shares that GPU's array and leaves the last call's
+ *  contents in it: two calls that may run at the same time on one GPU (on
+ *  different streams, or on one stream from different host threads without
+ *  ordering) race on it and must not be issued; calls on one stream are
+ *  ordered and safe. Nothing in it needs clearing between calls (every
+ *  kernel writes what it later reads).
+ */
+#define CE_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+ce_status ce_fused_fwd_bwd_noalloc(const ce_problem* p,
+                                   const void* logits,
+                                   const int64_t* targets,
+                                   const uint8_t* mask,
+                                   const int32_t* segment_ids,
+                                   float z_alpha,
+                                   float grad_scale,
+                                   float* loss_out,
+                                   float* seg_loss_out,
+                                   void* grad_out,
+                                   float* lse_out,
+                                   void* stream);
+
+/*
  * Forward only, with per-row statistics a caller may want from the same read
  * of the logits: the full logsumexp and the entropy of the row's softmax.
  * torchtitan PR #5661 "fix softmax collapse with improved CE perf" (fourth

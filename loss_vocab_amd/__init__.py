@@ -117,6 +117,31 @@ def ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale,
         raise CeError(st)
 
 
+def ce_fused_fwd_bwd_noalloc(logits, targets, mask, segment_ids, z_alpha, grad_scale,
+                             loss_out, seg_loss_out, grad_out, *, lse_out=None, num_segments=0,
+                             segment_mean=False, ignore_index=IGNORE_INDEX, stream=None,
+                             validate=False):
+    """Same-named wrapper of the allocation-free C entry point: arguments as
+    for ``ce_fused_fwd_bwd`` without a workspace (the library's fixed per-GPU
+    scratch array serves instead; calls that may overlap on one GPU race on
+    it). Allocates nothing; raises CeError(CE_ERR_WORKSPACE) when the problem
+    needs more than ``_lib.NOALLOC_SCRATCH_BYTES`` of workspace."""
+    p = make_problem(logits, grad_out, num_segments=num_segments,
+                     segment_mean=segment_mean, ignore_index=ignore_index, validate=validate)
+    for name, t, dt in (("targets", targets, torch.int64), ("mask", mask, torch.uint8),
+                        ("segment_ids", segment_ids, torch.int32),
+                        ("loss_out", loss_out, torch.float32),
+                        ("seg_loss_out", seg_loss_out, torch.float32),
+                        ("lse_out", lse_out, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous {dt} tensor")
+    st = _lib.noalloc_raw(p, _ptr(logits), _ptr(targets), _ptr(mask), _ptr(segment_ids),
+                          z_alpha, grad_scale, _ptr(loss_out), _ptr(seg_loss_out),
+                          _ptr(grad_out), _ptr(lse_out), _stream(logits, stream))
+    if st != CE_OK:
+        raise CeError(st, "ce_fused_fwd_bwd_noalloc")
+
+
 def ce_fused(logits, targets, *, mask=None, segment_ids=None, num_segments=0,
              z_alpha=0.0, grad_scale=1.0, segment_mean=False, grad_dtype=None,
              in_place=False, want_grad=True, ignore_index=IGNORE_INDEX, validate=False,

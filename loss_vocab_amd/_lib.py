@@ -28,9 +28,12 @@ CE_FLAG_VALIDATE = 0x2
 ROW_STATE = 8   # floats of saved state per row (ce_rows_finish)
 
 # Every symbol include/ce_fused.h declares.
-EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_fused_forward", "ce_shard_stats",
-           "ce_rows_finish", "ce_shard_grad", "ce_lmhead_workspace_bytes", "ce_lmhead_fwd_bwd",
-           "ce_fused_distill", "ce_status_string")
+EXPORTS = ("ce_workspace_bytes", "ce_fused_fwd_bwd", "ce_fused_fwd_bwd_noalloc", "ce_fused_forward",
+           "ce_shard_stats", "ce_rows_finish", "ce_shard_grad", "ce_lmhead_workspace_bytes",
+           "ce_lmhead_fwd_bwd", "ce_fused_distill", "ce_status_string")
+
+# Size of the library's fixed scratch array (CE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class CeProblem(ctypes.Structure):
@@ -93,6 +96,11 @@ def _load(path=LIB_PATH):
         vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
     ]
     lib.ce_fused_fwd_bwd.restype = ctypes.c_int
+    lib.ce_fused_fwd_bwd_noalloc.argtypes = [
+        ctypes.POINTER(CeProblem), vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+        vp, vp, vp, vp, vp,
+    ]
+    lib.ce_fused_fwd_bwd_noalloc.restype = ctypes.c_int
     lib.ce_fused_forward.argtypes = [
         ctypes.POINTER(CeProblem), vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
         ctypes.c_size_t, vp,
@@ -143,6 +151,15 @@ def call_raw(problem, logits, targets, mask, segment_ids, z_alpha, grad_scale,
         segment_ids or None, float(z_alpha), float(grad_scale), loss_out or None,
         seg_loss_out or None, grad_out or None, lse_out or None, workspace or None,
         int(workspace_bytes_), stream or None))
+
+
+def noalloc_raw(problem, logits, targets, mask, segment_ids, z_alpha, grad_scale,
+                loss_out, seg_loss_out, grad_out, lse_out, stream):
+    """Call ce_fused_fwd_bwd_noalloc with integer addresses (0 = NULL)."""
+    return int(LIB.ce_fused_fwd_bwd_noalloc(
+        ctypes.byref(problem), logits or None, targets or None, mask or None,
+        segment_ids or None, float(z_alpha), float(grad_scale), loss_out or None,
+        seg_loss_out or None, grad_out or None, lse_out or None, stream or None))
 
 
 def forward_raw(problem, logits, targets, mask, segment_ids, z_alpha, loss_out, seg_loss_out,

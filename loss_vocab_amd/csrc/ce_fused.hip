@@ -36,6 +36,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "ce_fused.h"
 
@@ -1667,7 +1668,71 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
 
 }  // namespace
 
+// Scratch of the allocation-free entry point: the workspace of
+// ce_fused_fwd_bwd (segment staging and offsets, pair-mode exchange slots,
+// the debug scan's words) in a fixed device array, one per GPU, held until
+// the process ends. In host code `scratch` names a host-side stand-in: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[CE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of this device's `scratch` (dev must be current).
+ce_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return CE_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (ptr == nullptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        return CE_ERR_HIP;
+      }
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return CE_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+ce_status ce_fused_fwd_bwd_noalloc(const ce_problem* p, const void* logits,
+                                   const int64_t* targets, const uint8_t* mask,
+                                   const int32_t* segment_ids, float z_alpha, float grad_scale,
+                                   float* loss_out, float* seg_loss_out, void* grad_out,
+                                   float* lse_out, void* stream_ptr) {
+  if (p == nullptr || p->T < 0 || p->num_segments < 0) return CE_ERR_INVALID_ARG;
+  // What ce_fused_fwd_bwd would ask of a workspace, against the fixed size.
+  const size_t need = segment_ws_bytes(p) + pair_ws_bytes(p, grad_out != nullptr) +
+                      validate_ws_bytes(p);
+  if (need > CE_NOALLOC_SCRATCH_BYTES) return CE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    // The scratch of the stream's device, which must be the current one
+    // (the symbol's address is looked up with that device current).
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    int cur = -1;
+    hipDevice_t sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+      (void)hipGetLastError();
+      return CE_ERR_HIP;
+    }
+    if (static_cast<int>(sdev) != cur) return CE_ERR_INVALID_ARG;
+    const ce_status st = scratch_address(cur, &ws);
+    if (st != CE_OK) return st;
+  }
+  return run_rows(p, logits, targets, mask, segment_ids, z_alpha, grad_scale, loss_out,
+                  seg_loss_out, grad_out, lse_out, nullptr, ws, need > 0 ? CE_NOALLOC_SCRATCH_BYTES : 0,
+                  stream_ptr);
+}
 
 size_t ce_workspace_bytes(const ce_problem* p) {
   if (p == nullptr || p->T < 0 || p->num_segments < 0) return 0;

@@ -390,6 +390,13 @@ out["shard_stats"] = L.shard_stats_raw(s, 0x10000000, 0x20000000, 0, 0x30000000,
 out["rows_finish"] = L.rows_finish_raw(p, 1, 0x10000000, 0x20000000, 0, 0, 0.0, 0x30000000, 0,
                                        0x40000000, 0, 0, 0)
 out["shard_grad"] = L.shard_grad_raw(s, 0x10000000, 0x20000000, 0x30000000, 0, 1.0, 0x40000000, 0)
+out["noalloc"] = L.noalloc_raw(p, 0x10000000, 0x20000000, 0, 0, 0.0, 1.0, 0x30000000, 0,
+                               0x40000000, 0, 0)
+ps = L.CeProblem()
+ps.T, ps.V, ps.ld_logits, ps.ld_grad, ps.num_segments = 8, 100, 100, 100, 2
+ps.ignore_index = -100
+out["noalloc_segments"] = L.noalloc_raw(ps, 0x10000000, 0x20000000, 0, 0x70000000, 0.0, 1.0,
+                                        0x30000000, 0x80000000, 0x40000000, 0, 0)
 out["distill"] = L.distill_raw(p, 0x10000000, 0x60000000, 100, 0, 0x20000000, 0, 0.0, 1.0, 1.0,
                                0x30000000, 0, 0x40000000, 0)
 print(out)
@@ -409,7 +416,7 @@ def test_valid_calls_without_a_device_return_ce_err_hip(tmp_path):
     assert res.returncode == 0, res.stderr[-2000:]
     got = ast.literal_eval(res.stdout.strip().splitlines()[-1])
     assert got == {k: 5 for k in ("fused", "forward", "shard_stats", "rows_finish", "shard_grad",
-                                  "distill")}, got
+                                  "noalloc", "noalloc_segments", "distill")}, got
 
 
 def test_forward_only_needs_no_pair_slots():
@@ -430,3 +437,27 @@ def test_forward_only_needs_no_pair_slots():
     if not os.path.exists("/dev/kfd"):
         assert _call(p, grad=0) == 5
         assert _fwd(p) == 5
+
+
+def _noalloc(p, logits=A_LOGITS, targets=A_TGT, seg=0, loss=A_LOSS, seg_out=0, grad=A_GRAD, lse=0):
+    return _lib().noalloc_raw(p, logits, targets, 0, seg, 0.0, 1.0, loss, seg_out, grad, lse, 0)
+
+
+def test_noalloc_limits_and_validation():
+    """The allocation-free entry refuses, before any HIP call, a problem whose
+    workspace would exceed the fixed scratch (CE_ERR_WORKSPACE), and
+    validates like the workspace entry."""
+    L = _lib()
+    assert L.NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert L.LIB.ce_fused_fwd_bwd_noalloc(None, None, None, None, None, 0.0, 1.0, None, None,
+                                          None, None, None) == 1
+    # segments: 4 T bytes of staging past 8 MiB
+    big = _problem(T=2_200_000, V=100, S=4, flags=1)
+    assert _noalloc(big, seg=A_SEG, seg_out=A_LOSS + (1 << 24)) == 4
+    # two-workgroup fp32 rows: 32 T bytes of slots past 8 MiB with a gradient
+    pair = _problem(T=300_000, V=70000)
+    assert _noalloc(pair) == 4
+    # within the limit, host validation still applies first
+    assert _noalloc(_problem(V=0)) == 1
+    assert _noalloc(_problem(), grad=A_LOGITS + 64) == 3
+    assert _noalloc(_problem(), lse=A_LOGITS) == 3
