@@ -20,10 +20,15 @@ INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libce_fused.so")
 ARCH = "gfx950"
 
-# Packed-FP32 VALU forms are switched off for all device code.
+# Packed-FP32 VALU forms are switched off for all device code. Machine-level
+# loop-invariant code motion is off: the kernels are persistent loops over
+# rows, and hoisting per-slot lane masks, offsets and fp64 constants out of
+# the row loop only moved them into spilled registers (the row-resident
+# kernel keeps a whole row in 64 VGPRs per lane and has none to spare).
 HIP_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-disable-machine-licm",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -1106,6 +1106,301 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-resident kernel: rows (in pair mode, half rows) of up to
+// (NREG + NLDS) * 1024 16-byte chunks stay wholly on chip between the two
+// passes -- NREG slots per lane in VGPRs, NLDS slots per lane in LDS filled
+// straight from HBM -- so every logit is read from HBM exactly once (the
+// streamed-tier kernel re-reads what does not fit). Slot i of thread tid is
+// chunk i * 1024 + tid. All of a row's loads go out at its start, so pass 1
+// reduces slots as they land. (Issuing the next row's slots during this
+// row's gradient pass measured slower: it moves every read into the
+// gradient pass and leaves pass 1 with no memory traffic of its own.)
+//
+// Register discipline: every per-slot test compares the slot index with the
+// end slot `se` or the target's slot `st`, both re-read through an empty asm
+// at each use, and the lane index is re-derived every row, so the compiler
+// keeps a few scalars live instead of a lane mask or offset per slot. In the
+// end slot, lanes past the row end load the last chunk again (in bounds),
+// count as -inf and store nothing; register slots past the end slot load the
+// last chunk (one line per wave) and are not reduced or stored; LDS slots
+// past it are not loaded.
+// ---------------------------------------------------------------------------
+template <typename TI, typename TO, int NREG, int NLDS, int MODE>
+__global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
+  static_assert(MODE == kFused || MODE == kPair, "the fused call, whole or half rows");
+  constexpr int BLOCK = 1024;
+  constexpr bool PAIR = MODE == kPair;
+  constexpr int W = Elem<TI>::VEC;                 // elements per chunk
+  constexpr uint32_t OB = W * Elem<TO>::BYTES;     // gradient bytes per chunk
+  constexpr uint32_t SLOT = BLOCK * 16u;           // bytes of input per slot
+  __shared__ float red_m[2][BLOCK / 64];
+  __shared__ float red_s[2][BLOCK / 64];
+  __shared__ u32x4 stage[NLDS > 0 ? NLDS : 1][BLOCK];
+  __shared__ float epi[2][4];
+  [[maybe_unused]] __shared__ float pair_sh[2][4];
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wid = tid >> 6;
+  const uint32_t half = PAIR ? (blockIdx.x >> 3) & 1u : 0u;
+  const int64_t row0 = PAIR ? static_cast<int64_t>(blockIdx.x >> 4) * 8 + (blockIdx.x & 7u)
+                            : static_cast<int64_t>(blockIdx.x);
+  const int64_t row_step = PAIR ? gridDim.x / 2 : gridDim.x;
+  const int64_t c0 = (PAIR && half) ? p.pair_split : 0;
+  [[maybe_unused]] bool pair_broken = false;
+  const uint32_t V = static_cast<uint32_t>(PAIR ? (half ? p.V - p.pair_split : p.pair_split) : p.V);
+  const uint32_t nchunk = V / W;
+  const uint32_t c16_last = (nchunk > 0 ? nchunk - 1 : 0) * 16u;
+  const uint32_t tail_begin = nchunk * W;
+  const size_t in_row_bytes = static_cast<size_t>(p.ld_in) * Elem<TI>::BYTES;
+  const size_t out_row_bytes = static_cast<size_t>(p.ld_out) * Elem<TO>::BYTES;
+  const uint32_t neg_w = Elem<TI>::NEG_INF_WORD;
+  const kconst_i64* labels = (const kconst_i64*)p.targets;
+  const kconst_i32* seg_ids = (const kconst_i32*)p.seg_ids;
+  const kconst_i32* seg_start = (const kconst_i32*)p.seg_start;
+  // The slot that holds the row's last chunk (-1: no whole chunk).
+  const int se_row = nchunk > 0 ? static_cast<int>((nchunk - 1) / BLOCK) : -1;
+  auto end_slot = [&]() -> int {
+    int se = __builtin_amdgcn_readfirstlane(se_row);
+    asm volatile("" : "+s"(se));
+    return se;
+  };
+
+  int64_t t_next = row0 < p.T ? labels[row0] : 0;
+  int par = 0;
+  for (int64_t r = row0; r < p.T; r += row_step, par ^= 1) {
+    const int64_t t64 = t_next;
+    if (r + row_step < p.T) t_next = labels[r + row_step];
+    void* grow = static_cast<char*>(p.grad) + r * out_row_bytes + c0 * Elem<TO>::BYTES;
+    const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+    if (!valid || t64 - p.v0 < 0 || t64 - p.v0 >= p.V) {
+      // Ignored row: +0.0 everywhere, logits never read. Valid row with an
+      // out-of-range target: NaN loss and gradient row. (Both halves of a
+      // pair decide alike; half 0 writes the row's loss.)
+      fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true, !PAIR || half == 0);
+      continue;
+    }
+    const int64_t tl = t64 - p.v0 - c0;
+    const bool owned = tl >= 0 && tl < static_cast<int64_t>(V);
+    const uint32_t t = owned ? static_cast<uint32_t>(tl) : V;
+    const char* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes + c0 * Elem<TI>::BYTES;
+    // The lane index, re-derived every row: every per-lane mask and offset
+    // below is formed inside the row, next to its use.
+    uint32_t tid_r = tid;
+    asm volatile("" : "+v"(tid_r));
+    const uint32_t vin = tid_r * 16u;
+
+    // ---- every slot's load goes out now (read once: non-temporal) --------
+    u32x4 raw[NREG];
+    {
+      const __amdgpu_buffer_rsrc_t rin =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(zrow), 0, nchunk * 16u, kBufWord3);
+#pragma unroll
+      for (int i = 0; i < NREG; ++i)
+        raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rin, min(vin + i * SLOT, c16_last), 0, kNT);
+    }
+#pragma unroll
+    for (int j = 0; j < NLDS; ++j) {
+      if (NREG + j > end_slot()) break;
+      // HBM -> LDS without a register round trip: lane l of a wave lands
+      // at base + 16 l, so slot j of thread tid is stage[j][tid].
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(zrow + min(vin + (NREG + j) * SLOT, c16_last)),
+          (__attribute__((address_space(3))) void*)(&stage[j][tid_r & ~63u]), 16, 0, kNT);
+    }
+    const float zt = owned ? Elem<TI>::load1(zrow, t) : kNegInf;
+    [[maybe_unused]] int32_t sid = 0;
+    if (p.seg_mean) sid = seg_ids[r];
+
+    // Where the target sits: chunk ct, element kt, slot st, lane `mine`.
+    const uint32_t ct = t / W;
+    const uint32_t kt = t - ct * W;
+    const int st_row = t < tail_begin ? static_cast<int>(ct / BLOCK) : -1;
+    const bool mine = t < tail_begin && (ct % BLOCK) == tid_r;
+    const uint32_t kq = (kt * Elem<TI>::BYTES) >> 2;
+    const uint32_t ksh = (kt * Elem<TI>::BYTES * 8u) & 31u;
+    const uint32_t kmask = Elem<TI>::BYTES == 4 ? 0xffffffffu : (0xffffu << ksh);
+    const uint32_t kput = Elem<TI>::BYTES == 4 ? 0xff800000u : (0xff80u << ksh);
+    auto tgt_slot = [&]() -> int {
+      int st = __builtin_amdgcn_readfirstlane(st_row);
+      asm volatile("" : "+s"(st));
+      return st;
+    };
+    // Lanes past the row end (in the end slot) count as -inf; the target's
+    // element in its slot too (in the one lane that holds it).
+    auto fixed = [&](u32x4 v, int slot) -> u32x4 {
+      if (slot == end_slot()) {
+        const bool out = static_cast<uint32_t>(slot) * BLOCK + tid_r >= nchunk;
+        v.x = out ? neg_w : v.x;
+        v.y = out ? neg_w : v.y;
+        v.z = out ? neg_w : v.z;
+        v.w = out ? neg_w : v.w;
+      }
+      if (slot == tgt_slot()) {
+        const uint32_t am = mine ? ~kmask : ~0u, om = mine ? kput : 0u;
+        v.x = kq == 0 ? (v.x & am) | om : v.x;
+        v.y = kq == 1 ? (v.y & am) | om : v.y;
+        v.z = kq == 2 ? (v.z & am) | om : v.z;
+        v.w = kq == 3 ? (v.w & am) | om : v.w;
+      }
+      return v;
+    };
+
+    [[maybe_unused]] int32_t seg_len = 1;
+    if (p.seg_mean) {
+      sid = sid < 0 ? 0 : (sid >= p.num_segments ? p.num_segments - 1 : sid);
+      const int32_t len = seg_start[sid + 1] - seg_start[sid];
+      seg_len = len > 0 ? len : 1;
+    }
+
+    // ---- pass 1: register slots, then LDS slots, one online update each ----
+    float mL = kNegInf, s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      if (i > end_slot()) break;
+      float x[W];
+      Elem<TI>::unpack(fixed(raw[i], i), x);
+      online_group<W>(mL, s, x);
+    }
+    if constexpr (NLDS > 0) {
+      if (NREG <= end_slot()) {
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's HBM -> LDS copies have landed
+#pragma unroll
+        for (int j = 0; j < NLDS; ++j) {
+          if (NREG + j > end_slot()) break;
+          float x[W];
+          Elem<TI>::unpack(fixed(stage[j][tid_r], NREG + j), x);
+          online_group<W>(mL, s, x);
+        }
+      }
+    }
+    if (tid_r < V - tail_begin) {
+      const uint32_t j = tail_begin + tid_r;
+      const float xv = (j == t) ? kNegInf : Elem<TI>::load1(zrow, j);
+      merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
+    }
+    block_reduce<BLOCK>(mL, s, red_m, red_s, par, tid_r & 63u, tid_r >> 6);
+
+    float ztm = zt;
+    if constexpr (PAIR) {
+      // Exchange with the partner half as the pair-mode row kernel does:
+      // two self-validating 64-bit words per half, relaxed device-scope
+      // atomics, a bounded wait that gives a NaN row instead of a hang.
+      uint64_t* slot = reinterpret_cast<uint64_t*>(p.pair_part) + 4 * r;
+      if (tid == 0) {
+        const uint64_t ms = (static_cast<uint64_t>(__float_as_uint(s)) << 32) | __float_as_uint(mL);
+        __hip_atomic_store(slot + 2 * half, ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(slot + 2 * half + 1, static_cast<uint64_t>(__float_as_uint(zt)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float pm = __builtin_nanf(""), ps = __builtin_nanf(""), pz = __builtin_nanf("");
+        if (!pair_broken) {
+          uint64_t w0 = ~0ull, w1 = ~0ull;
+          uint32_t n = 0;
+          while (n < kPairSpin) {
+            if (w0 == ~0ull)
+              w0 = __hip_atomic_load(slot + 2 * (half ^ 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (w1 == ~0ull)
+              w1 = __hip_atomic_load(slot + 2 * (half ^ 1u) + 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+            if (w0 != ~0ull && w1 != ~0ull) break;
+            __builtin_amdgcn_s_sleep(2);
+            ++n;
+          }
+          if (n < kPairSpin) {
+            pm = __uint_as_float(static_cast<uint32_t>(w0));
+            ps = __uint_as_float(static_cast<uint32_t>(w0 >> 32));
+            pz = __uint_as_float(static_cast<uint32_t>(w1));
+          } else {
+            pair_broken = true;
+          }
+        }
+        pair_sh[par][0] = pm;
+        pair_sh[par][1] = ps;
+        pair_sh[par][2] = pz;
+      }
+      __syncthreads();
+      const float pm = pair_sh[par][0], ps = pair_sh[par][1], pz = pair_sh[par][2];
+      if (pm != pm) {
+        mL = __builtin_nanf("");
+        s = __builtin_nanf("");
+      } else {
+        merge(mL, s, pm, ps);
+      }
+      ztm = fmaxf(zt, pz);
+    }
+    // Wave 0 runs the fp64 epilogue and shares the row factors through LDS.
+    // (Its scalar inputs pass an empty asm, so their fp64 forms are made
+    // here, not hoisted out of the row loop into registers held throughout.)
+    if (wid == 0) {
+      RowParams q = p;
+      asm volatile("" : "+s"(q.grad_scale), "+s"(q.z_alpha));
+      const RowOut o = row_epilogue(q, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0),
+                                    1.0 / static_cast<double>(seg_len));
+      if (lane == 0) {
+        epi[par][0] = o.g_t;
+        epi[par][1] = o.cnt;
+        epi[par][2] = o.kl;
+      }
+    }
+    __syncthreads();
+    const float cnt = epi[par][1], kl = epi[par][2];
+
+    // ---- pass 2: gradient ----------------------------------------------
+    const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(grow, 0, nchunk * OB, kBufWord3);
+    // (opaque: with equal element sizes the store offsets equal the load
+    // offsets, and the compiler would keep every load's offset live for them)
+    uint32_t vout = tid_r * OB;
+    asm volatile("" : "+v"(vout));
+    auto store_slot = [&](int slot, const u32x4 v) {
+      float x[W];
+      Elem<TI>::unpack(v, x);
+      float g[W];
+#pragma unroll
+      for (int k = 0; k < W; ++k) g[k] = cnt * fexp2(__builtin_fmaf(x[k], kL2E, -kl));
+      if (slot == end_slot() && static_cast<uint32_t>(slot) * BLOCK + tid_r >= nchunk) return;
+      const uint32_t vo = vout + static_cast<uint32_t>(slot) * BLOCK * OB;
+      if constexpr (Elem<TO>::BYTES == 2 && W == 8) {
+        const u32x4 q = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
+                         pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(q, rout, vo, 0, kNT);
+      } else if constexpr (Elem<TO>::BYTES == 2) {
+        const u32x2 q = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(q, rout, vo, 0, kNT);
+      } else {
+#pragma unroll
+        for (int h = 0; h < W / 4; ++h) {
+          const u32x4 q = {__float_as_uint(g[4 * h]), __float_as_uint(g[4 * h + 1]),
+                           __float_as_uint(g[4 * h + 2]), __float_as_uint(g[4 * h + 3])};
+          __builtin_amdgcn_raw_buffer_store_b128(q, rout, vo + 16u * h, 0, kNT);
+        }
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < NREG; ++i) {
+      if (i > end_slot()) break;
+      store_slot(i, raw[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NLDS; ++j) {
+      if (NREG + j > end_slot()) break;
+      store_slot(NREG + j, stage[j][tid_r]);
+    }
+    if (tid_r < V - tail_begin) {
+      const uint32_t j = tail_begin + tid_r;
+      const float g = (j == t) ? epi[par][0]
+                               : cnt * fexp2(__builtin_fmaf(Elem<TI>::load1(zrow, j), kL2E, -kl));
+      Elem<TO>::store1(grow, j, g);
+    }
+    // The target column: written after its chunk by the same lane, so this
+    // store lands last (a lane's stores to one address stay in order).
+    if (mine) Elem<TO>::store1(grow, t, epi[par][0]);
+    // The next row's HBM -> LDS copies overwrite the staging slots: every
+    // LDS read of them by this wave must have returned first.
+    if constexpr (NLDS > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+}
+
 // Debug scan (CE_FLAG_VALIDATE): block b writes to words[b] the OR over its
 // rows of 1 (target neither ignored nor in [0, V)), 2 (segment id outside
 // [0, S)) and 4 (segment id below the previous row's). Grid-stride over rows;
@@ -1303,6 +1598,23 @@ __global__ __launch_bounds__(256) void ce_fill_u32_kernel(uint32_t* __restrict__
 // refuses it, or the stream is being captured into a graph (whose replay
 // need not keep the co-residency a cooperative launch guarantees), the
 // whole-row kernel runs instead.
+#ifndef CE_ROWRES
+#define CE_ROWRES 1
+#endif
+constexpr bool rowres_off() { return CE_ROWRES == 0; }
+
+// Row-resident shape: 16 register slots and 9 LDS slots per lane of 1024,
+// 25600 chunks (400 KiB) of a row on chip.
+constexpr int kResReg = 16, kResLds = 9;
+constexpr int64_t kResChunks = int64_t{kResReg + kResLds} * 1024;
+
+template <typename TI, typename TO>
+ce_status launch_rowres(const RowParams& rp, hipStream_t stream) {
+  static std::atomic<int> occ{0};
+  return launch_persistent(ce_rowres_kernel<TI, TO, kResReg, kResLds, kFused>, 1024, occ, rp,
+                           stream, 64);
+}
+
 template <typename TI, typename TO>
 ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -1312,8 +1624,14 @@ ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
   }
   if (cap != hipStreamCaptureStatusNone)
     return launch_rows<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1>(rp, stream, 64);
-  auto kern = ce_rows_kernel<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1, kPair>;
-  static std::atomic<int> occ{0};
+  // Half rows that fit on chip take the row-resident kernel.
+  const bool res = (rp.V - rp.pair_split) / Elem<TI>::VEC <= kResChunks && !rowres_off();
+  const void* kern = res ? reinterpret_cast<const void*>(
+                               ce_rowres_kernel<TI, TO, kResReg, kResLds, kPair>)
+                         : reinterpret_cast<const void*>(
+                               ce_rows_kernel<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1, kPair>);
+  static std::atomic<int> occ_res{0}, occ_rows{0};
+  std::atomic<int>& occ = res ? occ_res : occ_rows;
   int per_cu = occ.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 1024, 0) != hipSuccess)
@@ -1328,8 +1646,8 @@ ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
     RowParams arg = rp;
     void* args[] = {&arg};
-    if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3(static_cast<unsigned>(grid)),
-                                   dim3(1024), args, 0, stream) == hipSuccess)
+    if (hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(1024), args, 0,
+                                   stream) == hipSuccess)
       return CE_OK;
     (void)hipGetLastError();
   }
@@ -1359,11 +1677,14 @@ ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   if (!vec) return launch_rows_scalar<TI, TO, WRITE>(rp, stream);
   const int64_t nchunk = rp.V / Elem<TI>::VEC;
   if (nchunk <= 8192) return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
+  if constexpr (WRITE) {
+    if (nchunk <= kResChunks && !rowres_off()) return launch_rowres<TI, TO>(rp, stream);
+  }
   if (nchunk <= 16384)
     return launch_rows<TI, TO, 1024, 0, 0, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
   if constexpr (WRITE && Elem<TI>::BYTES == 4) {
     // fp32 rows this long: two workgroups per row keep twice the share of
-    // each row on chip (the pass-2 re-reads fall by half)
+    // each row on chip (the whole half row up to 2 * 25600 chunks)
     if (rp.pair_part != nullptr) return launch_rows_pair<TI, TO>(rp, stream);
   }
   return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true, 1>(rp, stream, 64);

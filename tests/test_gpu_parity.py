@@ -309,10 +309,12 @@ def test_deterministic():
 
 # ---------------------------------------------------------------------------
 # Kernel tiers by row length in 16-byte chunks: up to 8192 chunks (512 lanes,
-# 8 LDS slots per lane, rest streamed), up to 16384 (1024 lanes, 9 LDS slots),
-# beyond (1024 lanes, 4 VGPR + 9 LDS slots, rest streamed). Targets
-# are placed in each kind of slot: register, LDS, streamed, the row's partial
-# last slot and the tail past the last whole chunk.
+# 8 LDS slots per lane, rest streamed); up to 25600 (the row-resident kernel:
+# 1024 lanes, 16 register slots then 9 LDS slots, the whole row on chip);
+# beyond (1024 lanes, 4 VGPR + 9 LDS slots, rest streamed), and for fp32 rows
+# up to 51200 chunks two workgroups per row, each row-resident on its half.
+# Targets are placed in each kind of slot: register, LDS, streamed, the row's
+# partial last slot and the tail past the last whole chunk.
 # ---------------------------------------------------------------------------
 
 TIER_CASES = [
@@ -335,7 +337,8 @@ def _tier_targets(V, W):
     nchunk = V // W
     lanes = 512 if nchunk <= 8192 else 1024
     marks = [0, 1, lanes - 1, lanes, 4 * lanes - 1, 4 * lanes, 8 * lanes - 1, 8 * lanes,
-             13 * lanes - 1, 13 * lanes, 17 * lanes + 5, nchunk - 1]
+             13 * lanes - 1, 13 * lanes, 16 * lanes - 1, 16 * lanes, 17 * lanes + 5,
+             24 * lanes + 3, nchunk - 1]
     elems = sorted({min(V - 1, c * W + (c % W)) for c in marks if c < max(nchunk, 1)})
     return elems + [V - 1, V // 2]
 
@@ -373,12 +376,12 @@ def test_very_long_rows(dtype, V):
 
 
 def test_long_fp32_rows_two_workgroups_per_row():
-    """fp32 rows past 16384 chunks run two workgroups per row that exchange
+    """fp32 rows past 25600 chunks run two workgroups per row that exchange
     their halves' statistics: segments, a mask, ignored and out-of-range rows,
     targets in either half and at the split, in place equal to out of place."""
     import loss_vocab_amd as L
     g = torch.Generator(device=DEV).manual_seed(71)
-    T, V, S = 40, 70001, 3
+    T, V, S = 40, 110001, 3
     split = (V // 4 // 2) * 4
     z = torch.randn(T, V, generator=g, device=DEV) * 2
     t = torch.randint(0, V, (T,), generator=g, device=DEV)
@@ -398,6 +401,42 @@ def test_long_fp32_rows_two_workgroups_per_row():
     assert torch.equal(loss_a.nan_to_num(7.0), loss_b.nan_to_num(7.0))
     assert torch.equal(grad_a.nan_to_num(7.0), grad_b.nan_to_num(7.0))
     assert torch.equal(seg_a.nan_to_num(7.0), seg_b.nan_to_num(7.0))   # a NaN row poisons its segment
+
+
+@pytest.mark.parametrize("dtype,V,T", [(torch.bfloat16, 201088, 600), (torch.float32, 151936, 520),
+                                       (torch.bfloat16, 70001, 900)])
+def test_row_resident_many_rows(dtype, V, T):
+    """More rows than workgroups on the row-resident kernel (whole rows, and
+    fp32 half rows in pairs): a workgroup issues its next read row's loads
+    during the gradient pass and fills the ignored, masked and out-of-range
+    rows it skips in between. Runs of skipped rows, a skipped last row,
+    segments, and in place equal to out of place."""
+    import loss_vocab_amd as L
+    print(f"[parity] row-resident many rows V={V} T={T} {dtype}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V + T)
+    z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[::10] = -100                                 # every tenth row ignored
+    t[256:262] = -100                              # a run of ignored rows
+    t[T - 1] = -100                                # the last row is not read
+    t[300] = V + 5                                 # out of range: NaN row
+    mask = torch.ones(T, dtype=torch.uint8, device=DEV)
+    mask[[7, 263, 511]] = 0
+    for r in (5, 299, T - 3):
+        z[r, t[r]] = float(z[r].float().max()) + 33.0
+    S = 9
+    seg = (torch.arange(T, device=DEV) * S // T).to(torch.int32)
+    inp = _inp(z, t, alpha=1e-4, gamma=1.0, seg=seg, S=S, seg_mean=True)
+    loss_a, grad_a, seg_a, _ = compare_all(inp, mask=mask, what=f"rowres V={V}")
+    zc = z.clone()
+    loss_b, grad_b, seg_b = L.ce_fused(zc, t, mask=mask, segment_ids=seg, num_segments=S,
+                                       z_alpha=1e-4, grad_scale=1.0, segment_mean=True,
+                                       in_place=True)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(loss_a.nan_to_num(7.0), loss_b.nan_to_num(7.0))
+    assert torch.equal(grad_a.nan_to_num(7.0).view(bits), grad_b.nan_to_num(7.0).view(bits))
+    assert torch.equal(seg_a.nan_to_num(7.0), seg_b.nan_to_num(7.0))
 
 
 def test_many_rows_per_workgroup():
