@@ -404,11 +404,11 @@ def bench_workload(wl, args, dev, stream, main=True):
     bracketed by synchronisation, nothing else enqueued between the calls (an
     event around every call costs ~9 us per call on MI355X: the next kernel
     waits for the marker). A workload whose gradient overwrites its logits
-    (in place) instead restores each step's logits from a pristine copy
-    before the step, outside two events around the step, so that every step
-    computes on the recipe's logits; its figure is the mean of the per-step
-    event times. One call per step, so the figure is the average launch
-    duration of the fused call."""
+    (in place) runs in rounds of back-to-back steps, one per buffer set, each
+    round between two events, with every set's logits restored from a
+    pristine copy before the round (outside the events), so that every step
+    computes on the recipe's logits. One call per step, so the figure is the
+    average launch duration of the fused call."""
     import torch
 
     import loss_vocab_amd as L
@@ -417,6 +417,10 @@ def bench_workload(wl, args, dev, stream, main=True):
     in_place = wl.grad == "inplace" and args.path != "forward"
     logit_bytes = wl.T * wl.V * (4 if wl.dtype == "f32" else 2)
     rotate = args.rotate or (3 if logit_bytes < (2 << 30) else 2)
+    if in_place and not args.rotate:
+        # in place: enough sets (each with a pristine copy) for runs of
+        # back-to-back steps between restores, within about 40 GB
+        rotate = max(2, min(args.steps, int(40e9 // (2 * logit_bytes))))
     sets = []
     for i in range(rotate):
         inp = make_inputs(wl, device=dev, seed_offset=i)
@@ -503,22 +507,41 @@ def bench_workload(wl, args, dev, stream, main=True):
     torch.cuda.synchronize()
 
     if in_place:
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        for i in range(args.steps):
+        # Rounds of back-to-back steps, one per buffer set, between two events;
+        # before each round every set's logits are restored from its pristine
+        # copy (outside the events), so every step computes on the recipe.
+        total_ms, done, wall = 0.0, 0, 0.0
+        while done < args.steps:
+            n = min(len(sets), args.steps - done)
+            for i in range(n):
+                restore(i)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            wall0 = time.perf_counter()
+            a.record(stream)
+            for i in range(n):
+                step(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - wall0
+            total_ms += a.elapsed_time(b)
+            done += n
+        ms_per_step = total_ms / args.steps
+        timing = (f"rounds of up to {len(sets)} back-to-back steps (one per buffer set) between "
+                  "two events; logits restored from pristine copies before each round, outside "
+                  "the events")
+        for i in range(min(20, len(sets))):
             restore(i)
-            ev[i][0].record(stream)
-            step(i)
-            ev[i][1].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        per_step = [a.elapsed_time(b) for a, b in ev]
-        ms_per_step = sum(per_step) / len(per_step)
-        timing = ("per-step events; logits restored from a pristine copy before each step, "
-                  "outside the events")
-        per_call_ms = sorted(per_step)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(20, len(sets)))]
+        for i, (a, b) in enumerate(ev):
+            a.record(stream)
+            step(i)
+            b.record(stream)
+        torch.cuda.synchronize()
+        per_call_ms = sorted(a.elapsed_time(b) for a, b in ev)
     else:
         t_start = torch.cuda.Event(enable_timing=True)
         t_end = torch.cuda.Event(enable_timing=True)

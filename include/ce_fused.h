@@ -62,7 +62,9 @@ typedef enum ce_status {
   CE_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
   CE_ERR_ALIAS = 3,        /* grad_out overlaps logits other than exactly in place */
   CE_ERR_WORKSPACE = 4,    /* workspace missing or smaller than ce_workspace_bytes() */
-  CE_ERR_HIP = 5           /* a HIP runtime call failed */
+  CE_ERR_HIP = 5,          /* a HIP runtime call failed */
+  CE_ERR_TIMEOUT = 6       /* CE_FLAG_VALIDATE only: a two-workgroup fp32 row gave up
+                              waiting for its other half (that row's outputs are NaN) */
 } ce_status;
 
 /* Divide row r's gradient scale by the number of rows that carry r's segment
@@ -76,7 +78,15 @@ typedef enum ce_status {
  * returns CE_ERR_INVALID_ARG, with nothing else enqueued, if any check fails.
  * Without the flag an out-of-range target gives a NaN row and unsorted ids
  * are undefined. The scan's per-block results take 4096 bytes of workspace
- * (counted by ce_workspace_bytes). */
+ * (counted by ce_workspace_bytes). A gradient call on fp32 rows of
+ * 102404..204803 columns (two workgroups per row, which exchange their
+ * halves' statistics through the workspace with a bounded wait) also waits
+ * for its kernels and returns CE_ERR_TIMEOUT if any half row stopped waiting
+ * for its partner; such rows are NaN. The wait ends only when something
+ * outside the call holds the partner workgroup off the GPU for well over
+ * 0.1 s. Environment variable CE_PAIR_SPIN_LIMIT, when set to a number up
+ * to 2097152, replaces that wait's poll limit (0: no wait at all, every such
+ * row NaN); a test hook. */
 #define CE_FLAG_VALIDATE 0x2u
 
 /* Shape and options of one call. */
@@ -93,10 +103,13 @@ typedef struct ce_problem {
 } ce_problem;
 
 /* Device workspace (bytes) a call with this problem needs: room for a [T]
- * float NLL staging array and [S+1] segment offsets when S > 0; for fp32
- * logits of more than 65536 columns, 32 bytes per row for the two-workgroup
- * row mode of the gradient pass (its per-row exchange slots); plus 4096
- * bytes under CE_FLAG_VALIDATE; zero otherwise. This is what a call that
+ * float NLL staging array and [S+1] segment offsets when S > 0; for the
+ * gradient pass's row scheduling, 256 bytes (a ticket counter) when rows
+ * hold 8193..25600 16-byte chunks (bf16: 65544..204807 columns, fp32:
+ * 32772..102403), and for fp32 logits of 102404..204803 columns (two
+ * workgroups per row) 32 bytes per row plus 8 (the counter and a give-up
+ * count); plus 4096 bytes
+ * under CE_FLAG_VALIDATE; zero otherwise. This is what a call that
  * writes a gradient needs; a forward-only call (grad_out NULL, or
  * ce_fused_forward) needs no exchange slots, so it accepts a workspace
  * smaller by those bytes. Returns 0 for a null or invalid problem. */
@@ -171,10 +184,10 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p,
  *  Returns CE_ERR_WORKSPACE when the call would need more than
  *  CE_NOALLOC_SCRATCH_BYTES (ce_workspace_bytes(p) for a gradient call; less
  *  without a gradient): with S segments, 4 T + 4 (S + 1) bytes (each rounded
- *  up to 256); for fp32 logits past 65536 columns with a gradient, 32 T
- *  bytes more; 4096 more under CE_FLAG_VALIDATE. That is up to about 2
- *  million rows with segments, or 262144 rows of the two-workgroup fp32
- *  mode. CE_ERR_INVALID_ARG when the stream belongs to another device than
+ *  up to 256); with a gradient, 256 bytes for rows of 8193..25600 16-byte
+ *  chunks, or 32 T + 8 bytes for the two-workgroup fp32 rows; 4096 more
+ *  under CE_FLAG_VALIDATE. That is up to about 2 million rows with
+ *  segments, or 262143 rows of the two-workgroup fp32 mode. CE_ERR_INVALID_ARG when the stream belongs to another device than
  *  the current one.
  *  Every call on one GPU shares that GPU's array and leaves the last call's
  *  contents in it: two calls that may run at the same time on one GPU (on

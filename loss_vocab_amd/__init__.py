@@ -94,7 +94,10 @@ def ce_fused_fwd_bwd(logits, targets, mask, segment_ids, z_alpha, grad_scale,
     stream). ``validate`` sets CE_FLAG_VALIDATE: a device scan of the targets
     and segment ids, after which the call waits for the stream and raises
     CeError(CE_ERR_INVALID_ARG) before writing anything if one is out of range
-    or the ids are unsorted. Raises CeError on a non-OK status.
+    or the ids are unsorted; on fp32 rows of 102404..204803 columns (two
+    workgroups per row) it also waits for the kernels and raises
+    CeError(CE_ERR_TIMEOUT) if a half row gave up waiting for its partner.
+    Raises CeError on a non-OK status.
     """
     p = make_problem(logits, grad_out, num_segments=num_segments,
                      segment_mean=segment_mean, ignore_index=ignore_index, validate=validate)
@@ -299,10 +302,12 @@ def shard_bounds(V, num_shards, align=8):
 
 def ce_split(logits, targets, *, shards=2, mask=None, segment_ids=None, num_segments=0,
              z_alpha=0.0, grad_scale=1.0, segment_mean=False, grad_dtype=None, in_place=False,
-             align=8, row_weight=None, ignore_index=IGNORE_INDEX):
+             align=8, row_weight=None, ignore_index=IGNORE_INDEX, grad_out=None):
     """The split form on one device: the columns of ``logits`` cut into shards,
     statistics per shard, one finish, gradient per shard.
 
+    ``grad_out`` ([T, V], any row stride) receives the gradient when given
+    (otherwise a new tensor, or ``logits`` itself with ``in_place``).
     Returns ``(loss[T], grad[T, V], seg_loss[S] or None, row_state[T, 8])``.
     """
     T, V = logits.shape
@@ -318,7 +323,12 @@ def ce_split(logits, targets, *, shards=2, mask=None, segment_ids=None, num_segm
     ce_rows_finish(len(bounds), stats, targets, mask, segment_ids, z_alpha, loss, seg, row_state,
                    vocab=V, num_segments=num_segments, segment_mean=segment_mean,
                    ignore_index=ignore_index)
-    grad = logits if in_place else torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
+    if in_place:
+        grad = logits
+    elif grad_out is not None:
+        grad = grad_out
+    else:
+        grad = torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
     for a, b in bounds:
         ce_shard_grad(logits[:, a:b], targets, row_state, grad_scale, grad[:, a:b], v0=a,
                       row_weight=row_weight, ignore_index=ignore_index)

@@ -21,6 +21,7 @@ CE_ERR_UNSUPPORTED = 2
 CE_ERR_ALIAS = 3
 CE_ERR_WORKSPACE = 4
 CE_ERR_HIP = 5
+CE_ERR_TIMEOUT = 6
 
 CE_FLAG_SEGMENT_MEAN = 0x1
 CE_FLAG_VALIDATE = 0x2

@@ -29,6 +29,11 @@ HIP_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-mllvm", "-disable-machine-licm",
+    # Atomic read-modify-writes stay single-lane operations: the wave-level
+    # rewrite would read each result right after issuing it, and on gfx9 that
+    # wait drains every earlier load and store of the wave (one in-order
+    # counter) -- a row-resident workgroup's ticket would hold up its row.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -35,6 +35,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -214,6 +215,11 @@ struct RowParams {
   // [0, pair_split) are half 0, [pair_split, V) half 1
   uint32_t* pair_part;
   int64_t pair_split;
+  uint32_t pair_spin;        // polls of a partner's words before giving up
+  // row-resident kernel: tickets[0] is the counter that deals out rows (pair
+  // mode: half rows); pair mode: tickets[1] counts the half rows that ended
+  // without their partner's statistics. Both start at all-ones.
+  uint32_t* tickets;
 };
 
 // What a row-kernel launch does.
@@ -230,8 +236,10 @@ enum RowMode : int {
 //   [4] segment factor (1 / length, or 1)   [5] kind
 //   [6] lse log2(e) - [0] (the rounding residue of [0])   [7] zero
 constexpr int kRowState = 8;
-// Pair mode: polls of a partner's flag (each after s_sleep 2, ~128 cycles)
-// before the wait is given up (~0.1 s).
+// Pair mode: polls of a partner's words (each an L2 round trip plus
+// s_sleep 2) before the wait is given up, well over 0.1 s. The partner of a
+// waiting half is always resident and publishes before it waits, so the
+// limit only ends waits that something outside the kernel stalls.
 constexpr uint32_t kPairSpin = 1u << 21;
 constexpr float kRowValid = 0.f, kRowIgnored = 1.f, kRowPoisoned = 2.f;
 
@@ -553,8 +561,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
                 "the entropy variant is a forward with streamed or LDS-staged slots");
   static_assert(MODE != kGrad || (NRES + NRAW + NLDS == 0 && WRITE), "gradient mode streams");
   static_assert(MODE != kStats || !WRITE, "statistics mode writes no gradient");
-  static_assert(MODE != kPair || (WRITE && !ENT), "pair mode is the fused call");
-  constexpr bool PAIR = MODE == kPair;
+  static_assert(MODE != kPair, "two workgroups per row: the row-resident kernel");
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
   constexpr uint32_t OB = W * Elem<TO>::BYTES;     // gradient bytes per chunk
   constexpr int NON = NRES + NRAW + NLDS;          // on-chip slots per thread
@@ -568,17 +575,10 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
   const uint32_t wid = tid >> 6;
-  // Pair mode: blocks b and b + 8 (same XCD, same L2) take the two halves of
-  // one row; half 0 holds columns [0, pair_split), half 1 the rest.
-  const uint32_t half = PAIR ? (blockIdx.x >> 3) & 1u : 0u;
-  const int64_t row0 = PAIR ? static_cast<int64_t>(blockIdx.x >> 4) * 8 + (blockIdx.x & 7u)
-                            : static_cast<int64_t>(blockIdx.x);
-  const int64_t row_step = PAIR ? gridDim.x / 2 : gridDim.x;
-  const int64_t c0 = (PAIR && half) ? p.pair_split : 0;
-  [[maybe_unused]] __shared__ float pair_sh[2][4];
-  [[maybe_unused]] bool pair_broken = false;   // thread 0: a partner once failed to arrive
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x);
+  const int64_t row_step = gridDim.x;
   // In-row offsets are 32-bit (the host bounds a row below 2 GiB).
-  const uint32_t V = static_cast<uint32_t>(PAIR ? (half ? p.V - p.pair_split : p.pair_split) : p.V);
+  const uint32_t V = static_cast<uint32_t>(p.V);
   const uint32_t nchunk = V / W;
   const uint32_t clast = nchunk > 0 ? nchunk - 1 : 0;
   const uint32_t tail_begin = nchunk * W;
@@ -603,13 +603,10 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
   for (int64_t r = row0; r < p.T; r += row_step, par ^= 1) {
     const int64_t t64 = t_next;
     if (r + row_step < p.T) t_next = labels[r + row_step];
-    void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes + c0 * Elem<TO>::BYTES
-                       : nullptr;
+    void* grow = WRITE ? static_cast<char*>(p.grad) + r * out_row_bytes : nullptr;
     // The target's column within these rows (t_local = V: not among them).
-    const int64_t tl = t64 - p.v0 - c0;
+    const int64_t tl = t64 - p.v0;
     const bool owned = tl >= 0 && tl < static_cast<int64_t>(V);
-    // Whether the target lies in the row at all (in pair mode, in either half).
-    const bool in_row = PAIR ? (t64 - p.v0 >= 0 && t64 - p.v0 < p.V) : owned;
     RowOut saved{};
     if constexpr (MODE == kGrad) {
       // The saved state says whether the row is ignored (+0.0), poisoned
@@ -633,18 +630,16 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
           }
           continue;
         }
-      } else if (!valid || !in_row) {
+      } else if (!valid || !owned) {
         // Ignored row: +0.0 everywhere, logits never read. Valid row with an
-        // out-of-range target: NaN loss and gradient row. (Both halves of a
-        // pair decide alike; half 0 writes the row's loss.)
-        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE,
-                            !PAIR || half == 0);
+        // out-of-range target: NaN loss and gradient row.
+        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, WRITE);
         continue;
       }
     }
 
     const uint32_t t = owned ? static_cast<uint32_t>(tl) : V;
-    const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes + c0 * Elem<TI>::BYTES;
+    const void* zrow = static_cast<const char*>(p.logits) + r * in_row_bytes;
     const float zt = (MODE != kGrad && owned) ? Elem<TI>::load1(zrow, t) : kNegInf;
     const __amdgpu_buffer_rsrc_t rin =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(zrow), 0, nchunk * 16u, kBufWord3);
@@ -909,59 +904,6 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       }
       continue;
     }
-    float ztm = zt;   // the row's target logit (pair mode: from whichever half holds it)
-    if constexpr (PAIR) {
-      // Publish this half's partial, then take the partner's. Each half's slot
-      // is two 64-bit words, (shift, sum) and (target logit, 0), filled with
-      // all-ones before the launch; each word is stored and polled as one
-      // relaxed device-scope atomic, so a word that differs from all-ones is
-      // complete and no fence is needed (a fence at device scope would write
-      // back and invalidate this XCD's L2, which pass 2 re-reads from). The
-      // merge is symmetric, so both halves hold the same row statistics. A
-      // partner that never arrives (it cannot: the launch is cooperative)
-      // gives a NaN row after a bounded wait instead of a hang.
-      uint64_t* slot = reinterpret_cast<uint64_t*>(p.pair_part) + 4 * r;
-      if (tid == 0) {
-        const uint64_t ms = (static_cast<uint64_t>(__float_as_uint(s)) << 32) | __float_as_uint(mL);
-        __hip_atomic_store(slot + 2 * half, ms, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(slot + 2 * half + 1, static_cast<uint64_t>(__float_as_uint(zt)),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        float pm = __builtin_nanf(""), ps = __builtin_nanf(""), pz = __builtin_nanf("");
-        if (!pair_broken) {
-          uint64_t w0 = ~0ull, w1 = ~0ull;
-          uint32_t n = 0;
-          while (n < kPairSpin) {
-            if (w0 == ~0ull)
-              w0 = __hip_atomic_load(slot + 2 * (half ^ 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (w1 == ~0ull)
-              w1 = __hip_atomic_load(slot + 2 * (half ^ 1u) + 1, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-            if (w0 != ~0ull && w1 != ~0ull) break;
-            __builtin_amdgcn_s_sleep(2);
-            ++n;
-          }
-          if (n < kPairSpin) {
-            pm = __uint_as_float(static_cast<uint32_t>(w0));
-            ps = __uint_as_float(static_cast<uint32_t>(w0 >> 32));
-            pz = __uint_as_float(static_cast<uint32_t>(w1));
-          } else {
-            pair_broken = true;
-          }
-        }
-        pair_sh[par][0] = pm;
-        pair_sh[par][1] = ps;
-        pair_sh[par][2] = pz;
-      }
-      __syncthreads();
-      const float pm = pair_sh[par][0], ps = pair_sh[par][1], pz = pair_sh[par][2];
-      if (pm != pm) {
-        mL = __builtin_nanf("");
-        s = __builtin_nanf("");
-      } else {
-        merge(mL, s, pm, ps);
-      }
-      ztm = fmaxf(zt, pz);
-    }
     RowOut o;
     [[maybe_unused]] const double seg_f = 1.0 / static_cast<double>(seg_len);
     if constexpr (MODE == kGrad) {
@@ -970,7 +912,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       // Wave 0 alone runs the fp64 epilogue; the others wait at the barrier,
       // leaving the SIMDs to other workgroups.
       if (wid == 0) {
-        o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0), seg_f);
+        o = row_epilogue(p, r, mL, s, zt, tid == 0, seg_f);
         if (lane == 0) {
           epi[par][0] = o.g_t;
           epi[par][1] = o.cnt;
@@ -986,7 +928,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       o.cnt = epi[par][1];
       o.kl = epi[par][2];
     } else {
-      o = row_epilogue(p, r, mL, s, ztm, tid == 0 && (!PAIR || half == 0), seg_f);
+      o = row_epilogue(p, r, mL, s, zt, tid == 0, seg_f);
       if constexpr (ENT) {
         if (tid == 0) p.ent_out[r] = row_entropy(mL, s, hs, zt);
       }
@@ -1113,18 +1055,32 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 // straight from HBM -- so every logit is read from HBM exactly once (the
 // streamed-tier kernel re-reads what does not fit). Slot i of thread tid is
 // chunk i * 1024 + tid. All of a row's loads go out at its start, so pass 1
-// reduces slots as they land. (Issuing the next row's slots during this
+// reduces slots as they land: the row takes no other load whose value is
+// needed early (the target logit comes from the lane whose slot holds it),
+// since on gfx9 waiting for one load waits for every load issued before it. (Issuing the next row's slots during this
 // row's gradient pass measured slower: it moves every read into the
 // gradient pass and leaves pass 1 with no memory traffic of its own.)
+//
+// Rows are dealt out by a ticket counter in the workspace (all-ones before
+// the launch, so the first ticket is 0): a workgroup that finishes early
+// takes more rows, which evens out rows of unequal cost (ignored rows are
+// only written). In pair mode (fp32 rows too long for one workgroup's chip
+// space) the two halves of row r are tickets 2r and 2r + 1, and a
+// workgroup takes its next ticket only after its current half has exchanged
+// statistics with its partner. That makes the waits deadlock-free without
+// co-residency guarantees: a waiting half's partner ticket is either held
+// by a running workgroup, which publishes before it waits, or is the newest
+// ticket, taken by the next workgroup to finish a half -- so any two
+// resident workgroups make progress. (The wait is bounded all the same; a
+// partner that never comes gives a NaN row.)
 //
 // Register discipline: every per-slot test compares the slot index with the
 // end slot `se` or the target's slot `st`, both re-read through an empty asm
 // at each use, and the lane index is re-derived every row, so the compiler
 // keeps a few scalars live instead of a lane mask or offset per slot. In the
 // end slot, lanes past the row end load the last chunk again (in bounds),
-// count as -inf and store nothing; register slots past the end slot load the
-// last chunk (one line per wave) and are not reduced or stored; LDS slots
-// past it are not loaded.
+// count as -inf and store nothing; slots past the end slot load the last
+// chunk (one line per wave) and are not reduced or stored.
 // ---------------------------------------------------------------------------
 template <typename TI, typename TO, int NREG, int NLDS, int MODE>
 __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
@@ -1139,46 +1095,80 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
   __shared__ u32x4 stage[NLDS > 0 ? NLDS : 1][BLOCK];
   __shared__ float epi[2][4];
   [[maybe_unused]] __shared__ float pair_sh[2][4];
+  [[maybe_unused]] __shared__ uint32_t tick_sh[2];
+  __shared__ float zt_sh[2];   // the row's target logit, from the lane that holds it
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
   const uint32_t wid = tid >> 6;
-  const uint32_t half = PAIR ? (blockIdx.x >> 3) & 1u : 0u;
-  const int64_t row0 = PAIR ? static_cast<int64_t>(blockIdx.x >> 4) * 8 + (blockIdx.x & 7u)
-                            : static_cast<int64_t>(blockIdx.x);
-  const int64_t row_step = PAIR ? gridDim.x / 2 : gridDim.x;
-  const int64_t c0 = (PAIR && half) ? p.pair_split : 0;
-  [[maybe_unused]] bool pair_broken = false;
-  const uint32_t V = static_cast<uint32_t>(PAIR ? (half ? p.V - p.pair_split : p.pair_split) : p.V);
-  const uint32_t nchunk = V / W;
-  const uint32_t c16_last = (nchunk > 0 ? nchunk - 1 : 0) * 16u;
-  const uint32_t tail_begin = nchunk * W;
   const size_t in_row_bytes = static_cast<size_t>(p.ld_in) * Elem<TI>::BYTES;
   const size_t out_row_bytes = static_cast<size_t>(p.ld_out) * Elem<TO>::BYTES;
   const uint32_t neg_w = Elem<TI>::NEG_INF_WORD;
   const kconst_i64* labels = (const kconst_i64*)p.targets;
   const kconst_i32* seg_ids = (const kconst_i32*)p.seg_ids;
   const kconst_i32* seg_start = (const kconst_i32*)p.seg_start;
-  // The slot that holds the row's last chunk (-1: no whole chunk).
-  const int se_row = nchunk > 0 ? static_cast<int>((nchunk - 1) / BLOCK) : -1;
-  auto end_slot = [&]() -> int {
-    int se = __builtin_amdgcn_readfirstlane(se_row);
-    asm volatile("" : "+s"(se));
-    return se;
+  [[maybe_unused]] bool pair_broken = false;     // thread 0: a partner once failed to arrive
+  // The counter starts at all-ones: a ticket is the value returned plus one,
+  // added where the value is read back (using the return value right away
+  // would make the wave wait for it, and with it every earlier access).
+  auto take_ticket = [&]() -> uint32_t {
+    return __hip_atomic_fetch_add(p.tickets, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto read_ticket = [&](uint32_t i) -> uint32_t {
+    return __builtin_amdgcn_readfirstlane(tick_sh[i]) + 1u;
+  };
+  auto ticket_row = [&](uint32_t tk) -> int64_t {
+    return static_cast<int64_t>(PAIR ? tk >> 1 : tk);
   };
 
-  int64_t t_next = row0 < p.T ? labels[row0] : 0;
+  // Ticket k is row k (pair mode: row k / 2, half k % 2). Thread 0 takes
+  // the next ticket while the current row is in flight (whole rows: right
+  // after the row's loads go out; pair mode: once the half's exchange is
+  // done, which keeps the pairing deadlock-free) and shares it through LDS
+  // at the one barrier every row passes after its last use of the previous
+  // value. Tickets are read back as scalars, so the row index and all that
+  // derives from it stay uniform. (Measured against a static grid stride
+  // and against tickets taken two rows ahead: dealing rows one ahead was
+  // the fastest on the 201088-column bf16 rows and level with the best on
+  // the others.)
+  if (tid == 0) tick_sh[0] = take_ticket();
+  __syncthreads();
+  uint32_t k = read_ticket(0);
+  __syncthreads();                                // tick_sh[0] is rewritten by the first row
+  int64_t r = ticket_row(k);
+  int64_t t_next = r < p.T ? labels[r] : 0;
   int par = 0;
-  for (int64_t r = row0; r < p.T; r += row_step, par ^= 1) {
+  while (r < p.T) {
+    const uint32_t half = PAIR ? (k & 1u) : 0u;
     const int64_t t64 = t_next;
-    if (r + row_step < p.T) t_next = labels[r + row_step];
+    // this row's (half row's) geometry
+    const int64_t c0 = (PAIR && half) ? p.pair_split : 0;
+    const uint32_t V = static_cast<uint32_t>(PAIR ? (half ? p.V - p.pair_split : p.pair_split) : p.V);
+    const uint32_t nchunk = V / W;
+    const uint32_t c16_last = (nchunk > 0 ? nchunk - 1 : 0) * 16u;
+    const uint32_t tail_begin = nchunk * W;
+    // the slot that holds the (half) row's last chunk (-1: no whole chunk)
+    const int se_row = nchunk > 0 ? static_cast<int>((nchunk - 1) / BLOCK) : -1;
+    auto end_slot = [&]() -> int {
+      int se = __builtin_amdgcn_readfirstlane(se_row);
+      asm volatile("" : "+s"(se));
+      return se;
+    };
     void* grow = static_cast<char*>(p.grad) + r * out_row_bytes + c0 * Elem<TO>::BYTES;
     const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
     if (!valid || t64 - p.v0 < 0 || t64 - p.v0 >= p.V) {
       // Ignored row: +0.0 everywhere, logits never read. Valid row with an
       // out-of-range target: NaN loss and gradient row. (Both halves of a
       // pair decide alike; half 0 writes the row's loss.)
+      uint32_t kn = 0;
+      if (tid == 0) kn = take_ticket();
       fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true, !PAIR || half == 0);
+      if (tid == 0) tick_sh[par] = kn;
+      __syncthreads();
+      k = read_ticket(par);
+      r = ticket_row(k);
+      t_next = r < p.T ? labels[r] : 0;
+      par ^= 1;
       continue;
     }
     const int64_t tl = t64 - p.v0 - c0;
@@ -1200,18 +1190,20 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       for (int i = 0; i < NREG; ++i)
         raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rin, min(vin + i * SLOT, c16_last), 0, kNT);
     }
+    // (every LDS slot is loaded, those past the end slot from the last chunk:
+    // loads on only some paths would make the first slot's wait cover them)
 #pragma unroll
     for (int j = 0; j < NLDS; ++j) {
-      if (NREG + j > end_slot()) break;
       // HBM -> LDS without a register round trip: lane l of a wave lands
       // at base + 16 l, so slot j of thread tid is stage[j][tid].
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(zrow + min(vin + (NREG + j) * SLOT, c16_last)),
           (__attribute__((address_space(3))) void*)(&stage[j][tid_r & ~63u]), 16, 0, kNT);
     }
-    const float zt = owned ? Elem<TI>::load1(zrow, t) : kNegInf;
     [[maybe_unused]] int32_t sid = 0;
     if (p.seg_mean) sid = seg_ids[r];
+    uint32_t k_next = 0;                           // thread 0: the next ticket
+    if (!PAIR && tid == 0) k_next = take_ticket();
 
     // Where the target sits: chunk ct, element kt, slot st, lane `mine`.
     const uint32_t ct = t / W;
@@ -1228,7 +1220,9 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       return st;
     };
     // Lanes past the row end (in the end slot) count as -inf; the target's
-    // element in its slot too (in the one lane that holds it).
+    // element in its slot too (in the one lane that holds it, which first
+    // hands its value to the row through LDS: the target logit takes no load
+    // of its own, whose early wait would hold pass 1 until every slot landed).
     auto fixed = [&](u32x4 v, int slot) -> u32x4 {
       if (slot == end_slot()) {
         const bool out = static_cast<uint32_t>(slot) * BLOCK + tid_r >= nchunk;
@@ -1238,6 +1232,10 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
         v.w = out ? neg_w : v.w;
       }
       if (slot == tgt_slot()) {
+        if (mine) {
+          const uint32_t w = kq == 0 ? v.x : (kq == 1 ? v.y : (kq == 2 ? v.z : v.w));
+          zt_sh[par] = Elem<TI>::BYTES == 4 ? __uint_as_float(w) : __uint_as_float((w >> ksh) << 16);
+        }
         const uint32_t am = mine ? ~kmask : ~0u, om = mine ? kput : 0u;
         v.x = kq == 0 ? (v.x & am) | om : v.x;
         v.y = kq == 1 ? (v.y & am) | om : v.y;
@@ -1277,16 +1275,25 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
     }
     if (tid_r < V - tail_begin) {
       const uint32_t j = tail_begin + tid_r;
-      const float xv = (j == t) ? kNegInf : Elem<TI>::load1(zrow, j);
+      float xv = Elem<TI>::load1(zrow, j);
+      if (j == t) {
+        zt_sh[par] = xv;
+        xv = kNegInf;
+      }
       merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
     }
     block_reduce<BLOCK>(mL, s, red_m, red_s, par, tid_r & 63u, tid_r >> 6);
+    const float zt = owned ? zt_sh[par] : kNegInf;   // written before the barrier above
 
     float ztm = zt;
     if constexpr (PAIR) {
-      // Exchange with the partner half as the pair-mode row kernel does:
-      // two self-validating 64-bit words per half, relaxed device-scope
-      // atomics, a bounded wait that gives a NaN row instead of a hang.
+      // Publish this half's partial, then take the partner's. Each half's
+      // slot is two 64-bit words, (shift, sum) and (target logit, 0), filled
+      // with all-ones before the launch; each word is stored and polled as
+      // one relaxed device-scope atomic, so a word that differs from all-ones
+      // is complete and no fence is needed. The merge is symmetric, so both
+      // halves hold the same row statistics. The next ticket is taken once
+      // the partner has been heard from (or given up on).
       uint64_t* slot = reinterpret_cast<uint64_t*>(p.pair_part) + 4 * r;
       if (tid == 0) {
         const uint64_t ms = (static_cast<uint64_t>(__float_as_uint(s)) << 32) | __float_as_uint(mL);
@@ -1297,7 +1304,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
         if (!pair_broken) {
           uint64_t w0 = ~0ull, w1 = ~0ull;
           uint32_t n = 0;
-          while (n < kPairSpin) {
+          while (n < p.pair_spin) {
             if (w0 == ~0ull)
               w0 = __hip_atomic_load(slot + 2 * (half ^ 1u), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (w1 == ~0ull)
@@ -1307,7 +1314,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
             __builtin_amdgcn_s_sleep(2);
             ++n;
           }
-          if (n < kPairSpin) {
+          if (n < p.pair_spin) {
             pm = __uint_as_float(static_cast<uint32_t>(w0));
             ps = __uint_as_float(static_cast<uint32_t>(w0 >> 32));
             pz = __uint_as_float(static_cast<uint32_t>(w1));
@@ -1315,6 +1322,9 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
             pair_broken = true;
           }
         }
+        if (pair_broken)   // counted, and reported by a validating call
+          __hip_atomic_fetch_add(p.tickets + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        k_next = take_ticket();
         pair_sh[par][0] = pm;
         pair_sh[par][1] = ps;
         pair_sh[par][2] = pz;
@@ -1329,9 +1339,10 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       }
       ztm = fmaxf(zt, pz);
     }
-    // Wave 0 runs the fp64 epilogue and shares the row factors through LDS.
-    // (Its scalar inputs pass an empty asm, so their fp64 forms are made
-    // here, not hoisted out of the row loop into registers held throughout.)
+    // Wave 0 runs the fp64 epilogue and shares the row factors through LDS
+    // (with the next ticket, whose atomic has returned by then). The epilogue's scalar inputs pass an empty asm, so their fp64
+    // forms are made here, not hoisted out of the row loop into registers
+    // held throughout.
     if (wid == 0) {
       RowParams q = p;
       asm volatile("" : "+s"(q.grad_scale), "+s"(q.z_alpha));
@@ -1341,10 +1352,14 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
         epi[par][0] = o.g_t;
         epi[par][1] = o.cnt;
         epi[par][2] = o.kl;
+        tick_sh[par] = k_next;
       }
     }
     __syncthreads();
     const float cnt = epi[par][1], kl = epi[par][2];
+    k = read_ticket(par);
+    t_next = ticket_row(k) < p.T ? labels[ticket_row(k)] : 0;
+    const int64_t r_next = ticket_row(k);
 
     // ---- pass 2: gradient ----------------------------------------------
     const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(grow, 0, nchunk * OB, kBufWord3);
@@ -1357,7 +1372,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       Elem<TI>::unpack(v, x);
       float g[W];
 #pragma unroll
-      for (int k = 0; k < W; ++k) g[k] = cnt * fexp2(__builtin_fmaf(x[k], kL2E, -kl));
+      for (int e = 0; e < W; ++e) g[e] = cnt * fexp2(__builtin_fmaf(x[e], kL2E, -kl));
       if (slot == end_slot() && static_cast<uint32_t>(slot) * BLOCK + tid_r >= nchunk) return;
       const uint32_t vo = vout + static_cast<uint32_t>(slot) * BLOCK * OB;
       if constexpr (Elem<TO>::BYTES == 2 && W == 8) {
@@ -1398,6 +1413,8 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
     // The next row's HBM -> LDS copies overwrite the staging slots: every
     // LDS read of them by this wave must have returned first.
     if constexpr (NLDS > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    r = r_next;
+    par ^= 1;
   }
 }
 
@@ -1592,12 +1609,6 @@ __global__ __launch_bounds__(256) void ce_fill_u32_kernel(uint32_t* __restrict__
     p[i] = v;
 }
 
-// Pair mode for long rows: the long-row shape on half rows, two workgroups
-// of one XCD per row. The launch is cooperative (every workgroup resident, so
-// a partner always arrives) on a grid of whole XCD pairs; when the runtime
-// refuses it, or the stream is being captured into a graph (whose replay
-// need not keep the co-residency a cooperative launch guarantees), the
-// whole-row kernel runs instead.
 #ifndef CE_ROWRES
 #define CE_ROWRES 1
 #endif
@@ -1608,50 +1619,44 @@ constexpr bool rowres_off() { return CE_ROWRES == 0; }
 constexpr int kResReg = 16, kResLds = 9;
 constexpr int64_t kResChunks = int64_t{kResReg + kResLds} * 1024;
 
+// Whole rows on the row-resident kernel: the ticket counter is set to
+// all-ones by a one-block fill kernel (capturable), then one workgroup per CU.
 template <typename TI, typename TO>
 ce_status launch_rowres(const RowParams& rp, hipStream_t stream) {
+  if (rp.tickets == nullptr) return CE_ERR_WORKSPACE;
+  hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(1), dim3(256), 0, stream, rp.tickets, int64_t{1}, ~0u);
+  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   static std::atomic<int> occ{0};
   return launch_persistent(ce_rowres_kernel<TI, TO, kResReg, kResLds, kFused>, 1024, occ, rp,
                            stream, 64);
 }
 
+// Pair mode: fp32 rows of 25601..51200 chunks, two workgroups per row, each
+// holding its half row on chip (the row-resident kernel's pair mode). The
+// exchange slots and the ticket counter are filled with all-ones first (a
+// kernel, so the call stays capturable in a graph). An ordinary launch: the
+// ticket order needs no co-residency guarantee beyond two resident
+// workgroups.
 template <typename TI, typename TO>
 ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) {
-    (void)hipGetLastError();
-    cap = hipStreamCaptureStatusActive;
-  }
-  if (cap != hipStreamCaptureStatusNone)
-    return launch_rows<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1>(rp, stream, 64);
-  // Half rows that fit on chip take the row-resident kernel.
-  const bool res = (rp.V - rp.pair_split) / Elem<TI>::VEC <= kResChunks && !rowres_off();
-  const void* kern = res ? reinterpret_cast<const void*>(
-                               ce_rowres_kernel<TI, TO, kResReg, kResLds, kPair>)
-                         : reinterpret_cast<const void*>(
-                               ce_rows_kernel<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1, kPair>);
-  static std::atomic<int> occ_res{0}, occ_rows{0};
-  std::atomic<int>& occ = res ? occ_res : occ_rows;
+  auto kern = ce_rowres_kernel<TI, TO, kResReg, kResLds, kPair>;
+  static std::atomic<int> occ{0};
   int per_cu = occ.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 1024, 0) != hipSuccess)
-      per_cu = 0;
-    occ.store(per_cu > 0 ? per_cu : -1, std::memory_order_relaxed);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 1024, 0) != hipSuccess ||
+        per_cu <= 0)
+      return CE_ERR_HIP;
+    occ.store(per_cu, std::memory_order_relaxed);
   }
-  const int64_t grid = static_cast<int64_t>(device_cus()) * (per_cu > 0 ? per_cu : 0) / 16 * 16;
-  if (grid >= 16) {
-    const int64_t n = 8 * rp.T;
-    const unsigned nb = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024));
-    hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(nb), dim3(256), 0, stream, rp.pair_part, n, ~0u);
-    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
-    RowParams arg = rp;
-    void* args[] = {&arg};
-    if (hipLaunchCooperativeKernel(kern, dim3(static_cast<unsigned>(grid)), dim3(1024), args, 0,
-                                   stream) == hipSuccess)
-      return CE_OK;
-    (void)hipGetLastError();
-  }
-  return launch_rows<TI, TO, 1024, 0, 4, 9, 4, true, true, true, 1>(rp, stream, 64);
+  const int cus = device_cus();
+  if (cus <= 0) return CE_ERR_HIP;
+  const int64_t grid = std::max<int64_t>(2, std::min<int64_t>(2 * rp.T, int64_t{cus} * per_cu));
+  const int64_t n = 8 * rp.T + 2;   // the slots, the ticket counter, the give-up count
+  const unsigned nb = static_cast<unsigned>(std::min<int64_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(nb), dim3(256), 0, stream, rp.pair_part, n, ~0u);
+  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(1024), 0, stream, rp);
+  return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
 }
 
 template <typename TI, typename TO, bool WRITE, int MODE = kFused, bool ENT = false>
@@ -1679,14 +1684,14 @@ ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   if (nchunk <= 8192) return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
   if constexpr (WRITE) {
     if (nchunk <= kResChunks && !rowres_off()) return launch_rowres<TI, TO>(rp, stream);
+    // fp32 rows up to twice that: two workgroups per row, each half on chip
+    // (the host sets pair_part exactly for those rows)
+    if constexpr (Elem<TI>::BYTES == 4) {
+      if (rp.pair_part != nullptr && !rowres_off()) return launch_rows_pair<TI, TO>(rp, stream);
+    }
   }
   if (nchunk <= 16384)
     return launch_rows<TI, TO, 1024, 0, 0, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
-  if constexpr (WRITE && Elem<TI>::BYTES == 4) {
-    // fp32 rows this long: two workgroups per row keep twice the share of
-    // each row on chip (the whole half row up to 2 * 25600 chunks)
-    if (rp.pair_part != nullptr) return launch_rows_pair<TI, TO>(rp, stream);
-  }
   return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
 }
 
@@ -1825,13 +1830,35 @@ size_t segment_ws_bytes(const ce_problem* p) {
          align_up((static_cast<size_t>(p->num_segments) + 1) * sizeof(int32_t));
 }
 
-// fp32 rows of more than 16384 16-byte chunks run the gradient pass in pair
-// mode, which needs 32 bytes of exchange slots per row (placed after the
-// segment arrays). A forward-only call runs no pair mode and needs none.
-bool pair_rows(const ce_problem* p) { return p->logits_dtype == CE_DTYPE_F32 && p->V / 4 > 16384; }
-size_t pair_ws_bytes(const ce_problem* p, bool grad = true) {
-  if (!grad || !pair_rows(p)) return 0;
-  return align_up(static_cast<size_t>(p->T) * 8 * sizeof(uint32_t));
+// Row scheduling space of the gradient pass (placed after the segment
+// arrays): rows of 8193..25600 16-byte chunks run the row-resident kernel,
+// whose ticket counter takes 4 bytes; fp32 rows of 25601..51200 chunks run
+// its pair mode, with 32 bytes of exchange slots per row before the counter.
+// A forward-only call needs none.
+bool pair_rows(const ce_problem* p) {
+  const int64_t nchunk = p->V / 4;
+  return p->logits_dtype == CE_DTYPE_F32 && nchunk > kResChunks && nchunk - nchunk / 2 <= kResChunks;
+}
+
+// The pair mode's wait limit: kPairSpin, or CE_PAIR_SPIN_LIMIT from the
+// environment (a test hook: 0 makes every half row give up at once, which
+// forces the give-up path without stalling anything).
+uint32_t pair_spin_limit() {
+  const char* e = std::getenv("CE_PAIR_SPIN_LIMIT");
+  if (e == nullptr || *e == '\0') return kPairSpin;
+  char* end = nullptr;
+  const unsigned long v = std::strtoul(e, &end, 10);
+  return (end != nullptr && *end == '\0' && v <= kPairSpin) ? static_cast<uint32_t>(v) : kPairSpin;
+}
+bool rowres_rows(const ce_problem* p) {
+  const int64_t nchunk = p->V / (p->logits_dtype == CE_DTYPE_F32 ? 4 : 8);
+  return nchunk > 8192 && nchunk <= kResChunks;
+}
+size_t sched_ws_bytes(const ce_problem* p, bool grad = true) {
+  if (!grad || p->T == 0) return 0;
+  if (pair_rows(p)) return align_up(static_cast<size_t>(p->T) * 8 * sizeof(uint32_t) + 2 * sizeof(uint32_t));
+  if (rowres_rows(p)) return align_up(sizeof(uint32_t));
+  return 0;
 }
 size_t validate_ws_bytes(const ce_problem* p) {
   return (p->flags & CE_FLAG_VALIDATE) ? align_up(kValidateBlocks * sizeof(uint32_t)) : 0;
@@ -1899,7 +1926,7 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
   // Workspace: segment arrays, pair-mode slots (gradient calls only), the
   // debug scan's words, in that order.
   const bool grad = grad_out != nullptr;
-  const size_t need = segment_ws_bytes(p) + pair_ws_bytes(p, grad) + validate_ws_bytes(p);
+  const size_t need = segment_ws_bytes(p) + sched_ws_bytes(p, grad) + validate_ws_bytes(p);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return CE_ERR_WORKSPACE;
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0) return CE_ERR_WORKSPACE;
 
@@ -1908,7 +1935,7 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
   if ((p->flags & CE_FLAG_VALIDATE) && T > 0) {
     // Scan, wait, and refuse before anything else is enqueued.
     uint32_t* words = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p) +
-                                                  pair_ws_bytes(p, grad));
+                                                  sched_ws_bytes(p, grad));
     const int64_t nb = std::min<int64_t>(kValidateBlocks, (T + 255) / 256);
     (void)hipGetLastError();
     hipLaunchKernelGGL(ce_validate_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, stream,
@@ -1936,6 +1963,7 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   }
 
+  const uint32_t* gave_up = nullptr;   // pair mode's give-up count, when it runs
   if (T > 0) {
     RowParams rp{};
     rp.logits = logits;
@@ -1957,16 +1985,26 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
     rp.grad_scale = grad_scale;
     rp.lse_out = lse_out;
     rp.ent_out = ent_out;
-    if (grad_out && pair_rows(p)) {
-      rp.pair_part = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p));
-      rp.pair_split = (V / 4 / 2) * 4;   // a chunk boundary
-    }
-
     const bool vec_in = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) &&
                         ((p->ld_logits * bi) % 16 == 0);
     const bool vec_out = !grad_out || ((reinterpret_cast<uintptr_t>(grad_out) % 16 == 0) &&
                                        ((p->ld_grad * bo) % 16 == 0));
     const bool vec = vec_in && vec_out;
+    if (grad_out && sched_ws_bytes(p) > 0) {
+      uint32_t* sched = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p));
+      if (pair_rows(p)) {
+        // pair_part is set exactly when the pair kernel runs (aligned rows)
+        if (vec && !ent_out && !rowres_off()) {
+          rp.pair_part = sched;
+          rp.pair_split = (V / 4 / 2) * 4;   // a chunk boundary
+          rp.tickets = sched + 8 * T;
+          rp.pair_spin = pair_spin_limit();
+          gave_up = rp.tickets + 1;
+        }
+      } else {
+        rp.tickets = sched;
+      }
+    }
     (void)hipGetLastError();
     ce_status st;
     if (ent_out)
@@ -1983,6 +2021,15 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
     hipLaunchKernelGGL(ce_seg_sum_kernel, dim3(static_cast<unsigned>(S)), dim3(256), 0, stream,
                        nll_ws, seg_start, S, seg_loss_out);
     if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  }
+  if ((p->flags & CE_FLAG_VALIDATE) && gave_up != nullptr) {
+    // Two-workgroup rows: wait, and report half rows that gave up on their
+    // partner (the count word starts at all-ones).
+    uint32_t host = 0;
+    if (hipMemcpyAsync(&host, gave_up, sizeof(host), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return CE_ERR_HIP;
+    if (host != ~0u) return CE_ERR_TIMEOUT;
   }
   return CE_OK;
 }
@@ -2032,7 +2079,7 @@ ce_status ce_fused_fwd_bwd_noalloc(const ce_problem* p, const void* logits,
                                    float* lse_out, void* stream_ptr) {
   if (p == nullptr || p->T < 0 || p->num_segments < 0) return CE_ERR_INVALID_ARG;
   // What ce_fused_fwd_bwd would ask of a workspace, against the fixed size.
-  const size_t need = segment_ws_bytes(p) + pair_ws_bytes(p, grad_out != nullptr) +
+  const size_t need = segment_ws_bytes(p) + sched_ws_bytes(p, grad_out != nullptr) +
                       validate_ws_bytes(p);
   if (need > CE_NOALLOC_SCRATCH_BYTES) return CE_ERR_WORKSPACE;
   void* ws = nullptr;
@@ -2057,7 +2104,7 @@ ce_status ce_fused_fwd_bwd_noalloc(const ce_problem* p, const void* logits,
 
 size_t ce_workspace_bytes(const ce_problem* p) {
   if (p == nullptr || p->T < 0 || p->num_segments < 0) return 0;
-  return segment_ws_bytes(p) + pair_ws_bytes(p) + validate_ws_bytes(p);
+  return segment_ws_bytes(p) + sched_ws_bytes(p) + validate_ws_bytes(p);
 }
 
 const char* ce_status_string(int status) {
@@ -2068,6 +2115,7 @@ const char* ce_status_string(int status) {
     case CE_ERR_ALIAS: return "CE_ERR_ALIAS";
     case CE_ERR_WORKSPACE: return "CE_ERR_WORKSPACE";
     case CE_ERR_HIP: return "CE_ERR_HIP";
+    case CE_ERR_TIMEOUT: return "CE_ERR_TIMEOUT";
     default: return "CE_ERR_UNKNOWN";
   }
 }

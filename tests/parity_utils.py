@@ -156,13 +156,53 @@ def check_zero_rows(loss_rows, grad_rows):
         assert int((bits != 0).sum()) == 0, "ignored gradient row not +0.0"
 
 
-def run_hip(inp, grad_dtype=None, in_place=False, want_grad=True, mask=None):
+ROW_ALIGN = 8      # elements: 16 bytes of bf16, 32 of fp32
+PAD_GRAD = 5.0     # what the padding columns of a padded gradient must keep
+
+
+def padded_rows(z, fill=float("nan")):
+    """A copy of z as the first V columns of a buffer whose rows are
+    ROW_ALIGN elements longer than V rounded up (16-byte aligned rows, so the
+    16-byte chunk kernels run even for a ragged V), padding set to ``fill``
+    (NaN: a read of the padding would poison the row)."""
+    T, V = z.shape
+    ld = -(-V // ROW_ALIGN) * ROW_ALIGN + ROW_ALIGN
+    big = torch.full((T, ld), fill, dtype=z.dtype, device=z.device)
+    big[:, :V] = z
+    return big[:, :V]
+
+
+def run_hip(inp, grad_dtype=None, in_place=False, want_grad=True, mask=None, pad=False):
+    """One fused call. ``pad``: logits and gradient as padded rows (the
+    logits padding NaN, the gradient padding PAD_GRAD, checked untouched)."""
     import loss_vocab_amd as L
-    return L.ce_fused(inp["logits"], inp["targets"], mask=mask,
-                      segment_ids=inp.get("segment_ids"), num_segments=inp.get("num_segments", 0),
-                      z_alpha=inp["z_alpha"], grad_scale=inp["grad_scale"],
-                      segment_mean=inp.get("segment_mean", False), grad_dtype=grad_dtype,
-                      in_place=in_place, want_grad=want_grad)
+    if not pad:
+        return L.ce_fused(inp["logits"], inp["targets"], mask=mask,
+                          segment_ids=inp.get("segment_ids"), num_segments=inp.get("num_segments", 0),
+                          z_alpha=inp["z_alpha"], grad_scale=inp["grad_scale"],
+                          segment_mean=inp.get("segment_mean", False), grad_dtype=grad_dtype,
+                          in_place=in_place, want_grad=want_grad)
+    z = padded_rows(inp["logits"])
+    T, V = z.shape
+    S = inp.get("num_segments", 0)
+    ids = inp.get("segment_ids")
+    loss = torch.empty(T, dtype=torch.float32, device=z.device)
+    seg = torch.empty(S, dtype=torch.float32, device=z.device) if ids is not None else None
+    if not want_grad:
+        grad = None
+    elif in_place:
+        grad = z
+    else:
+        grad = padded_rows(torch.empty((T, V), dtype=grad_dtype or z.dtype, device=z.device),
+                           fill=PAD_GRAD)
+    L.ce_fused_fwd_bwd(z, inp["targets"], mask, ids, inp["z_alpha"], inp["grad_scale"], loss, seg,
+                       grad, num_segments=S, segment_mean=inp.get("segment_mean", False))
+    if grad is not None:
+        rest = grad.as_strided((T, grad.stride(0) - V), (grad.stride(0), 1), grad.storage_offset() + V)
+        want = float("nan") if in_place else PAD_GRAD
+        assert bool(torch.all(rest.isnan() if in_place else rest == want)), \
+            "padding columns of the gradient were written"
+    return loss, grad, seg
 
 
 def run_oracle(logits_cpu64, targets, *, mask=None, segment_ids=None, num_segments=0,

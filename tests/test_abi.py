@@ -66,7 +66,8 @@ def test_struct_layout_matches_header(tmp_path, ctype, pytype):
 def test_status_strings():
     L = _lib()
     for code, name in [(0, "CE_OK"), (1, "CE_ERR_INVALID_ARG"), (2, "CE_ERR_UNSUPPORTED"),
-                       (3, "CE_ERR_ALIAS"), (4, "CE_ERR_WORKSPACE"), (5, "CE_ERR_HIP")]:
+                       (3, "CE_ERR_ALIAS"), (4, "CE_ERR_WORKSPACE"), (5, "CE_ERR_HIP"),
+                       (6, "CE_ERR_TIMEOUT")]:
         assert L.status_string(code) == name
     assert L.status_string(99) == "CE_ERR_UNKNOWN"
 
@@ -420,15 +421,23 @@ def test_valid_calls_without_a_device_return_ce_err_hip(tmp_path):
 
 
 def test_forward_only_needs_no_pair_slots():
-    """fp32 rows past 65536 columns reserve pair-mode exchange slots for the
-    gradient pass only: ce_workspace_bytes counts them, a call without a
-    gradient (fused with grad_out NULL, or the forward entry) does not ask for
-    them, while a gradient call still does. T = 0 keeps every call on the
+    """The gradient pass's row scheduling space: a 4-byte ticket counter
+    (256 bytes) for rows of 8193..25600 16-byte chunks, and for fp32 rows of
+    25601..51200 chunks (two workgroups per row) 32 bytes of exchange slots
+    per row before it, and a give-up count after it. ce_workspace_bytes counts it; a call without a
+    gradient (fused with grad_out NULL, or the forward entry) does not ask
+    for it, while a gradient call still does. T = 0 keeps every call on the
     host (segment-free, so nothing is enqueued)."""
     L = _lib()
-    p = _problem(T=1000, V=70000)
-    assert L.workspace_bytes(p) == 1000 * 32
-    p0 = _problem(T=0, V=70000)
+    p = _problem(T=1000, V=110000)
+    assert L.workspace_bytes(p) == (1000 * 32 + 8 + 255) // 256 * 256
+    assert L.workspace_bytes(_problem(T=1000, V=204800)) > 256
+    for v, want in ((32768, 0), (32772, 256), (70000, 256), (102400, 256), (204804, 0),
+                    (300000, 0)):
+        assert L.workspace_bytes(_problem(T=1000, V=v)) == want, v
+    for v, want in ((65536, 0), (65544, 256), (201088, 256), (204800, 256), (204808, 0)):
+        assert L.workspace_bytes(_problem(T=1000, V=v, dt=1)) == want, v
+    p0 = _problem(T=0, V=110000)
     assert _call(p0, grad=A_GRAD) == 0 and _fwd(p0) == 0
     # rows present: without the slots a gradient call is refused, a
     # forward-only call is not refused for the workspace (it fails later, at
@@ -454,8 +463,8 @@ def test_noalloc_limits_and_validation():
     # segments: 4 T bytes of staging past 8 MiB
     big = _problem(T=2_200_000, V=100, S=4, flags=1)
     assert _noalloc(big, seg=A_SEG, seg_out=A_LOSS + (1 << 24)) == 4
-    # two-workgroup fp32 rows: 32 T bytes of slots past 8 MiB with a gradient
-    pair = _problem(T=300_000, V=70000)
+    # two-workgroup fp32 rows: 32 T + 8 bytes of slots past 8 MiB with a gradient
+    pair = _problem(T=300_000, V=110000)
     assert _noalloc(pair) == 4
     # within the limit, host validation still applies first
     assert _noalloc(_problem(V=0)) == 1

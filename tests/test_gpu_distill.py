@@ -21,7 +21,7 @@ import torch
 
 from oracle import distill_oracle
 from distill_checks import check_rows
-from parity_utils import bf16_ulp, to_np64
+from parity_utils import PAD_GRAD, ROW_ALIGN, bf16_ulp, padded_rows, to_np64
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -42,13 +42,30 @@ def _np(t):
 
 
 def compare(zs, zt, t, *, mask=None, alpha=0.0, beta=1.0, gamma=1.0, grad_dtype=None,
-            in_place=False, what=""):
+            in_place=False, what="", pad=False):
+    """``pad``: student, teacher and gradient as the first V columns of
+    16-byte aligned rows (the chunk kernels and their ragged tail; packed
+    rows of a ragged V take the one-element kernel)."""
     import loss_vocab_amd as L
     zs64, zt64, t_np = to_np64(zs), to_np64(zt), _np(t)
     gdt = grad_dtype or zs.dtype
-    loss, kl, grad = L.ce_distill(zs, zt, t, mask=mask, z_alpha=alpha, kl_beta=beta,
-                                  grad_scale=gamma, grad_dtype=gdt, in_place=in_place)
-    torch.cuda.synchronize()
+    if pad:
+        T, V = zs.shape
+        zsp, ztp = padded_rows(zs), padded_rows(zt)
+        loss = torch.empty(T, device=DEV)
+        kl = torch.empty(T, device=DEV)
+        grad = zsp if in_place else padded_rows(torch.empty(T, V, dtype=gdt, device=DEV),
+                                                fill=PAD_GRAD)
+        L.ce_fused_distill(zsp, ztp, t, mask, alpha, beta, gamma, loss, kl, grad)
+        torch.cuda.synchronize()
+        if not in_place:
+            ld = grad.stride(0)
+            rest = grad.as_strided((T, ld - V), (ld, 1), grad.storage_offset() + V)
+            assert bool((rest == PAD_GRAD).all()), "padding columns of the gradient were written"
+    else:
+        loss, kl, grad = L.ce_distill(zs, zt, t, mask=mask, z_alpha=alpha, kl_beta=beta,
+                                      grad_scale=gamma, grad_dtype=gdt, in_place=in_place)
+        torch.cuda.synchronize()
     ref = distill_oracle(zs64, zt64, t_np, mask=_np(mask), z_alpha=alpha, kl_beta=beta,
                          grad_scale=gamma)
     check_rows(zs64, zt64, t_np, _np(loss), _np(kl), to_np64(grad), ref, alpha=alpha, beta=beta,
@@ -70,7 +87,8 @@ def test_vocab_sizes(dtype, V):
     print(f"[distill] V={V} {dtype}", flush=True)
     zs, zt, t = _pair(6, V, dtype, seed=V)
     t[2] = -100
-    compare(zs, zt, t, alpha=1e-3, beta=0.7, gamma=0.2, what=f"V={V}")
+    for pad in ((False, True) if V % ROW_ALIGN else (False,)):
+        compare(zs, zt, t, alpha=1e-3, beta=0.7, gamma=0.2, what=f"V={V} pad={pad}", pad=pad)
 
 
 @pytest.mark.parametrize("sd,td,gd", [(torch.float32, torch.bfloat16, torch.float32),
@@ -180,4 +198,6 @@ def test_target_positions(dtype, gdt, V):
     print(f"[distill positions] V={V} {dtype} -> {gdt}: {pos}", flush=True)
     zs, zt, _ = _pair(len(pos), V, dtype, seed=V % 97)
     t = torch.as_tensor(pos, device=DEV)
-    compare(zs, zt, t, alpha=1e-4, beta=0.6, gamma=0.05, grad_dtype=gdt, what=f"pos V={V}")
+    for pad in (False, True):
+        compare(zs, zt, t, alpha=1e-4, beta=0.6, gamma=0.05, grad_dtype=gdt,
+                what=f"pos V={V} pad={pad}", pad=pad)

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 from oracle import ce_oracle, row_entropy
-from parity_utils import check_loss, to_np64
+from parity_utils import ROW_ALIGN, check_loss, padded_rows, to_np64
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -43,10 +43,13 @@ def _bits_zero(x):
     return bool((x.detach().cpu().contiguous().view(torch.int32) == 0).all())
 
 
-def compare_forward(z, t, *, mask=None, seg=None, S=0, alpha=0.0, what=""):
+def compare_forward(z, t, *, mask=None, seg=None, S=0, alpha=0.0, what="", pad=False):
+    """``pad``: the call reads z as the first V columns of 16-byte aligned
+    rows with NaN padding (the chunk kernels and their ragged tail; packed
+    rows of a ragged V take the one-element kernel)."""
     import loss_vocab_amd as L
-    loss, lse, ent, segl = L.ce_forward(z, t, mask=mask, segment_ids=seg, num_segments=S,
-                                        z_alpha=alpha)
+    loss, lse, ent, segl = L.ce_forward(padded_rows(z) if pad else z, t, mask=mask,
+                                        segment_ids=seg, num_segments=S, z_alpha=alpha)
     torch.cuda.synchronize()
     z64, t_np, m_np = to_np64(z), _np(t), _np(mask)
     ref = ce_oracle(z64, t_np, mask=m_np, segment_ids=_np(seg), num_segments=S, z_alpha=alpha,
@@ -76,8 +79,10 @@ SMALL = [
 def test_small_workloads_forward(name, wl):
     print(f"[forward] {name} T={wl.T} V={wl.V}", flush=True)
     inp = make_inputs(wl, device=DEV)
-    compare_forward(inp["logits"], inp["targets"], seg=inp["segment_ids"],
-                    S=inp["num_segments"], alpha=inp["z_alpha"], what=name)
+    for pad in ((False, True) if wl.V % ROW_ALIGN else (False,)):
+        compare_forward(inp["logits"], inp["targets"], seg=inp["segment_ids"],
+                        S=inp["num_segments"], alpha=inp["z_alpha"], what=f"{name} pad={pad}",
+                        pad=pad)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -89,7 +94,8 @@ def test_forward_vocab_sizes(dtype, V):
     z = (torch.randn(T, V, generator=g, device=DEV) * 2).to(dtype)
     t = torch.randint(0, V, (T,), generator=g, device=DEV)
     t[1] = -100
-    compare_forward(z, t, alpha=1e-3, what=f"V={V}")
+    for pad in ((False, True) if V % ROW_ALIGN else (False,)):
+        compare_forward(z, t, alpha=1e-3, what=f"V={V} pad={pad}", pad=pad)
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -178,7 +184,8 @@ SHAPES = [(torch.float32, 50001), (torch.bfloat16, 100003), (torch.float32, 1700
 
 @pytest.mark.parametrize("dtype,V", SHAPES, ids=[f"{str(d)[6:]}-{v}" for d, v in SHAPES])
 def test_forward_row_shapes(dtype, V):
-    """Medium and long rows take the LDS-staged forward shapes: with and
+    """Medium and long rows take the LDS-staged forward shapes (as padded
+    16-byte rows; packed ragged rows take the one-element kernel): with and
     without the entropy output, and the fused call without a gradient."""
     import loss_vocab_amd as L
     print(f"[forward] shapes V={V} {dtype}", flush=True)
@@ -189,8 +196,10 @@ def test_forward_row_shapes(dtype, V):
     t[2] = -100
     z[4, t[4]] = z[4].max() + 30          # a confident row
     compare_forward(z, t, alpha=1e-4, what=f"shape V={V}")
-    loss2, lse2, ent2, _ = L.ce_forward(z, t, z_alpha=1e-4, entropy=False)
-    loss3, _, _ = L.ce_fused(z, t, z_alpha=1e-4, want_grad=False)
+    compare_forward(z, t, alpha=1e-4, what=f"shape V={V} padded", pad=True)
+    zp = padded_rows(z)
+    loss2, lse2, ent2, _ = L.ce_forward(zp, t, z_alpha=1e-4, entropy=False)
+    loss3, _, _ = L.ce_fused(zp, t, z_alpha=1e-4, want_grad=False)
     torch.cuda.synchronize()
     z64 = to_np64(z)
     ref = ce_oracle(z64, _np(t), z_alpha=1e-4, want_grad=False)

@@ -17,8 +17,8 @@ import numpy as np
 import pytest
 import torch
 
-from parity_utils import (check_grad, check_loss, check_zero_rows, row_scales, run_hip,
-                          run_oracle, to_np64)
+from parity_utils import (ROW_ALIGN, check_grad, check_loss, check_zero_rows, padded_rows,
+                          row_scales, run_hip, run_oracle, to_np64)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -39,12 +39,13 @@ def _np(t):
     return None if t is None else t.detach().cpu().numpy()
 
 
-def compare_all(inp, *, grad_dtype=None, in_place=False, mask=None, want_grad=True, what=""):
+def compare_all(inp, *, grad_dtype=None, in_place=False, mask=None, want_grad=True, what="",
+                pad=False):
     logits = inp["logits"]
     z64 = to_np64(logits)
     gdt = grad_dtype or logits.dtype
     loss, grad, seg = run_hip(inp, grad_dtype=gdt, in_place=in_place, want_grad=want_grad,
-                              mask=mask)
+                              mask=mask, pad=pad)
     torch.cuda.synchronize()
     ref = run_oracle(z64, _np(inp["targets"]), mask=_np(mask), segment_ids=_np(inp.get("segment_ids")),
                      num_segments=inp.get("num_segments", 0), z_alpha=inp["z_alpha"],
@@ -84,7 +85,8 @@ SMALL = [
 def test_small_workloads(name, wl, opt):
     print(f"[parity] {name} T={wl.T} V={wl.V}", flush=True)
     inp = make_inputs(wl, device=DEV)
-    compare_all(inp, in_place=opt.get("in_place", False), what=name)
+    for pad in ((False, True) if wl.V % ROW_ALIGN else (False,)):
+        compare_all(inp, in_place=opt.get("in_place", False), what=f"{name} pad={pad}", pad=pad)
 
 
 # ---------------------------------------------------------------------------
@@ -133,9 +135,10 @@ def test_zero_rows():
 
 
 @pytest.mark.parametrize("dtype,pad", [(torch.float32, 13), (torch.bfloat16, 13),
-                                       (torch.float32, 64), (torch.bfloat16, 64)])
+                                       (torch.float32, 7), (torch.bfloat16, 7)])
 def test_row_stride_larger_than_V(dtype, pad):
-    """pad 13 makes rows misaligned (scalar path); pad 64 keeps 16-byte rows."""
+    """V = 1001 in rows of 1014 elements (misaligned: the one-element path)
+    or of 1008 (16-byte rows: the chunk kernel with a 1- or 9-column tail)."""
     g = torch.Generator(device=DEV).manual_seed(pad)
     T, V = 33, 1001
     big = (torch.randn(T, V + pad, generator=g, device=DEV) * 2).to(dtype)
@@ -322,13 +325,13 @@ TIER_CASES = [
     (torch.bfloat16, 8192 * 8), (torch.bfloat16, 8192 * 8 + 8), (torch.bfloat16, 70001),
     (torch.bfloat16, 16384 * 8), (torch.bfloat16, 16384 * 8 + 3), (torch.bfloat16, 150000),
     (torch.float32, 8192 * 4 + 1), (torch.float32, 40000), (torch.float32, 70003),
-    # long-row shapes (13 on-chip slots of 1024 chunks per lane, then steps of
-    # 4 streamed slots, two steps per loop turn): streamed parts of 3 slots and
-    # one chunk, exactly 2 and 3 steps (a step and a turn wholly past the end)
+    # row-resident rows: the end in the first LDS slot (16385 chunks), in a
+    # middle one, and exactly filling all 25 slots (25600 chunks)
     (torch.bfloat16, 16385 * 8 + 5), (torch.bfloat16, (13312 + 8192) * 8),
     (torch.bfloat16, (13312 + 12288) * 8),
-    # two workgroups per fp32 row: halves with one streamed chunk and with
-    # exactly one step of streamed slots
+    # past one workgroup's chip space: bf16 rows take the streamed long-row
+    # shape, fp32 rows two workgroups (halves of 13313 and 17408 chunks)
+    (torch.bfloat16, 25601 * 8 + 3),
     (torch.float32, 2 * (13312 + 1) * 4), (torch.float32, 2 * (13312 + 4096) * 4),
 ]
 
@@ -357,10 +360,15 @@ def test_kernel_tiers(dtype, V):
     for i in range(0, len(tg), 2):
         z[i, tg[i]] = z[i].max() + 30.0
     z = z.to(dtype)
-    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / (T - 1)), what=f"tier V={V}")
-    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / (T - 1)),
-                grad_dtype=torch.float32 if dtype == torch.bfloat16 else torch.bfloat16,
-                what=f"tier V={V} mixed")
+    # a ragged V with packed rows takes the one-element kernel; as the first
+    # V columns of 16-byte aligned rows it takes the tier's chunk kernel and
+    # its tail of V % W columns
+    for pad in ((False, True) if V % ROW_ALIGN else (False,)):
+        compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / (T - 1)), what=f"tier V={V} pad={pad}",
+                    pad=pad)
+        compare_all(_inp(z, t, alpha=1e-4, gamma=1.0 / (T - 1)),
+                    grad_dtype=torch.float32 if dtype == torch.bfloat16 else torch.bfloat16,
+                    what=f"tier V={V} mixed pad={pad}", pad=pad)
 
 
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, (1 << 22) + 3), (torch.float32, (1 << 21) + 1)])
@@ -392,8 +400,11 @@ def test_long_fp32_rows_two_workgroups_per_row():
     mask = (torch.arange(T, device=DEV) % 9 != 4).to(torch.uint8)
     seg = (torch.arange(T, device=DEV) * S // T).to(torch.int32)
     inp = _inp(z, t, alpha=1e-4, gamma=1.0, seg=seg, S=S, seg_mean=True)
-    loss_a, grad_a, seg_a, _ = compare_all(inp, mask=mask, what="pair rows")
-    zc = z.clone()
+    # padded 16-byte rows (a ragged V as it runs on the pair kernel), then
+    # packed rows (the one-element kernel) for comparison
+    loss_a, grad_a, seg_a, _ = compare_all(inp, mask=mask, what="pair rows", pad=True)
+    compare_all(inp, mask=mask, what="pair rows packed")
+    zc = padded_rows(z)
     loss_b, grad_b, seg_b = L.ce_fused(zc, t, mask=mask, segment_ids=seg, num_segments=S,
                                        z_alpha=1e-4, grad_scale=1.0, segment_mean=True,
                                        in_place=True)
@@ -401,6 +412,43 @@ def test_long_fp32_rows_two_workgroups_per_row():
     assert torch.equal(loss_a.nan_to_num(7.0), loss_b.nan_to_num(7.0))
     assert torch.equal(grad_a.nan_to_num(7.0), grad_b.nan_to_num(7.0))
     assert torch.equal(seg_a.nan_to_num(7.0), seg_b.nan_to_num(7.0))   # a NaN row poisons its segment
+
+
+def test_pair_give_up_is_reported(monkeypatch):
+    """The two-workgroup fp32 rows' bounded wait, forced from the host: with
+    the poll limit at 0 every half row gives up at once (no kernel waits),
+    those rows come out NaN, and a validating call returns CE_ERR_TIMEOUT.
+    With the limit restored the same validating call succeeds and matches
+    the plain call bit for bit."""
+    import loss_vocab_amd as L
+    from loss_vocab_amd._lib import CE_ERR_TIMEOUT, CeError
+    print("[parity] pair give-up report V=110003", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(17)
+    T, V = 12, 110003
+    z = padded_rows(torch.randn(T, V, generator=g, device=DEV))   # 16-byte rows: the pair kernel
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[3] = -100
+
+    def call(validate=False):
+        loss = torch.empty(T, device=DEV)
+        grad = padded_rows(torch.empty(T, V, device=DEV), fill=0.0)
+        L.ce_fused_fwd_bwd(z, t, None, None, 1e-4, 0.5, loss, None, grad, validate=validate)
+        torch.cuda.synchronize()
+        return loss, grad
+
+    ref_loss, ref_grad = call()
+    assert torch.isfinite(ref_loss).all()
+    monkeypatch.setenv("CE_PAIR_SPIN_LIMIT", "0")
+    loss, grad = call()
+    live = t != -100
+    assert torch.isnan(loss[live]).all() and torch.isnan(grad[live]).all()
+    assert (loss[~live] == 0).all() and (grad[~live] == 0).all()
+    with pytest.raises(CeError) as err:
+        call(validate=True)
+    assert err.value.status == CE_ERR_TIMEOUT
+    monkeypatch.delenv("CE_PAIR_SPIN_LIMIT")
+    loss_v, grad_v = call(validate=True)
+    assert torch.equal(loss_v, ref_loss) and torch.equal(grad_v, ref_grad)
 
 
 @pytest.mark.parametrize("dtype,V,T", [(torch.bfloat16, 201088, 600), (torch.float32, 151936, 520),
@@ -427,8 +475,9 @@ def test_row_resident_many_rows(dtype, V, T):
     S = 9
     seg = (torch.arange(T, device=DEV) * S // T).to(torch.int32)
     inp = _inp(z, t, alpha=1e-4, gamma=1.0, seg=seg, S=S, seg_mean=True)
-    loss_a, grad_a, seg_a, _ = compare_all(inp, mask=mask, what=f"rowres V={V}")
-    zc = z.clone()
+    pad = V % ROW_ALIGN != 0                       # a ragged V runs as padded 16-byte rows
+    loss_a, grad_a, seg_a, _ = compare_all(inp, mask=mask, what=f"rowres V={V}", pad=pad)
+    zc = padded_rows(z) if pad else z.clone()
     loss_b, grad_b, seg_b = L.ce_fused(zc, t, mask=mask, segment_ids=seg, num_segments=S,
                                        z_alpha=1e-4, grad_scale=1.0, segment_mean=True,
                                        in_place=True)

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 from oracle import shard_nontarget_lse
-from parity_utils import (check_grad, check_loss, check_zero_rows, row_scales, run_oracle,
-                          to_np64)
+from parity_utils import (PAD_GRAD, ROW_ALIGN, check_grad, check_loss, check_zero_rows,
+                          padded_rows, row_scales, run_oracle, to_np64)
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -76,12 +76,26 @@ def test_split_matches_oracle(dtype, T, V, shards, align, alpha, S):
         seg = torch.sort(torch.randint(0, S, (T,), generator=g, device=DEV)).values.to(torch.int32)
     gamma = 1.0 / (T - 1)
     z64 = to_np64(z)
-    loss, grad, segsum, row_state = L.ce_split(z, t, shards=shards, segment_ids=seg, num_segments=S,
-                                               z_alpha=alpha, grad_scale=gamma,
-                                               segment_mean=S > 0, align=align)
-    torch.cuda.synchronize()
     ref = run_oracle(z64, _np(t), segment_ids=_np(seg), num_segments=S, z_alpha=alpha,
                      grad_scale=gamma, segment_mean=S > 0)
+    # packed rows of a ragged V run the one-element kernels; padded 16-byte
+    # rows (NaN padding) run the chunk kernels on aligned shards
+    for pad in ((False, True) if V % ROW_ALIGN else (False,)):
+        _split_case(L, z, t, seg, S, shards, align, alpha, gamma, dtype, ref, pad)
+
+
+def _split_case(L, z, t, seg, S, shards, align, alpha, gamma, dtype, ref, pad):
+    T, V = z.shape
+    gout = padded_rows(torch.empty_like(z), fill=PAD_GRAD) if pad else None
+    loss, grad, segsum, row_state = L.ce_split(padded_rows(z) if pad else z, t, shards=shards,
+                                               segment_ids=seg, num_segments=S,
+                                               z_alpha=alpha, grad_scale=gamma,
+                                               segment_mean=S > 0, align=align, grad_out=gout)
+    torch.cuda.synchronize()
+    if pad:
+        ld = gout.stride(0)
+        rest = gout.as_strided((T, ld - V), (ld, 1), gout.storage_offset() + V)
+        assert bool((rest == PAD_GRAD).all()), "padding columns of the gradient were written"
     check_loss(_np(loss), ref["loss"], "split loss")
     check_grad(to_np64(grad), ref["grad"], dtype, "split grad",
                scale=row_scales(T, gamma, _np(seg), S, S > 0), targets=_np(t))
