@@ -1055,16 +1055,18 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 // straight from HBM -- so every logit is read from HBM exactly once (the
 // streamed-tier kernel re-reads what does not fit). Slot i of thread tid is
 // chunk i * 1024 + tid. All of a row's loads go out at its start, so pass 1
-// reduces slots as they land: the row takes no other load whose value is
-// needed early (the target logit comes from the lane whose slot holds it),
-// since on gfx9 waiting for one load waits for every load issued before it. (Issuing the next row's slots during this
-// row's gradient pass measured slower: it moves every read into the
-// gradient pass and leaves pass 1 with no memory traffic of its own.)
+// reduces slots as they land. (Issuing the next row's slots
+// during this row's gradient pass measured slower: it moves every read into
+// the gradient pass and leaves pass 1 with no memory traffic of its own.)
 //
-// Rows are dealt out by a ticket counter in the workspace (all-ones before
-// the launch, so the first ticket is 0): a workgroup that finishes early
-// takes more rows, which evens out rows of unequal cost (ignored rows are
-// only written). In pair mode (fp32 rows too long for one workgroup's chip
+// With DEAL, rows are dealt out by a ticket counter in the workspace
+// (all-ones before the launch, so the first ticket is 0): a workgroup that
+// finishes early takes more rows, which evens out rows of unequal cost
+// (ignored rows are only written). Without it, workgroup b takes rows b,
+// b + grid, ... . Measured on MI355X: dealing is faster for rows that use
+// the LDS slots (201088-column bf16 rows 8.95 -> 8.76 ms) and for pairs, the
+// fixed stride for rows held in registers alone (128256-column bf16 rows
+// 1.457 -> 1.339 ms). In pair mode (fp32 rows too long for one workgroup's chip
 // space) the two halves of row r are tickets 2r and 2r + 1, and a
 // workgroup takes its next ticket only after its current half has exchanged
 // statistics with its partner. That makes the waits deadlock-free without
@@ -1082,9 +1084,10 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 // count as -inf and store nothing; slots past the end slot load the last
 // chunk (one line per wave) and are not reduced or stored.
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int NREG, int NLDS, int MODE>
+template <typename TI, typename TO, int NREG, int NLDS, int MODE, bool DEAL>
 __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
   static_assert(MODE == kFused || MODE == kPair, "the fused call, whole or half rows");
+  static_assert(DEAL || MODE == kFused, "pairs are dealt by ticket");
   constexpr int BLOCK = 1024;
   constexpr bool PAIR = MODE == kPair;
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
@@ -1092,11 +1095,11 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
   constexpr uint32_t SLOT = BLOCK * 16u;           // bytes of input per slot
   __shared__ float red_m[2][BLOCK / 64];
   __shared__ float red_s[2][BLOCK / 64];
-  __shared__ u32x4 stage[NLDS > 0 ? NLDS : 1][BLOCK];
+  __shared__ u32x4 stage[NLDS > 0 ? NLDS : 1][NLDS > 0 ? BLOCK : 1];
   __shared__ float epi[2][4];
   [[maybe_unused]] __shared__ float pair_sh[2][4];
   [[maybe_unused]] __shared__ uint32_t tick_sh[2];
-  __shared__ float zt_sh[2];   // the row's target logit, from the lane that holds it
+  [[maybe_unused]] __shared__ float zt_sh[2];    // whole rows: the target logit
 
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
@@ -1127,14 +1130,15 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
   // done, which keeps the pairing deadlock-free) and shares it through LDS
   // at the one barrier every row passes after its last use of the previous
   // value. Tickets are read back as scalars, so the row index and all that
-  // derives from it stay uniform. (Measured against a static grid stride
-  // and against tickets taken two rows ahead: dealing rows one ahead was
-  // the fastest on the 201088-column bf16 rows and level with the best on
-  // the others.)
-  if (tid == 0) tick_sh[0] = take_ticket();
-  __syncthreads();
-  uint32_t k = read_ticket(0);
-  __syncthreads();                                // tick_sh[0] is rewritten by the first row
+  // derives from it stay uniform. (Tickets taken two rows ahead measured
+  // slower.)
+  uint32_t k = blockIdx.x;
+  if constexpr (DEAL) {
+    if (tid == 0) tick_sh[0] = take_ticket();
+    __syncthreads();
+    k = read_ticket(0);
+    __syncthreads();                              // tick_sh[0] is rewritten by the first row
+  }
   int64_t r = ticket_row(k);
   int64_t t_next = r < p.T ? labels[r] : 0;
   int par = 0;
@@ -1160,12 +1164,18 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       // Ignored row: +0.0 everywhere, logits never read. Valid row with an
       // out-of-range target: NaN loss and gradient row. (Both halves of a
       // pair decide alike; half 0 writes the row's loss.)
-      uint32_t kn = 0;
-      if (tid == 0) kn = take_ticket();
-      fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true, !PAIR || half == 0);
-      if (tid == 0) tick_sh[par] = kn;
-      __syncthreads();
-      k = read_ticket(par);
+      if constexpr (DEAL) {
+        uint32_t kn = 0;
+        if (tid == 0) kn = take_ticket();
+        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true,
+                            !PAIR || half == 0);
+        if (tid == 0) tick_sh[par] = kn;
+        __syncthreads();
+        k = read_ticket(par);
+      } else {
+        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true);
+        k += gridDim.x;
+      }
       r = ticket_row(k);
       t_next = r < p.T ? labels[r] : 0;
       par ^= 1;
@@ -1202,8 +1212,13 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
     }
     [[maybe_unused]] int32_t sid = 0;
     if (p.seg_mean) sid = seg_ids[r];
-    uint32_t k_next = 0;                           // thread 0: the next ticket
-    if (!PAIR && tid == 0) k_next = take_ticket();
+    // The target logit: in pair mode its own load, issued behind the slots
+    // and first needed after the exchange; for whole rows the lane whose
+    // slot holds it hands it over through LDS (measured 5% faster on
+    // 128256-column bf16 rows, level on the others).
+    [[maybe_unused]] const float zt_ld = (PAIR && owned) ? Elem<TI>::load1(zrow, t) : kNegInf;
+    [[maybe_unused]] uint32_t k_next = 0;          // thread 0: the next ticket
+    if (DEAL && !PAIR && tid == 0) k_next = take_ticket();
 
     // Where the target sits: chunk ct, element kt, slot st, lane `mine`.
     const uint32_t ct = t / W;
@@ -1220,9 +1235,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       return st;
     };
     // Lanes past the row end (in the end slot) count as -inf; the target's
-    // element in its slot too (in the one lane that holds it, which first
-    // hands its value to the row through LDS: the target logit takes no load
-    // of its own, whose early wait would hold pass 1 until every slot landed).
+    // element in its slot too (in the one lane that holds it).
     auto fixed = [&](u32x4 v, int slot) -> u32x4 {
       if (slot == end_slot()) {
         const bool out = static_cast<uint32_t>(slot) * BLOCK + tid_r >= nchunk;
@@ -1232,7 +1245,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
         v.w = out ? neg_w : v.w;
       }
       if (slot == tgt_slot()) {
-        if (mine) {
+        if (!PAIR && mine) {
           const uint32_t w = kq == 0 ? v.x : (kq == 1 ? v.y : (kq == 2 ? v.z : v.w));
           zt_sh[par] = Elem<TI>::BYTES == 4 ? __uint_as_float(w) : __uint_as_float((w >> ksh) << 16);
         }
@@ -1277,13 +1290,14 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       const uint32_t j = tail_begin + tid_r;
       float xv = Elem<TI>::load1(zrow, j);
       if (j == t) {
-        zt_sh[par] = xv;
+        if (!PAIR) zt_sh[par] = xv;
         xv = kNegInf;
       }
       merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
     }
     block_reduce<BLOCK>(mL, s, red_m, red_s, par, tid_r & 63u, tid_r >> 6);
-    const float zt = owned ? zt_sh[par] : kNegInf;   // written before the barrier above
+    // (zt_sh is written before the reduction's barrier)
+    const float zt = PAIR ? zt_ld : (owned ? zt_sh[par] : kNegInf);
 
     float ztm = zt;
     if constexpr (PAIR) {
@@ -1340,9 +1354,10 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       ztm = fmaxf(zt, pz);
     }
     // Wave 0 runs the fp64 epilogue and shares the row factors through LDS
-    // (with the next ticket, whose atomic has returned by then). The epilogue's scalar inputs pass an empty asm, so their fp64
-    // forms are made here, not hoisted out of the row loop into registers
-    // held throughout.
+    // (with the next ticket, whose atomic has returned by then). The
+    // epilogue's scalar inputs pass an empty asm, so their fp64 forms are
+    // made here, not hoisted out of the row loop into registers held
+    // throughout.
     if (wid == 0) {
       RowParams q = p;
       asm volatile("" : "+s"(q.grad_scale), "+s"(q.z_alpha));
@@ -1352,12 +1367,12 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
         epi[par][0] = o.g_t;
         epi[par][1] = o.cnt;
         epi[par][2] = o.kl;
-        tick_sh[par] = k_next;
+        if constexpr (DEAL) tick_sh[par] = k_next;
       }
     }
     __syncthreads();
     const float cnt = epi[par][1], kl = epi[par][2];
-    k = read_ticket(par);
+    k = DEAL ? read_ticket(par) : k + gridDim.x;
     t_next = ticket_row(k) < p.T ? labels[ticket_row(k)] : 0;
     const int64_t r_next = ticket_row(k);
 
@@ -1615,31 +1630,45 @@ __global__ __launch_bounds__(256) void ce_fill_u32_kernel(uint32_t* __restrict__
 constexpr bool rowres_off() { return CE_ROWRES == 0; }
 
 // Row-resident shape: 16 register slots and 9 LDS slots per lane of 1024,
-// 25600 chunks (400 KiB) of a row on chip.
+// 25600 chunks (400 KiB) of a row on chip. Rows (half rows) that fit in the
+// register slots take an instance without the LDS slots: a load into an LDS
+// slot past the row end would still cost its copy, and the first register
+// slot's wait would cover it.
 constexpr int kResReg = 16, kResLds = 9;
 constexpr int64_t kResChunks = int64_t{kResReg + kResLds} * 1024;
+constexpr int64_t kResRegChunks = int64_t{kResReg} * 1024;
 
-// Whole rows on the row-resident kernel: the ticket counter is set to
-// all-ones by a one-block fill kernel (capturable), then one workgroup per CU.
+// Whole rows on the row-resident kernel, one workgroup per CU. Rows that use
+// the LDS slots are dealt by ticket: the counter is set to all-ones by a
+// one-block fill kernel first (capturable).
+template <typename TI, typename TO, int NLDS>
+ce_status launch_rowres_shape(const RowParams& rp, hipStream_t stream) {
+  if constexpr (NLDS > 0) {
+    if (rp.tickets == nullptr) return CE_ERR_WORKSPACE;
+    hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(1), dim3(256), 0, stream, rp.tickets, int64_t{1},
+                       ~0u);
+    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
+  }
+  static std::atomic<int> occ{0};
+  return launch_persistent(ce_rowres_kernel<TI, TO, kResReg, NLDS, kFused, (NLDS > 0)>, 1024, occ,
+                           rp, stream, 64);
+}
+
 template <typename TI, typename TO>
 ce_status launch_rowres(const RowParams& rp, hipStream_t stream) {
-  if (rp.tickets == nullptr) return CE_ERR_WORKSPACE;
-  hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(1), dim3(256), 0, stream, rp.tickets, int64_t{1}, ~0u);
-  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
-  static std::atomic<int> occ{0};
-  return launch_persistent(ce_rowres_kernel<TI, TO, kResReg, kResLds, kFused>, 1024, occ, rp,
-                           stream, 64);
+  if (rp.V / Elem<TI>::VEC <= kResRegChunks) return launch_rowres_shape<TI, TO, 0>(rp, stream);
+  return launch_rowres_shape<TI, TO, kResLds>(rp, stream);
 }
 
 // Pair mode: fp32 rows of 25601..51200 chunks, two workgroups per row, each
 // holding its half row on chip (the row-resident kernel's pair mode). The
-// exchange slots and the ticket counter are filled with all-ones first (a
-// kernel, so the call stays capturable in a graph). An ordinary launch: the
-// ticket order needs no co-residency guarantee beyond two resident
-// workgroups.
-template <typename TI, typename TO>
-ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
-  auto kern = ce_rowres_kernel<TI, TO, kResReg, kResLds, kPair>;
+// exchange slots, the ticket counter and the give-up count are filled with
+// all-ones first (a kernel, so the call stays capturable in a graph). An
+// ordinary launch: the ticket order needs no co-residency guarantee beyond
+// two resident workgroups.
+template <typename TI, typename TO, int NLDS>
+ce_status launch_pair_shape(const RowParams& rp, hipStream_t stream) {
+  auto kern = ce_rowres_kernel<TI, TO, kResReg, NLDS, kPair, true>;
   static std::atomic<int> occ{0};
   int per_cu = occ.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
@@ -1657,6 +1686,14 @@ ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(1024), 0, stream, rp);
   return hipGetLastError() == hipSuccess ? CE_OK : CE_ERR_HIP;
+}
+
+template <typename TI, typename TO>
+ce_status launch_rows_pair(const RowParams& rp, hipStream_t stream) {
+  // the longer half: columns [pair_split, V)
+  if ((rp.V - rp.pair_split) / Elem<TI>::VEC <= kResRegChunks)
+    return launch_pair_shape<TI, TO, 0>(rp, stream);
+  return launch_pair_shape<TI, TO, kResLds>(rp, stream);
 }
 
 template <typename TI, typename TO, bool WRITE, int MODE = kFused, bool ENT = false>
@@ -1850,9 +1887,11 @@ uint32_t pair_spin_limit() {
   const unsigned long v = std::strtoul(e, &end, 10);
   return (end != nullptr && *end == '\0' && v <= kPairSpin) ? static_cast<uint32_t>(v) : kPairSpin;
 }
+// Rows dealt by ticket on the row-resident kernel: those that use its LDS
+// slots (rows held in registers alone take a fixed stride).
 bool rowres_rows(const ce_problem* p) {
   const int64_t nchunk = p->V / (p->logits_dtype == CE_DTYPE_F32 ? 4 : 8);
-  return nchunk > 8192 && nchunk <= kResChunks;
+  return nchunk > kResRegChunks && nchunk <= kResChunks;
 }
 size_t sched_ws_bytes(const ce_problem* p, bool grad = true) {
   if (!grad || p->T == 0) return 0;

@@ -268,10 +268,13 @@ LMHEAD_WORKLOADS = {
 }
 
 
-def lmhead_flops(w: LmHeadWorkload, backward=True):
-    """Matrix-core flops of one call: the logit product once forward and once
-    more in the backward (recomputed), plus dX = G W and dW = G^T X."""
-    return (8 if backward else 2) * w.T * w.V * w.H
+def lmhead_flops(w: LmHeadWorkload, backward=True, recompute=True):
+    """Matrix-core flops of one call: the logit product forward (2 T V H),
+    dX = G W and dW = G^T X backward (4 T V H), and with ``recompute`` the
+    logit product once more in the backward (executed, not algorithmic)."""
+    if not backward:
+        return 2 * w.T * w.V * w.H
+    return (8 if recompute else 6) * w.T * w.V * w.H
 
 
 def make_lmhead_inputs(w: LmHeadWorkload, device="cpu", seed_offset=0, rows=None):
