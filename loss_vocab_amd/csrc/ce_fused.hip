@@ -123,6 +123,18 @@ __device__ __forceinline__ void touch(u32x4& v) { asm volatile("" : "+v"(v)); }
 
 // Merge partial (m, s) -- s = sum 2^(y - m) over a set, m a float shift in
 // log2 units -- with (m2, s2). An empty partial is (-inf, 0).
+// A (shift, sum) pair's shift must be the rounded float its sum was formed
+// against. HIP contracts floating-point expressions across statements by
+// default, so a shift written as a product (max * log2e) could reach a later
+// subtraction unrounded -- fused into fma(max, log2e, -sh) -- and the rescale
+// factor of that pair would pick up the product's rounding residue (up to
+// 2.6e-6 relative at |z| ~ 64). Passing the product through an empty asm makes
+// it a plain register value that every use sees rounded.
+__device__ __forceinline__ float as_rounded(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ void merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
   const float sh = (mn == kNegInf) ? 0.f : mn;
@@ -735,7 +747,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 #pragma unroll
         for (int k = 0; k < W; ++k) rmax = fmaxf(rmax, e[i][k]);
       }
-      const float rml = rmax * kL2E;
+      const float rml = as_rounded(rmax * kL2E);
       rsh = (rml == kNegInf) ? 0.f : rml;
       float rs = 0.f;
 #pragma unroll
@@ -766,7 +778,7 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 #pragma unroll
         for (int k = 0; k < W; ++k) vmax = fmaxf(vmax, x[k]);
       }
-      const float vml = vmax * kL2E;
+      const float vml = as_rounded(vmax * kL2E);
       const float vsh = (vml == kNegInf) ? 0.f : vml;
 #pragma unroll
       for (int i = 0; i < NRAW; ++i) touch(rawv[i]);

@@ -667,8 +667,13 @@ def test_lse_out_on_fused_call(dtype, V):
     assert torch.equal(grad_a.view(bits), grad_b.view(bits))
 
 
+# short rows (512-lane tier), register-only and register + LDS row-resident
+# rows, two-workgroup fp32 rows, and the streamed long-row tier (fp32 past
+# 51200 chunks, bf16 past 25600); ragged lengths run packed (one-element
+# kernel) and padded (the chunk kernels and their tails)
 FP32_UNIT_CASES = [(torch.float32, 3001), (torch.float32, 40000), (torch.float32, 70003),
-                   (torch.bfloat16, 16385 * 8 + 5), (torch.float32, 8192 * 4 + 1)]
+                   (torch.bfloat16, 16385 * 8 + 5), (torch.float32, 8192 * 4 + 1),
+                   (torch.float32, 110003), (torch.float32, 210001), (torch.bfloat16, 205001)]
 
 
 @pytest.mark.parametrize("dtype,V", FP32_UNIT_CASES,
@@ -694,4 +699,36 @@ def test_fp32_grad_unit_scale_large_lse(dtype, V):
         z[r, j] = float(torch.logsumexp(z[r], 0)) + 0.5 + 0.5 * (r % 6)
         z[r] += 50.0 if r % 2 == 0 else -55.0
     z = z.to(dtype)
-    compare_all(_inp(z, t, alpha=1e-4, gamma=1.0), grad_dtype=torch.float32, what=f"unit V={V}")
+    for pad in ((False, True) if V % ROW_ALIGN else (False,)):
+        compare_all(_inp(z, t, alpha=1e-4, gamma=1.0), grad_dtype=torch.float32,
+                    what=f"unit V={V} pad={pad}", pad=pad)
+
+
+def test_side_stream_without_workspace():
+    """The binding allocates the segment workspace itself when none is given;
+    on a stream other than torch's current one the block must not be handed
+    out again before the call has run. The side stream is held busy first,
+    so the call's kernels run late, and an allocation of the same size on
+    the current stream is filled right after the call returns."""
+    import loss_vocab_amd as L
+    g = torch.Generator(device=DEV).manual_seed(21)
+    T, V, S = 4096, 2048, 64
+    z = torch.randn(T, V, generator=g, device=DEV)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    seg = (torch.arange(T, device=DEV) * S // T).to(torch.int32)
+    need = L.workspace_bytes(z, num_segments=S)
+    assert need > 0
+    loss = torch.empty(T, device=DEV)
+    segl = torch.empty(S, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)           # ~10 ms of spinning on the side stream
+    L.ce_fused_fwd_bwd(z, t, None, seg, 0.0, 1.0, loss, segl, None, num_segments=S,
+                       stream=side.cuda_stream)
+    junk = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)   # current stream
+    torch.cuda.synchronize()
+    del junk
+    ref = run_oracle(to_np64(z), _np(t), segment_ids=_np(seg), num_segments=S, want_grad=False)
+    check_loss(_np(loss), ref["loss"], "side stream loss")
+    check_loss(_np(segl), ref["seg_nll"], "side stream segments")
