@@ -231,3 +231,35 @@ def test_weighted_backward(dtype, shards, V):
     # sum that may cancel, so no relative bar here
     check_grad(to_np64(grad), ref_w["grad"], dtype, "weighted grad",
                scale=np.maximum(np.abs(_np(w_row).astype(np.float64)), gamma), rel=False)
+
+
+@pytest.mark.parametrize("dtype,V,shards", [(torch.float32, 30001, 2), (torch.float32, 230011, 3),
+                                            (torch.bfloat16, 230011, 2)])
+def test_split_fp32_grad_unit_scale_large_lse(dtype, V, shards):
+    """The split form at grad_scale 1 on rows near +-50 (|lse| > 40) whose
+    largest softmax value, 0.6-0.95, is a non-target column in either shard,
+    fp32 gradient, padded rows: every element within 1e-6 absolute and 2^-16
+    relative of the oracle (the row state carries lse log2 e as a float and
+    its residue)."""
+    import loss_vocab_amd as L
+    print(f"[split] unit scale V={V} {dtype} shards={shards}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(V + shards)
+    T = 10
+    z = torch.randn(T, V, generator=g, device=DEV) * 2
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    cols = [3, V // 2 + 5, V - 2, 1100, 2 * V // 3]
+    for r in range(T):
+        j = cols[r % len(cols)]
+        if int(t[r]) == j:
+            t[r] = (j + 1) % V
+        z[r, j] = float(torch.logsumexp(z[r], 0)) + 0.5 + 0.5 * (r % 6)
+        z[r] += 50.0 if r % 2 == 0 else -55.0
+    z = z.to(dtype)
+    ref = run_oracle(to_np64(z), _np(t), z_alpha=1e-4, grad_scale=1.0)
+    gout = padded_rows(torch.empty(T, V, device=DEV), fill=PAD_GRAD)
+    loss, grad, _, _ = L.ce_split(padded_rows(z), t, shards=shards, z_alpha=1e-4, grad_scale=1.0,
+                                  align=8, grad_out=gout)
+    torch.cuda.synchronize()
+    check_loss(_np(loss), ref["loss"], "split unit loss")
+    check_grad(to_np64(grad), ref["grad"], torch.float32, "split unit grad", scale=1.0,
+               targets=_np(t))
