@@ -1636,11 +1636,6 @@ __global__ __launch_bounds__(256) void ce_fill_u32_kernel(uint32_t* __restrict__
     p[i] = v;
 }
 
-#ifndef CE_ROWRES
-#define CE_ROWRES 1
-#endif
-constexpr bool rowres_off() { return CE_ROWRES == 0; }
-
 // Row-resident shape: 16 register slots and 9 LDS slots per lane of 1024,
 // 25600 chunks (400 KiB) of a row on chip. Rows (half rows) that fit in the
 // register slots take an instance without the LDS slots: a load into an LDS
@@ -1731,16 +1726,13 @@ ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   if (!vec) return launch_rows_scalar<TI, TO, WRITE>(rp, stream);
   const int64_t nchunk = rp.V / Elem<TI>::VEC;
   if (nchunk <= 8192) return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
-  if constexpr (WRITE) {
-    if (nchunk <= kResChunks && !rowres_off()) return launch_rowres<TI, TO>(rp, stream);
-    // fp32 rows up to twice that: two workgroups per row, each half on chip
-    // (the host sets pair_part exactly for those rows)
-    if constexpr (Elem<TI>::BYTES == 4) {
-      if (rp.pair_part != nullptr && !rowres_off()) return launch_rows_pair<TI, TO>(rp, stream);
-    }
+  static_assert(WRITE, "the gradient call: forward-only rows take dispatch_forward");
+  if (nchunk <= kResChunks) return launch_rowres<TI, TO>(rp, stream);
+  // fp32 rows up to twice that: two workgroups per row, each half on chip
+  // (the host sets pair_part exactly for those rows)
+  if constexpr (Elem<TI>::BYTES == 4) {
+    if (rp.pair_part != nullptr) return launch_rows_pair<TI, TO>(rp, stream);
   }
-  if (nchunk <= 16384)
-    return launch_rows<TI, TO, 1024, 0, 0, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
   return launch_rows<TI, TO, 1024, 0, 4, 9, 4, WRITE, true, true, 1>(rp, stream, 64);
 }
 
@@ -2045,7 +2037,7 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
       uint32_t* sched = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + segment_ws_bytes(p));
       if (pair_rows(p)) {
         // pair_part is set exactly when the pair kernel runs (aligned rows)
-        if (vec && !ent_out && !rowres_off()) {
+        if (vec && !ent_out) {
           rp.pair_part = sched;
           rp.pair_split = (V / 4 / 2) * 4;   // a chunk boundary
           rp.tickets = sched + 8 * T;
