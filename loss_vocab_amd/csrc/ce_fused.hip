@@ -1932,6 +1932,8 @@ ce_status run_rows(const ce_problem* p, const void* logits, const int64_t* targe
   if (seg_loss_out && p->num_segments == 0) return CE_ERR_INVALID_ARG;
   if ((p->flags & CE_FLAG_SEGMENT_MEAN) && p->num_segments == 0) return CE_ERR_INVALID_ARG;
   if (T > INT32_MAX) return CE_ERR_UNSUPPORTED;  // segment offsets are int32
+  // two-workgroup rows deal 2 T tickets from a 32-bit counter
+  if (grad_out && pair_rows(p) && T > (int64_t{1} << 31) - (int64_t{1} << 20)) return CE_ERR_UNSUPPORTED;
   if (V > (int64_t{1} << 28)) return CE_ERR_UNSUPPORTED;  // in-row byte offsets are 32-bit
   if (T > 0 && (!logits || !targets || !loss_out)) return CE_ERR_INVALID_ARG;
   if (!std::isfinite(z_alpha) || !std::isfinite(grad_scale)) return CE_ERR_INVALID_ARG;
