@@ -51,6 +51,11 @@ constexpr int kNT = 2;                           // cache policy bits: non-tempo
 typedef const __attribute__((address_space(4))) int64_t kconst_i64;
 typedef const __attribute__((address_space(4))) int32_t kconst_i32;
 constexpr int kBufWord3 = 0x00020000;            // buffer descriptor word 3 (gfx9 raw buffer)
+// s_waitcnt immediate (gfx9 layout): wait until at most `vm` vector memory,
+// `exp` export and `lgkm` LDS/scalar-memory operations are outstanding.
+constexpr int waitcnt_imm(int vm, int exp, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (exp << 4) | (lgkm << 8);
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -1177,11 +1182,14 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       // out-of-range target: NaN loss and gradient row. (Both halves of a
       // pair decide alike; half 0 writes the row's loss.)
       if constexpr (DEAL) {
-        uint32_t kn = 0;
-        if (tid == 0) kn = take_ticket();
+        // The next ticket is taken and published before the row's stores go
+        // out: loads, atomics and stores share one in-order counter, so
+        // reading it after the fill would wait for every store of the fill.
+        // (Taking it and reading it in one thread-0 block also keeps the
+        // compiler from treating it as pending in the other waves.)
+        if (tid == 0) tick_sh[par] = take_ticket();
         fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true,
                             !PAIR || half == 0);
-        if (tid == 0) tick_sh[par] = kn;
         __syncthreads();
         k = read_ticket(par);
       } else {
@@ -1204,6 +1212,29 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
     const uint32_t vin = tid_r * 16u;
 
     // ---- every slot's load goes out now (read once: non-temporal) --------
+    // While an HBM -> LDS copy is outstanding the compiler cannot count the
+    // memory counter (the copy writes LDS through the vector memory path):
+    // the first use of a register slot then waits for every load of the row.
+    // Half rows issue their LDS copies first and wait for them explicitly
+    // before pass 1 (the oldest loads, so the register slots stay in flight
+    // and get per-slot waits): the half reaches its exchange sooner (151936-
+    // column fp32 rows 6.52 -> 6.45 ms). Whole rows issue them last and wait
+    // for the whole row (the copies-first order measured 0.5% slower on
+    // 201088-column bf16 rows, whose pass-1 latency is hidden by other CUs).
+    constexpr bool kCopiesFirst = PAIR;
+    auto issue_copies = [&]() {
+      // (every LDS slot is loaded, those past the end slot from the last
+      // chunk: loads on only some paths would make the first wait cover them)
+#pragma unroll
+      for (int j = 0; j < NLDS; ++j) {
+        // HBM -> LDS without a register round trip: lane l of a wave lands
+        // at base + 16 l, so slot j of thread tid is stage[j][tid].
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(zrow + min(vin + (NREG + j) * SLOT, c16_last)),
+            (__attribute__((address_space(3))) void*)(&stage[j][tid_r & ~63u]), 16, 0, kNT);
+      }
+    };
+    if constexpr (kCopiesFirst) issue_copies();
     u32x4 raw[NREG];
     {
       const __amdgpu_buffer_rsrc_t rin =
@@ -1212,16 +1243,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       for (int i = 0; i < NREG; ++i)
         raw[i] = __builtin_amdgcn_raw_buffer_load_b128(rin, min(vin + i * SLOT, c16_last), 0, kNT);
     }
-    // (every LDS slot is loaded, those past the end slot from the last chunk:
-    // loads on only some paths would make the first slot's wait cover them)
-#pragma unroll
-    for (int j = 0; j < NLDS; ++j) {
-      // HBM -> LDS without a register round trip: lane l of a wave lands
-      // at base + 16 l, so slot j of thread tid is stage[j][tid].
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(zrow + min(vin + (NREG + j) * SLOT, c16_last)),
-          (__attribute__((address_space(3))) void*)(&stage[j][tid_r & ~63u]), 16, 0, kNT);
-    }
+    if constexpr (!kCopiesFirst) issue_copies();
     [[maybe_unused]] int32_t sid = 0;
     if (p.seg_mean) sid = seg_ids[r];
     // The target logit: in pair mode its own load, issued behind the slots
@@ -1250,6 +1272,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
     // element in its slot too (in the one lane that holds it).
     auto fixed = [&](u32x4 v, int slot) -> u32x4 {
       if (slot == end_slot()) {
+        asm volatile("");                         // a branch, not selects in every slot
         const bool out = static_cast<uint32_t>(slot) * BLOCK + tid_r >= nchunk;
         v.x = out ? neg_w : v.x;
         v.y = out ? neg_w : v.y;
@@ -1279,6 +1302,11 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
 
     // ---- pass 1: register slots, then LDS slots, one online update each ----
     float mL = kNegInf, s = 0.f;
+    if constexpr (kCopiesFirst && NLDS > 0) {
+      // this wave's HBM -> LDS copies have landed (and the scalar reads of
+      // the row set-up); the register slots may still be in flight
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(NREG, 7, 0));
+    }
 #pragma unroll
     for (int i = 0; i < NREG; ++i) {
       if (i > end_slot()) break;
@@ -1288,7 +1316,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
     }
     if constexpr (NLDS > 0) {
       if (NREG <= end_slot()) {
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's HBM -> LDS copies have landed
+        if constexpr (!kCopiesFirst) __builtin_amdgcn_s_waitcnt(0);   // the copies have landed
 #pragma unroll
         for (int j = 0; j < NLDS; ++j) {
           if (NREG + j > end_slot()) break;
@@ -1307,6 +1335,11 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       }
       merge(mL, s, xv * kL2E, (xv == kNegInf) ? 0.f : 1.f);
     }
+    // Every load of the row has landed (slots past the end slot were issued
+    // with the others). Saying so here keeps the compiler from waiting for
+    // each slot's load again in pass 2, where its count would leave out the
+    // gradient stores issued in between and stall on them.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 7, 15));
     block_reduce<BLOCK>(mL, s, red_m, red_s, par, tid_r & 63u, tid_r >> 6);
     // (zt_sh is written before the reduction's barrier)
     const float zt = PAIR ? zt_ld : (owned ? zt_sh[par] : kNegInf);
