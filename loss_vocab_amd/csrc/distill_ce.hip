@@ -127,6 +127,28 @@ struct DistillParams {
   float z_alpha, kl_beta, grad_scale;
 };
 
+// A row's label with the mask folded in (ignore_index where the mask byte is
+// 0: a row counts exactly when its label is not ignore_index and its mask
+// byte is nonzero). Both are read-only for the call and are read through the
+// scalar cache; the mask byte within its aligned 4-byte word when that word
+// lies inside the mask, a plain byte load otherwise. (A vector load would be
+// counted with the previous row's gradient stores, and waiting for it would
+// wait for all of them.)
+__device__ __forceinline__ int64_t row_label(const DistillParams& p, int64_t r) {
+  const int64_t t = ((const __attribute__((address_space(4))) int64_t*)p.targets)[r];
+  if (p.mask == nullptr) return t;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p.mask + r);
+  const uintptr_t w = a & ~uintptr_t{3};
+  uint32_t m;
+  if (w >= reinterpret_cast<uintptr_t>(p.mask) && w + 4 <= reinterpret_cast<uintptr_t>(p.mask + p.T)) {
+    const uint32_t v = *(const __attribute__((address_space(4))) uint32_t*)w;
+    m = (v >> (8u * static_cast<uint32_t>(a & 3u))) & 0xffu;
+  } else {
+    m = p.mask[r];
+  }
+  return m != 0 ? t : p.ignore_index;
+}
+
 // Running (shift, sum) in log2 units plus the teacher's U.
 struct Part {
   float ms, ss;      // student non-target
@@ -267,8 +289,8 @@ __global__ __launch_bounds__(kBlock) void distill_rows_kernel(DistillParams p) {
   const int64_t nch = VEC ? V / 8 : 0;            // full 8-element chunks
   const int64_t tail0 = nch * 8;                  // first element of the tail
   for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x) {
-    const int64_t t = p.targets[r];
-    const bool valid = (t != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+    const int64_t t = row_label(p, r);
+    const bool valid = t != p.ignore_index;   // (the mask is folded into the label)
     const bool owned = t >= 0 && t < V;
     void* grow = p.grad ? static_cast<char*>(p.grad) + r * p.ld_g * Ld<TO>::BYTES : nullptr;
     if (!valid || !owned) {
@@ -488,17 +510,15 @@ __global__ __launch_bounds__(BLOCK) void distill_chunk_kernel(DistillParams p) {
   const uint32_t tail_begin = nchunk * W;
   const uint32_t nslot = (nchunk + BLOCK - 1) / BLOCK;
   const u32x4 neg4 = {Chunk<TI>::NEG, Chunk<TI>::NEG, Chunk<TI>::NEG, Chunk<TI>::NEG};
-  // Labels are read through the scalar cache (constant address space: the
-  // kernel never writes them), one row ahead, so a row does not open by
-  // waiting on a vector load (and with it on the previous row's stores).
-  typedef const __attribute__((address_space(4))) int64_t label_t;
-  const label_t* labels = (const label_t*)p.targets;
-  int64_t t_next = static_cast<int64_t>(blockIdx.x) < p.T ? labels[blockIdx.x] : 0;
+  // Labels (mask folded in) are read through the scalar cache, one row ahead,
+  // so a row does not open by waiting on a vector load (and with it on the
+  // previous row's stores).
+  int64_t t_next = static_cast<int64_t>(blockIdx.x) < p.T ? row_label(p, blockIdx.x) : 0;
   int par = 0;
   for (int64_t r = blockIdx.x; r < p.T; r += gridDim.x, par ^= 1) {
     const int64_t t64 = t_next;
-    if (r + gridDim.x < p.T) t_next = labels[r + gridDim.x];
-    const bool valid = (t64 != p.ignore_index) && (p.mask == nullptr || p.mask[r] != 0);
+    if (r + gridDim.x < p.T) t_next = row_label(p, r + gridDim.x);
+    const bool valid = t64 != p.ignore_index;   // (the mask is folded into the label)
     const bool owned = t64 >= 0 && t64 < static_cast<int64_t>(V);
     void* grow = p.grad ? static_cast<char*>(p.grad) + r * p.ld_g * static_cast<int64_t>(sizeof(TO))
                         : nullptr;

@@ -151,6 +151,23 @@ def test_in_place_and_mask():
             what="in place")
 
 
+@pytest.mark.parametrize("V,dtype", [(8192, torch.bfloat16), (70001, torch.bfloat16),
+                                     (30000, torch.float32)])
+@pytest.mark.parametrize("offset", [1, 3])
+def test_unaligned_mask(V, dtype, offset):
+    """A mask that starts at an odd address over 13 rows: its bytes are read
+    within aligned 4-byte words where the word lies inside the mask, by byte
+    at the ends (chunk kernel for the aligned rows, element kernel for the
+    odd row length)."""
+    zs, zt, t = _pair(13, V, dtype, seed=40 + offset)
+    buf = torch.ones(13 + 8, dtype=torch.uint8, device=DEV)
+    mask = buf[offset:offset + 13]
+    assert mask.data_ptr() % 4 == offset % 4
+    mask[[0, 3, 4, 7, 12]] = 0
+    t[6] = -100
+    compare(zs, zt, t, mask=mask, alpha=1e-4, beta=0.5, gamma=1 / 7, what=f"unaligned mask +{offset}")
+
+
 @pytest.mark.parametrize("name", ["cez_bf16_T8192_V32000_collapse",
                                   "ce_bf16_T16384_V128256_zipf_inplace",
                                   "cez_f32_T32768_V151936_peaked"])

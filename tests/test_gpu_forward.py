@@ -165,6 +165,22 @@ def test_forward_matches_fused_loss_and_mask():
     check_loss(_np(loss), to_np64(loss_f), "forward vs fused", rel=2e-6)
 
 
+@pytest.mark.parametrize("V,dtype", [(2050, torch.bfloat16), (140005, torch.bfloat16),
+                                     (70003, torch.float32)])
+def test_forward_unaligned_mask(V, dtype):
+    """A mask that starts at an odd address over 13 rows (bytes read within
+    aligned 4-byte words inside the mask, by byte at the ends)."""
+    g = torch.Generator(device=DEV).manual_seed(21)
+    z = (2 * torch.randn(13, V, generator=g, device=DEV)).to(dtype)
+    t = torch.randint(0, V, (13,), generator=g, device=DEV)
+    t[6] = -100
+    buf = torch.ones(13 + 8, dtype=torch.uint8, device=DEV)
+    mask = buf[3:16]
+    mask[[0, 3, 4, 7, 12]] = 0
+    compare_forward(z, t, mask=mask, alpha=1e-4, what="unaligned mask", pad=True)
+    compare_forward(z, t, mask=mask, alpha=1e-4, what="unaligned mask packed")
+
+
 def test_forward_without_entropy():
     """entropy_out NULL runs the plain forward; lse alone is still written."""
     import loss_vocab_amd as L

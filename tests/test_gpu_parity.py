@@ -176,6 +176,38 @@ def test_mask_array_and_ignore_index():
     compare_all(_inp(z, t, alpha=1e-4, gamma=1 / 59), mask=mask, what="mask")
 
 
+# A mask that starts at an odd address, over a row count that is not a
+# multiple of 4: the kernels read a mask byte within its aligned 4-byte word
+# when that word lies inside the mask, and with a byte load at the ends.
+# Masked rows at the first and last rows and next to word edges; each shape
+# runs one kernel tier (row kernel; row-resident in registers, with LDS
+# slots; fp32 half rows in pairs).
+MASK_TIER_CASES = [
+    ("rows_bf16", torch.bfloat16, 2050),
+    ("resident_reg_bf16", torch.bfloat16, 70001),
+    ("resident_lds_bf16", torch.bfloat16, 140005),
+    ("pair_f32", torch.float32, 110003),
+]
+
+
+@pytest.mark.parametrize("name,dtype,V", MASK_TIER_CASES, ids=[c[0] for c in MASK_TIER_CASES])
+@pytest.mark.parametrize("offset", [1, 3])
+def test_unaligned_mask(name, dtype, V, offset):
+    g = torch.Generator(device=DEV).manual_seed(31 + offset)
+    T = 13
+    z = (2 * torch.randn(T, V, generator=g, device=DEV)).to(dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    t[6] = -100
+    buf = torch.ones(T + 8, dtype=torch.uint8, device=DEV)
+    mask = buf[offset:offset + T]
+    assert mask.data_ptr() % 4 == offset % 4
+    mask[[0, 3, 4, 7, 12]] = 0
+    z[3] = float("nan")            # a masked row is never read
+    inp = _inp(z, t, alpha=1e-4, gamma=1 / 7)
+    compare_all(inp, mask=mask, what=f"unaligned mask {name}", pad=True)
+    compare_all(inp, mask=mask, what=f"unaligned mask {name} packed")
+
+
 @pytest.mark.parametrize("all_masked", [True, False])
 def test_all_or_none_masked(all_masked):
     g = torch.Generator(device=DEV).manual_seed(4)
