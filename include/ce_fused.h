@@ -105,8 +105,8 @@ typedef struct ce_problem {
 /* Device workspace (bytes) a call with this problem needs: room for a [T]
  * float NLL staging array and [S+1] segment offsets when S > 0; for the
  * gradient pass's row scheduling, 256 bytes (a ticket counter) when rows
- * hold 16385..25600 16-byte chunks (bf16: 131080..204807 columns, fp32:
- * 65540..102403), and for fp32 logits of 102404..204803 columns (two
+ * hold 8193..25600 16-byte chunks (bf16: 65544..204807 columns, fp32:
+ * 32772..102403), and for fp32 logits of 102404..204803 columns (two
  * workgroups per row) 32 bytes per row plus 8 (the counter and a give-up
  * count); plus 4096 bytes
  * under CE_FLAG_VALIDATE; zero otherwise. This is what a call that
@@ -184,7 +184,7 @@ ce_status ce_fused_fwd_bwd(const ce_problem* p,
  *  Returns CE_ERR_WORKSPACE when the call would need more than
  *  CE_NOALLOC_SCRATCH_BYTES (ce_workspace_bytes(p) for a gradient call; less
  *  without a gradient): with S segments, 4 T + 4 (S + 1) bytes (each rounded
- *  up to 256); with a gradient, 256 bytes for rows of 16385..25600 16-byte
+ *  up to 256); with a gradient, 256 bytes for rows of 8193..25600 16-byte
  *  chunks, or 32 T + 8 bytes for the two-workgroup fp32 rows; 4096 more
  *  under CE_FLAG_VALIDATE. That is up to about 2 million rows with
  *  segments, or 262143 rows of the two-workgroup fp32 mode. CE_ERR_INVALID_ARG when the stream belongs to another device than

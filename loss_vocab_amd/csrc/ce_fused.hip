@@ -1099,14 +1099,14 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 // during this row's gradient pass measured slower: it moves every read into
 // the gradient pass and leaves pass 1 with no memory traffic of its own.)
 //
-// With DEAL, rows are dealt out by a ticket counter in the workspace
-// (all-ones before the launch, so the first ticket is 0): a workgroup that
+// Rows are dealt out by a ticket counter in the workspace (all-ones before
+// the launch, so the first ticket is 0) to the resident workgroups: one that
 // finishes early takes more rows, which evens out rows of unequal cost
-// (ignored rows are only written). Without it, workgroup b takes rows b,
-// b + grid, ... . Measured on MI355X: dealing is faster for rows that use
-// the LDS slots (201088-column bf16 rows 8.95 -> 8.76 ms) and for pairs, the
-// fixed stride for rows held in registers alone (128256-column bf16 rows
-// 1.457 -> 1.339 ms). In pair mode (fp32 rows too long for one workgroup's chip
+// (ignored rows are only written), and the next row's loads go out right
+// behind this row's gradient stores. Measured on MI355X against a fixed
+// stride (workgroup b takes rows b, b + grid, ...): 201088-column bf16 rows
+// 8.95 -> 8.76 ms; 128256-column bf16 rows 1.318 -> 1.298 ms, and with no
+// ignored rows 1.575 -> 1.411 ms. In pair mode (fp32 rows too long for one workgroup's chip
 // space) the two halves of row r are tickets 2r and 2r + 1, and a
 // workgroup takes its next ticket only after its current half has exchanged
 // statistics with its partner. That makes the waits deadlock-free without
@@ -1124,10 +1124,9 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
 // count as -inf and store nothing; slots past the end slot load the last
 // chunk (one line per wave) and are not reduced or stored.
 // ---------------------------------------------------------------------------
-template <typename TI, typename TO, int NREG, int NLDS, int MODE, bool DEAL>
+template <typename TI, typename TO, int NREG, int NLDS, int MODE>
 __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
   static_assert(MODE == kFused || MODE == kPair, "the fused call, whole or half rows");
-  static_assert(DEAL || MODE == kFused, "pairs are dealt by ticket");
   constexpr int BLOCK = 1024;
   constexpr bool PAIR = MODE == kPair;
   constexpr int W = Elem<TI>::VEC;                 // elements per chunk
@@ -1171,13 +1170,10 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
   // value. Tickets are read back as scalars, so the row index and all that
   // derives from it stay uniform. (Tickets taken two rows ahead measured
   // slower.)
-  uint32_t k = blockIdx.x;
-  if constexpr (DEAL) {
-    if (tid == 0) tick_sh[0] = take_ticket();
-    __syncthreads();
-    k = read_ticket(0);
-    __syncthreads();                              // tick_sh[0] is rewritten by the first row
-  }
+  if (tid == 0) tick_sh[0] = take_ticket();
+  __syncthreads();
+  uint32_t k = read_ticket(0);
+  __syncthreads();                                // tick_sh[0] is rewritten by the first row
   int64_t r = ticket_row(k);
   int64_t t_next = r < p.T ? row_label(p, r) : 0;
   int par = 0;
@@ -1203,21 +1199,16 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
       // Ignored row: +0.0 everywhere, logits never read. Valid row with an
       // out-of-range target: NaN loss and gradient row. (Both halves of a
       // pair decide alike; half 0 writes the row's loss.)
-      if constexpr (DEAL) {
-        // The next ticket is taken and published before the row's stores go
-        // out: loads, atomics and stores share one in-order counter, so
-        // reading it after the fill would wait for every store of the fill.
-        // (Taking it and reading it in one thread-0 block also keeps the
-        // compiler from treating it as pending in the other waves.)
-        if (tid == 0) tick_sh[par] = take_ticket();
-        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true,
-                            !PAIR || half == 0);
-        __syncthreads();
-        k = read_ticket(par);
-      } else {
-        fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true);
-        k += gridDim.x;
-      }
+      // The next ticket is taken and published before the row's stores go
+      // out: loads, atomics and stores share one in-order counter, so
+      // reading it after the fill would wait for every store of the fill.
+      // (Taking it and reading it in one thread-0 block also keeps the
+      // compiler from treating it as pending in the other waves.)
+      if (tid == 0) tick_sh[par] = take_ticket();
+      fill_row<TO, BLOCK>(p, r, grow, V, valid ? __builtin_nanf("") : 0.f, true,
+                          !PAIR || half == 0);
+      __syncthreads();
+      k = read_ticket(par);
       r = ticket_row(k);
       t_next = r < p.T ? row_label(p, r) : 0;
       par ^= 1;
@@ -1274,7 +1265,7 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
     // 128256-column bf16 rows, level on the others).
     [[maybe_unused]] const float zt_ld = (PAIR && owned) ? Elem<TI>::load1(zrow, t) : kNegInf;
     [[maybe_unused]] uint32_t k_next = 0;          // thread 0: the next ticket
-    if (DEAL && !PAIR && tid == 0) k_next = take_ticket();
+    if (!PAIR && tid == 0) k_next = take_ticket();
 
     // Where the target sits: chunk ct, element kt, slot st, lane `mine`.
     const uint32_t ct = t / W;
@@ -1434,12 +1425,12 @@ __global__ __launch_bounds__(1024) void ce_rowres_kernel(RowParams p) {
         epi[par][0] = o.g_t;
         epi[par][1] = o.cnt;
         epi[par][2] = o.kl;
-        if constexpr (DEAL) tick_sh[par] = k_next;
+        tick_sh[par] = k_next;
       }
     }
     __syncthreads();
     const float cnt = epi[par][1], kl = epi[par][2];
-    k = DEAL ? read_ticket(par) : k + gridDim.x;
+    k = read_ticket(par);
     t_next = ticket_row(k) < p.T ? row_label(p, ticket_row(k)) : 0;
     const int64_t r_next = ticket_row(k);
 
@@ -1699,26 +1690,23 @@ __global__ __launch_bounds__(256) void ce_fill_u32_kernel(uint32_t* __restrict__
 constexpr int kResReg = 16, kResLds = 9;
 constexpr int64_t kResChunks = int64_t{kResReg + kResLds} * 1024;
 constexpr int64_t kResRegChunks = int64_t{kResReg} * 1024;
+// Rows of up to this many chunks take the row kernel (512 lanes, the whole
+// row in LDS up to 4096 chunks); longer ones the row-resident kernel.
+constexpr int64_t kRowsChunks = 8192;
 
-// Whole rows on the row-resident kernel, one workgroup per CU. Rows that use
-// the LDS slots are dealt by ticket: the counter is set to all-ones by a
-// one-block fill kernel first (capturable), and the grid is the resident
-// workgroups only -- every workgroup beyond them would launch after the
-// tickets run out, only to take one past the end (16384 workgroups instead of
-// 256 measured 8.77 vs 8.62 ms on 201088-column bf16 rows). Rows held in
-// registers alone keep a fixed stride over up to 64 workgroups per CU, so the
-// hardware deals them.
+// Whole rows on the row-resident kernel, one workgroup per CU, dealt by
+// ticket: the counter is set to all-ones by a one-block fill kernel first
+// (capturable), and the grid is the resident workgroups only -- every
+// workgroup beyond them would launch after the tickets run out, only to take
+// one past the end (16384 workgroups instead of 256 measured 8.77 vs 8.62 ms
+// on 201088-column bf16 rows).
 template <typename TI, typename TO, int NLDS>
 ce_status launch_rowres_shape(const RowParams& rp, hipStream_t stream) {
-  if constexpr (NLDS > 0) {
-    if (rp.tickets == nullptr) return CE_ERR_WORKSPACE;
-    hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(1), dim3(256), 0, stream, rp.tickets, int64_t{1},
-                       ~0u);
-    if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
-  }
+  if (rp.tickets == nullptr) return CE_ERR_WORKSPACE;
+  hipLaunchKernelGGL(ce_fill_u32_kernel, dim3(1), dim3(256), 0, stream, rp.tickets, int64_t{1}, ~0u);
+  if (hipGetLastError() != hipSuccess) return CE_ERR_HIP;
   static std::atomic<int> occ{0};
-  return launch_persistent(ce_rowres_kernel<TI, TO, kResReg, NLDS, kFused, (NLDS > 0)>, 1024, occ,
-                           rp, stream, NLDS > 0 ? 0 : 64);
+  return launch_persistent(ce_rowres_kernel<TI, TO, kResReg, NLDS, kFused>, 1024, occ, rp, stream);
 }
 
 template <typename TI, typename TO>
@@ -1735,7 +1723,7 @@ ce_status launch_rowres(const RowParams& rp, hipStream_t stream) {
 // two resident workgroups.
 template <typename TI, typename TO, int NLDS>
 ce_status launch_pair_shape(const RowParams& rp, hipStream_t stream) {
-  auto kern = ce_rowres_kernel<TI, TO, kResReg, NLDS, kPair, true>;
+  auto kern = ce_rowres_kernel<TI, TO, kResReg, NLDS, kPair>;
   static std::atomic<int> occ{0};
   int per_cu = occ.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
@@ -1773,19 +1761,24 @@ ce_status launch_rows_scalar(const RowParams& rp, hipStream_t stream) {
 // Pick a kernel variant for (input type, output type, vector path or not).
 // Kernel shape by row length (chunks of 16 bytes), measured on MI355X; the
 // more of a row stays on chip, the less of it pass 2 reads again:
-//  * up to 8192 chunks: 512 lanes, 8 slots per lane in LDS (64 KiB: all of
-//    a row of up to 4096 chunks), the rest streamed 2 slots per step;
-//  * up to 16384 chunks: 1024 lanes, 9 LDS slots per lane (144 KiB), the
-//    rest streamed 4 slots per step with one online update per slot;
-//  * longer rows: 1024 lanes, 13 slots per lane on chip (4 VGPR + 9 LDS:
-//    208 KiB of a row), the rest streamed with one online update per slot.
-// All use one workgroup per row until the grid reaches 64 per compute unit
-// (in practice the LDS footprint bounds the workgroups per CU first).
+//  * up to 8192 chunks: the row kernel, 512 lanes, 8 slots per lane in LDS
+//    (64 KiB: all of a row of up to 4096 chunks), the rest streamed 2 slots
+//    per step, one workgroup per row (up to 64 per CU in the grid; the LDS
+//    footprint lets two run at once);
+//  * 8193..25600 chunks: the row-resident kernel, the whole row on chip
+//    (16 register slots, and 9 LDS slots past 16384 chunks), one workgroup
+//    per CU, rows dealt by ticket;
+//  * fp32 rows of 25601..51200 chunks: the row-resident kernel in pair mode,
+//    two workgroups per row;
+//  * longer rows: the row kernel, 1024 lanes, 13 slots per lane on chip
+//    (4 VGPR + 9 LDS: 208 KiB of a row), the rest streamed with one online
+//    update per slot.
 template <typename TI, typename TO, bool WRITE>
 ce_status dispatch_rows(const RowParams& rp, bool vec, hipStream_t stream) {
   if (!vec) return launch_rows_scalar<TI, TO, WRITE>(rp, stream);
   const int64_t nchunk = rp.V / Elem<TI>::VEC;
-  if (nchunk <= 8192) return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
+  if (nchunk <= kRowsChunks)
+    return launch_rows<TI, TO, 512, 0, 0, 8, 2, WRITE, true, true>(rp, stream, 64);
   static_assert(WRITE, "the gradient call: forward-only rows take dispatch_forward");
   if (nchunk <= kResChunks) return launch_rowres<TI, TO>(rp, stream);
   // fp32 rows up to twice that: two workgroups per row, each half on chip
@@ -1951,11 +1944,11 @@ uint32_t pair_spin_limit() {
   const unsigned long v = std::strtoul(e, &end, 10);
   return (end != nullptr && *end == '\0' && v <= kPairSpin) ? static_cast<uint32_t>(v) : kPairSpin;
 }
-// Rows dealt by ticket on the row-resident kernel: those that use its LDS
-// slots (rows held in registers alone take a fixed stride).
+// Whole rows on the row-resident kernel (dealt by ticket): 8193..25600
+// chunks of 16 bytes.
 bool rowres_rows(const ce_problem* p) {
   const int64_t nchunk = p->V / (p->logits_dtype == CE_DTYPE_F32 ? 4 : 8);
-  return nchunk > kResRegChunks && nchunk <= kResChunks;
+  return nchunk > kRowsChunks && nchunk <= kResChunks;
 }
 size_t sched_ws_bytes(const ce_problem* p, bool grad = true) {
   if (!grad || p->T == 0) return 0;

@@ -422,7 +422,7 @@ def test_valid_calls_without_a_device_return_ce_err_hip(tmp_path):
 
 def test_forward_only_needs_no_pair_slots():
     """The gradient pass's row scheduling space: a 4-byte ticket counter
-    (256 bytes) for rows of 16385..25600 16-byte chunks, and for fp32 rows of
+    (256 bytes) for rows of 8193..25600 16-byte chunks, and for fp32 rows of
     25601..51200 chunks (two workgroups per row) 32 bytes of exchange slots
     per row before it, and a give-up count after it. ce_workspace_bytes counts it; a call without a
     gradient (fused with grad_out NULL, or the forward entry) does not ask
@@ -432,12 +432,11 @@ def test_forward_only_needs_no_pair_slots():
     p = _problem(T=1000, V=110000)
     assert L.workspace_bytes(p) == (1000 * 32 + 8 + 255) // 256 * 256
     assert L.workspace_bytes(_problem(T=1000, V=204800)) > 256
-    for v, want in ((32768, 0), (32772, 0), (65536, 0), (65540, 256), (70000, 256),
-                    (102400, 256), (204804, 0),
-                    (300000, 0)):
+    for v, want in ((32768, 0), (32771, 0), (32772, 256), (65536, 256), (65540, 256),
+                    (70000, 256), (102400, 256), (204804, 0), (300000, 0)):
         assert L.workspace_bytes(_problem(T=1000, V=v)) == want, v
-    for v, want in ((65536, 0), (65544, 0), (131072, 0), (131080, 256), (201088, 256),
-                    (204800, 256), (204808, 0)):
+    for v, want in ((65536, 0), (65543, 0), (65544, 256), (131072, 256), (131080, 256),
+                    (201088, 256), (204800, 256), (204808, 0)):
         assert L.workspace_bytes(_problem(T=1000, V=v, dt=1)) == want, v
     p0 = _problem(T=0, V=110000)
     assert _call(p0, grad=A_GRAD) == 0 and _fwd(p0) == 0
