@@ -903,14 +903,27 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       // no pass 1
     } else if constexpr (PF) {
       // Two groups in flight: group B's loads run while group A is reduced.
+      // A group is loaded only if it holds chunks of the row: a load left
+      // unused at the end would still be in flight at the next row's start,
+      // where waiting for it would also wait for this row's gradient stores.
       if (NON * BLOCK < nchunk) {
         u32x4 ra[U], rb[U];
-        load_group(ra, NON * BLOCK, load_slot);
-        for (uint32_t b = NON * BLOCK; b < nchunk; b += 2 * U * BLOCK) {
+        uint32_t b = NON * BLOCK;
+        load_group(ra, b, load_slot);
+        for (;;) {
+          if (b + U * BLOCK >= nchunk) {
+            stream1(ra, b);
+            break;
+          }
           load_group(rb, b + U * BLOCK, load_slot);
           stream1(ra, b);
+          if (b + 2 * U * BLOCK >= nchunk) {
+            stream1(rb, b + U * BLOCK);
+            break;
+          }
           load_group(ra, b + 2 * U * BLOCK, load_slot);
           stream1(rb, b + U * BLOCK);
+          b += 2 * U * BLOCK;
         }
       }
     } else {
@@ -931,6 +944,10 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
       }
     }
 
+    // Every load of pass 1 has landed. Saying so keeps the compiler from
+    // assuming some of them may still be in flight at the next row's start,
+    // where it would otherwise wait for every gradient store of this row.
+    if constexpr (MODE != kGrad) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 7, 15));
     if constexpr (ENT) {
       block_reduce3<BLOCK>(mL, s, hs, red_m, red_s, red_u, par, lane, wid);
     } else if constexpr (MODE != kGrad) {
@@ -1051,14 +1068,25 @@ __global__ __launch_bounds__(BLOCK) void ce_rows_kernel(RowParams p) {
         }
       };
       if constexpr (PF) {
+        // (as in pass 1: only groups that hold chunks of the row are loaded)
         if (NON * BLOCK < nchunk) {
           u32x4 ra[U], rb[U];
-          load_group(ra, NON * BLOCK, load_slot_last_use);
-          for (uint32_t b = NON * BLOCK; b < nchunk; b += 2 * U * BLOCK) {
+          uint32_t b = NON * BLOCK;
+          load_group(ra, b, load_slot_last_use);
+          for (;;) {
+            if (b + U * BLOCK >= nchunk) {
+              stream2(ra, b);
+              break;
+            }
             load_group(rb, b + U * BLOCK, load_slot_last_use);
             stream2(ra, b);
+            if (b + 2 * U * BLOCK >= nchunk) {
+              stream2(rb, b + U * BLOCK);
+              break;
+            }
             load_group(ra, b + 2 * U * BLOCK, load_slot_last_use);
             stream2(rb, b + U * BLOCK);
+            b += 2 * U * BLOCK;
           }
         }
       } else {
