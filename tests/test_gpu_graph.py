@@ -145,6 +145,36 @@ def test_long_fp32_rows_replay():
     _replay_matches(g, (loss, grad), eager, "long fp32 rows")
 
 
+@pytest.mark.parametrize("V", [70001, 140005], ids=["registers", "registers_and_lds"])
+def test_row_resident_rows_replay(V):
+    """Whole rows of 8193..25600 chunks: one workgroup per CU takes rows in
+    ticket order (a fill kernel resets the counter inside the call, so the
+    call records into a graph). Ignored rows take their next ticket before
+    their zero fill. Every replay equals the eager call bit for bit: which
+    workgroup takes a row does not change the row's arithmetic."""
+    import loss_vocab_amd as L
+    gen = torch.Generator(device=DEV).manual_seed(8)
+    T = 700
+    # 16-byte aligned rows (ld V + 7), as the row-resident kernel needs
+    z = torch.empty(T, V + 7, device=DEV, dtype=torch.bfloat16)[:, :V]
+    z.copy_(torch.randn(T, V, generator=gen, device=DEV) * 2)
+    t = torch.randint(0, V, (T,), generator=gen, device=DEV)
+    t[::6] = -100
+    loss = torch.empty(T, device=DEV)
+    grad = torch.empty(T, V + 7, device=DEV, dtype=torch.bfloat16)[:, :V]
+    ws = torch.empty(max(1, L.workspace_bytes(z)), dtype=torch.uint8, device=DEV)
+    assert L.workspace_bytes(z) > 0, "row-resident rows are dealt by a ticket in the workspace"
+
+    def call():
+        L.ce_fused_fwd_bwd(z, t, None, None, 1e-4, 1.0 / T, loss, None, grad, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = (loss.clone(), grad.clone())
+    g = _capture(call)
+    _replay_matches(g, (loss, grad), eager, f"row-resident rows V={V}")
+
+
 def _capture(call):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
