@@ -1,0 +1,84 @@
+"""Seeded random configurations of the fused call against the fp64 oracle.
+
+Each case draws, from its own seed: the logits dtype, a row length from one
+kernel tier (row kernel, row-resident rows in registers or with LDS slots,
+two-workgroup fp32 rows, the long-row kernel), a row count, the gradient
+dtype or an in-place gradient, 16-byte-aligned padded rows or packed ones, a
+mask (starting at an odd address) or none, ignored rows, confident rows, the
+z-loss weight and segments with or without the segment mean. Every output is
+held to the same bars as the hand-written parity cases (per-row loss,
+segment sums, every gradient element, ignored rows bit-exact).
+"""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from test_gpu_parity import _inp, compare_all
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# Row lengths (elements) per kernel tier: the row kernel (two ranges), the
+# row-resident kernel in registers and with LDS slots, fp32 rows on two
+# workgroups, and the long-row kernel.
+TIERS = {
+    torch.float32: [(1, 300), (301, 32771), (32772, 65536), (65537, 102403), (102404, 204803),
+                    (204804, 230000)],
+    torch.bfloat16: [(1, 300), (301, 65543), (65544, 131072), (131073, 204807), (204808, 240000)],
+}
+# CE_FUZZ_CASES raises the number of cases for a longer search (default 32).
+SEEDS = list(range(int(os.environ.get("CE_FUZZ_CASES", "32"))))
+
+
+def _case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    dtype = (torch.float32, torch.bfloat16)[seed % 2]
+    tiers = TIERS[dtype]
+    lo, hi = tiers[(seed // 2) % len(tiers)]
+    V = int(rng.integers(lo, hi + 1))
+    T = int(rng.integers(1, 33 if V < 70000 else 10))
+    sigma = float(rng.choice([0.5, 2.0, 4.0]))
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    z = (torch.randn(T, V, generator=g, device=DEV) * sigma).to(dtype)
+    t = torch.randint(0, V, (T,), generator=g, device=DEV)
+    ign = rng.random(T) < 0.2
+    t[torch.as_tensor(ign, device=DEV)] = -100
+    # a few confident rows: the target raised above the row maximum
+    for r in np.flatnonzero(rng.random(T) < 0.2):
+        if int(t[r]) >= 0:
+            z[r, int(t[r])] = (z[r].float().max() + float(rng.uniform(5.0, 40.0))).to(dtype)
+    mask = None
+    if rng.random() < 0.5:
+        off = int(rng.integers(1, 4))
+        buf = torch.ones(T + 8, dtype=torch.uint8, device=DEV)
+        mask = buf[off:off + T]
+        mask[torch.as_tensor(rng.random(T) < 0.25, device=DEV)] = 0
+    seg, S, seg_mean = None, 0, False
+    if rng.random() < 0.35 and T > 1:
+        S = int(rng.integers(1, T + 1))
+        ids = np.sort(rng.integers(0, S, T)).astype(np.int32)
+        seg = torch.as_tensor(ids, device=DEV)
+        seg_mean = bool(rng.random() < 0.5)
+    alpha = float(rng.choice([0.0, 1e-4]))
+    n_valid = max(1, int((~ign).sum()))
+    inp = _inp(z, t, alpha=alpha, gamma=1.0 / n_valid, seg=seg, S=S, seg_mean=seg_mean)
+    in_place = bool(rng.random() < 0.25)
+    grad_dtype = None if in_place else (torch.float32, torch.bfloat16, dtype)[int(rng.integers(3))]
+    pad = bool(rng.random() < 0.5)
+    desc = (f"seed={seed} {str(dtype)[6:]} T={T} V={V} sigma={sigma} mask={mask is not None} S={S} "
+            f"seg_mean={seg_mean} alpha={alpha} grad={'in place' if in_place else str(grad_dtype)[6:]} "
+            f"pad={pad}")
+    return inp, mask, grad_dtype, in_place, pad, desc
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_fused_call(seed):
+    inp, mask, grad_dtype, in_place, pad, desc = _case(seed)
+    print(f"[fuzz] {desc}", flush=True)
+    compare_all(inp, grad_dtype=grad_dtype, in_place=in_place, mask=mask, what=f"fuzz {desc}", pad=pad)
