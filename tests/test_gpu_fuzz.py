@@ -1,4 +1,4 @@
-"""Seeded random configurations of the fused call against the fp64 oracle.
+"""Seeded random configurations of every call against the fp64 oracle.
 
 Each case draws, from its own seed: the logits dtype, a row length from one
 kernel tier (row kernel, row-resident rows in registers or with LDS slots,
@@ -7,7 +7,10 @@ dtype or an in-place gradient, 16-byte-aligned padded rows or packed ones, a
 mask (starting at an odd address) or none, ignored rows, confident rows, the
 z-loss weight and segments with or without the segment mean. Every output is
 held to the same bars as the hand-written parity cases (per-row loss,
-segment sums, every gradient element, ignored rows bit-exact).
+segment sums, every gradient element, ignored rows bit-exact). The same
+draws feed the forward-only call, the split form (random shard counts and
+alignments) and the distillation child (a teacher of the same dtype, random
+weight).
 """
 
 from __future__ import annotations
@@ -18,7 +21,11 @@ import numpy as np
 import pytest
 import torch
 
+from parity_utils import run_oracle, to_np64
+from test_gpu_distill import compare as compare_distill
+from test_gpu_forward import compare_forward
 from test_gpu_parity import _inp, compare_all
+from test_gpu_split import _split_case
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +81,55 @@ def _case(seed):
     desc = (f"seed={seed} {str(dtype)[6:]} T={T} V={V} sigma={sigma} mask={mask is not None} S={S} "
             f"seg_mean={seg_mean} alpha={alpha} grad={'in place' if in_place else str(grad_dtype)[6:]} "
             f"pad={pad}")
-    return inp, mask, grad_dtype, in_place, pad, desc
+    return dict(inp=inp, mask=mask, grad_dtype=grad_dtype, in_place=in_place, pad=pad, desc=desc,
+                rng=rng, dtype=dtype, n_valid=n_valid)
 
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_fuzz_fused_call(seed):
-    inp, mask, grad_dtype, in_place, pad, desc = _case(seed)
-    print(f"[fuzz] {desc}", flush=True)
-    compare_all(inp, grad_dtype=grad_dtype, in_place=in_place, mask=mask, what=f"fuzz {desc}", pad=pad)
+    c = _case(seed)
+    print(f"[fuzz] {c['desc']}", flush=True)
+    compare_all(c["inp"], grad_dtype=c["grad_dtype"], in_place=c["in_place"], mask=c["mask"],
+                what=f"fuzz {c['desc']}", pad=c["pad"])
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_forward(seed):
+    c = _case(seed)
+    inp = c["inp"]
+    print(f"[fuzz forward] {c['desc']}", flush=True)
+    compare_forward(inp["logits"], inp["targets"], mask=c["mask"], seg=inp["segment_ids"],
+                    S=inp["num_segments"], alpha=inp["z_alpha"], what=f"fuzz forward {c['desc']}",
+                    pad=c["pad"])
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_split(seed):
+    import loss_vocab_amd as L
+    c = _case(seed)
+    inp, rng = c["inp"], c["rng"]
+    z, t = inp["logits"], inp["targets"]
+    T, V = z.shape
+    shards = int(rng.integers(1, 5))
+    align = int(rng.choice([1, 8 if c["dtype"] == torch.bfloat16 else 4]))
+    seg, S = inp["segment_ids"], inp["num_segments"]
+    print(f"[fuzz split] {c['desc']} shards={shards} align={align}", flush=True)
+    ref = run_oracle(to_np64(z), t.cpu().numpy(), segment_ids=None if seg is None else seg.cpu().numpy(),
+                     num_segments=S, z_alpha=inp["z_alpha"], grad_scale=inp["grad_scale"],
+                     segment_mean=S > 0)
+    _split_case(L, z, t, seg, S, shards, align, inp["z_alpha"], inp["grad_scale"], c["dtype"], ref,
+                c["pad"])
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_distill(seed):
+    c = _case(seed)
+    inp, rng = c["inp"], c["rng"]
+    zs, t = inp["logits"], inp["targets"]
+    g = torch.Generator(device=DEV).manual_seed(10_000 + seed)
+    zt = (torch.randn(zs.shape, generator=g, device=DEV) * float(rng.choice([0.5, 2.0]))).to(zs.dtype)
+    beta = float(rng.choice([0.0, 0.5, 1.0]))
+    print(f"[fuzz distill] {c['desc']} beta={beta}", flush=True)
+    compare_distill(zs, zt, t, mask=c["mask"], alpha=inp["z_alpha"], beta=beta, gamma=inp["grad_scale"],
+                    grad_dtype=c["grad_dtype"], in_place=c["in_place"], what=f"fuzz distill {c['desc']}",
+                    pad=c["pad"])
