@@ -185,7 +185,21 @@ static_assert(kStages <= 4 && 2 * kLoadsPerStage <= 63, "vmcnt holds the loads i
 // acc[mi][ni] covers rows wm*kRW + mi*32 + {8(q/4) + 4(lane/32) + q%4} and
 // column wn*128 + ni*32 + lane%32 of the tile (q = register index 0..15).
 // KMASK: K is not a multiple of kBK, so the last stage masks its tail.
+// The first kStages - 1 stages of a tile's operands, issued ahead of its
+// products (by tile_product itself, or earlier by the caller with
+// PREISSUED set, once no wave reads the stages any more).
 template <bool KMASK>
+__device__ __forceinline__ void issue_first_stages(const GemmParams& p, Stages& s, int64_t m0,
+                                                   int64_t n0) {
+  const __amdgpu_buffer_rsrc_t ra = window(p.a, m0), rb = window(p.b, n0);
+  const int64_t nk = (p.K + kBK - 1) / kBK;
+  for (int64_t j = 0; j < kStages - 1 && j < nk; ++j) {
+    load_operand<KMASK>(ra, p.a, p.K, j * kBK, s.a[j]);
+    load_operand<KMASK>(rb, p.b, p.K, j * kBK, s.b[j]);
+  }
+}
+
+template <bool KMASK, bool PREISSUED = false>
 __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int64_t m0,
                                              int64_t n0, f32x16 (&acc)[kMI][kNI]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -200,10 +214,7 @@ __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int
   const __amdgpu_buffer_rsrc_t ra = window(p.a, m0), rb = window(p.b, n0);
   const int64_t nk = (p.K + kBK - 1) / kBK;
   // prologue: stages 0 .. kStages - 2 in flight, wait for stage 0
-  for (int64_t j = 0; j < kStages - 1 && j < nk; ++j) {
-    load_operand<KMASK>(ra, p.a, p.K, j * kBK, s.a[j]);
-    load_operand<KMASK>(rb, p.b, p.K, j * kBK, s.b[j]);
-  }
+  if (!PREISSUED) issue_first_stages<KMASK>(p, s, m0, n0);
   wait_stages_left(std::min<int64_t>(kStages - 2, nk - 1));
   __syncthreads();
   for (int64_t kt = 0; kt < nk; ++kt) {
@@ -280,77 +291,125 @@ __device__ __forceinline__ void merge(float& mL, float& s, float m2, float s2) {
 
 // Statistics: grid = tiles_m * n_ranges, range = block % n_ranges (so the
 // workgroups of one XCD walk one range and share its weight tiles); each
-// walks the vocabulary tiles of its range. Per tile and band, thread
-// (row = tid / kTPR, part = tid % kTPR) reduces kCPT columns of one row.
+// walks the vocabulary tiles of its range for 256 rows. The products are
+// formed transposed, C^T = W X^T, so that a lane holds few rows (4: row m0 +
+// wn * 128 + ni * 32 + lane % 32) and many vocabulary columns of each (32 per
+// tile: wm * 64 + mi * 32 + 8 (q / 4) + 4 (lane / 32) + q % 4), and keeps the
+// rows' online (shift, sum) statistics in registers across the range; lanes and
+// waves holding the same rows are merged once at the end. The next tile's
+// first stage is in flight while a tile's statistics are formed. A tile takes
+// the masked path only when a row's target lies among a wave's columns or the
+// tile passes the vocabulary's end.
 template <bool KMASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void lm_stats_kernel(
     GemmParams p) {
+  static_assert(kWaves == 8 && kMI == 2, "statistics layout: 8 waves of 64 x 128");
   __shared__ __align__(16) Stages s;
-  float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
   const int range = blockIdx.x % p.n_ranges;
   const int mt = blockIdx.x / p.n_ranges;
   const int64_t per = (p.tiles_n + p.n_ranges - 1) / p.n_ranges;
   const int64_t nt0 = range * per, nt1 = std::min<int64_t>(p.tiles_n, nt0 + per);
   const int64_t m0 = static_cast<int64_t>(mt) * kBM;
-  const int row = threadIdx.x / kTPR, part = threadIdx.x % kTPR;
-  int64_t t[4];
-  float mL[4], sum[4], zt[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  // operands swapped: weight rows on the matrix-core rows, hidden rows on its columns
+  GemmParams q = p;
+  q.a = p.b;
+  q.b = p.a;
+  int64_t t[kNI];
+  float mL[kNI], sum[kNI], zt[kNI];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int64_t gr = m0 + b * kBand + row;
-    t[b] = gr < p.M ? p.targets[gr] : -1;
-    mL[b] = kNegInf;
-    sum[b] = 0.f;
-    zt[b] = kNegInf;
+  for (int ni = 0; ni < kNI; ++ni) {
+    const int64_t gr = m0 + wn * 128 + ni * 32 + (lane & 31);
+    t[ni] = gr < p.M ? p.targets[gr] : -1;
+    mL[ni] = kNegInf;
+    sum[ni] = 0.f;
+    zt[ni] = kNegInf;
   }
+  const int vrow = wm * 64 + 4 * (lane >> 5);   // + mi * 32 + 8 (q / 4) + q % 4
   f32x16 acc[kMI][kNI];
+  if (nt0 < nt1) issue_first_stages<KMASK>(q, s, nt0 * kBN, m0);
   for (int64_t nt = nt0; nt < nt1; ++nt) {
     const int64_t n0 = nt * kBN;
-    tile_product<KMASK>(p, s, m0, n0, acc);
-    const int64_t c0 = n0 + part * kCPT;
-    const int64_t nv = std::min<int64_t>(kCPT, p.N - c0);   // columns inside the vocabulary
+    tile_product<KMASK, true>(q, s, n0, m0, acc);
+    if (nt + 1 < nt1) issue_first_stages<KMASK>(q, s, n0 + kBN, m0);
+    const int64_t w0 = n0 + wm * 64;
+    bool hit = false;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      band_to_lds(cs, acc, b);
-      __syncthreads();
-      // two reads of the row's columns: masked max, then the sum
-      const int64_t tl = t[b] - c0;
-      const float* crow = &cs[row][part * kCPT];
-      if (tl >= 0 && tl < kCPT) zt[b] = crow[tl];
-      float gmax = kNegInf;
-#pragma unroll 16
-      for (int j = 0; j < kCPT; ++j) gmax = fmaxf(gmax, (j < nv && j != tl) ? crow[j] : kNegInf);
-      const float mn = fmaxf(mL[b], gmax * kL2E);
-      if (mn != kNegInf) {
-        float acc_s = 0.f;
-#pragma unroll 16
-        for (int j = 0; j < kCPT; ++j) {
-          const float v = (j < nv && j != tl) ? crow[j] : kNegInf;
-          acc_s += fexp2(__builtin_fmaf(v, kL2E, -mn));
-        }
-        sum[b] = (mL[b] == kNegInf ? 0.f : sum[b] * fexp2(mL[b] - mn)) + acc_s;
-        mL[b] = mn;
+    for (int ni = 0; ni < kNI; ++ni) hit |= t[ni] >= w0 && t[ni] < w0 + 64;
+    const bool masked = __builtin_amdgcn_ballot_w64(hit) != 0 || n0 + kBN > p.N;
+    if (masked) {
+      // the target's logit is taken out of the sum, columns past the vocabulary count nothing
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t tl = t[ni] - (n0 + vrow);
+        const int64_t cend = p.N - (n0 + vrow);
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int c = mi * 32 + 8 * (e >> 2) + (e & 3);
+            const float v = acc[mi][ni][e];
+            if (c == tl) zt[ni] = v;
+            acc[mi][ni][e] = (c < cend && c != tl) ? v : kNegInf;
+          }
       }
-      __syncthreads();   // the band is rewritten next (or the stages reloaded)
+    }
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      float gmax = acc[0][ni][0];
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) gmax = fmaxf(gmax, acc[mi][ni][e]);
+      const float mn = fmaxf(mL[ni], gmax * kL2E);
+      if (mn != kNegInf) {
+        float a = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) a += fexp2(__builtin_fmaf(acc[mi][ni][e], kL2E, -mn));
+        sum[ni] = (mL[ni] == kNegInf ? 0.f : sum[ni] * fexp2(mL[ni] - mn)) + a;
+        mL[ni] = mn;
+      }
     }
   }
-  // the kTPR parts of a row sit in adjacent lanes
+  // lanes l and l ^ 32 hold the same rows
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int ni = 0; ni < kNI; ++ni) {
+    const float m2 = __shfl_xor(mL[ni], 32, 64);
+    const float s2 = __shfl_xor(sum[ni], 32, 64);
+    const float z2 = __shfl_xor(zt[ni], 32, 64);
+    merge(mL[ni], sum[ni], m2, s2);
+    zt[ni] = fmaxf(zt[ni], z2);
+  }
+  // the four wave rows wm hold the same rows: merged through LDS in a fixed order
+  float (*red)[kBM][3] = reinterpret_cast<float (*)[kBM][3]>(&s);
+  __syncthreads();
+  if (lane < 32) {
 #pragma unroll
-    for (int off = 1; off < kTPR; off <<= 1) {
-      const float m2 = __shfl_xor(mL[b], off, 64);
-      const float s2 = __shfl_xor(sum[b], off, 64);
-      const float z2 = __shfl_xor(zt[b], off, 64);
-      merge(mL[b], sum[b], m2, s2);
-      zt[b] = fmaxf(zt[b], z2);
+    for (int ni = 0; ni < kNI; ++ni) {
+      float* r = red[wm][wn * 128 + ni * 32 + lane];
+      r[0] = mL[ni];
+      r[1] = sum[ni];
+      r[2] = zt[ni];
     }
-    const int64_t gr = m0 + b * kBand + row;
-    if (part == 0 && gr < p.M) {
+  }
+  __syncthreads();
+  if (threadIdx.x < kBM) {
+    const int row = threadIdx.x;
+    float m = red[0][row][0], sm = red[0][row][1], z = red[0][row][2];
+#pragma unroll
+    for (int w = 1; w < kWM; ++w) {
+      merge(m, sm, red[w][row][0], red[w][row][1]);
+      z = fmaxf(z, red[w][row][2]);
+    }
+    const int64_t gr = m0 + row;
+    if (gr < p.M) {
       float* st = p.stats + 3 * (static_cast<int64_t>(range) * p.M + gr);
-      st[0] = mL[b];
-      st[1] = sum[b];
-      st[2] = zt[b];
+      st[0] = m;
+      st[1] = sm;
+      st[2] = z;
     }
   }
 }
