@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -33,6 +34,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256;          // tile rows (A rows)
@@ -199,6 +201,15 @@ __device__ __forceinline__ void issue_first_stages(const GemmParams& p, Stages& 
   }
 }
 
+// Stage 0 alone, with no test of K (with K = 0 the products never read it):
+// what PREISSUED expects of a two-stage ring, issued unconditionally.
+template <bool KMASK>
+__device__ __forceinline__ void issue_stage0(const GemmParams& p, Stages& s, int64_t m0, int64_t n0) {
+  static_assert(kStages == 2, "one stage ahead");
+  load_operand<KMASK>(window(p.a, m0), p.a, p.K, 0, s.a[0]);
+  load_operand<KMASK>(window(p.b, n0), p.b, p.K, 0, s.b[0]);
+}
+
 template <bool KMASK, bool PREISSUED = false>
 __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int64_t m0,
                                              int64_t n0, f32x16 (&acc)[kMI][kNI]) {
@@ -328,11 +339,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
   }
   const int vrow = wm * 64 + 4 * (lane >> 5);   // + mi * 32 + 8 (q / 4) + q % 4
   f32x16 acc[kMI][kNI];
-  if (nt0 < nt1) issue_first_stages<KMASK>(q, s, nt0 * kBN, m0);
+  if (nt0 < nt1) issue_stage0<KMASK>(q, s, nt0 * kBN, m0);
   for (int64_t nt = nt0; nt < nt1; ++nt) {
     const int64_t n0 = nt * kBN;
     tile_product<KMASK, true>(q, s, n0, m0, acc);
-    if (nt + 1 < nt1) issue_first_stages<KMASK>(q, s, n0 + kBN, m0);
+    if (nt + 1 < nt1) issue_stage0<KMASK>(q, s, n0 + kBN, m0);
     const int64_t w0 = n0 + wm * 64;
     bool hit = false;
 #pragma unroll
@@ -427,114 +438,167 @@ __host__ __device__ inline int64_t tile_slots(int64_t tiles_m, int64_t tiles_n) 
   return (tiles_m + kGM - 1) / kGM * kGM * ((tiles_n + kGN - 1) / kGN * kGN);
 }
 
+__device__ __forceinline__ void tile_of_id(const GemmParams& p, int64_t bid, int64_t& m0,
+                                           int64_t& n0, bool& live) {
+  // 32-bit arithmetic: the host launches at most INT32_MAX blocks
+  const int slots = static_cast<int>(tile_slots(p.tiles_m, p.tiles_n));
+  const int per = (slots + 7) / 8;
+  const int b = static_cast<int>(bid);
+  const int id = (b % 8) * per + b / 8;
+  const int gms = (p.tiles_m + kGM - 1) / kGM;
+  const int g = id / (kGM * kGN), r = id % (kGM * kGN);
+  const int mt = (g % gms) * kGM + r % kGM, nt = (g / gms) * kGN + r / kGM;
+  live = id < slots && mt < p.tiles_m && nt < p.tiles_n;
+  m0 = static_cast<int64_t>(mt) * kBM;
+  n0 = static_cast<int64_t>(nt) * kBN;
+}
+
 __device__ __forceinline__ void tile_of_block(const GemmParams& p, int64_t& m0, int64_t& n0,
                                               bool& live) {
-  const int64_t slots = tile_slots(p.tiles_m, p.tiles_n);
-  const int64_t per = (slots + 7) / 8;
-  const int64_t id = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  const int64_t gms = (p.tiles_m + kGM - 1) / kGM;
-  const int64_t g = id / (kGM * kGN), r = id % (kGM * kGN);
-  const int64_t mt = (g % gms) * kGM + r % kGM, nt = (g / gms) * kGN + r / kGM;
-  live = id < slots && mt < p.tiles_m && nt < p.tiles_n;
-  m0 = mt * kBM;
-  n0 = nt * kBN;
+  tile_of_id(p, blockIdx.x, m0, n0, live);
+}
+
+// Persistent walk over the block ids of the one-tile-per-workgroup order:
+// workgroup b takes ids b, b + gridDim.x, ... (gridDim.x a multiple of 8
+// keeps every id on the XCD it is dealt to, and with 256 workgroups the 32 of
+// an XCD take one group of tiles at a time). Advances id to the next live
+// tile; false when none is left.
+__device__ __forceinline__ bool next_tile(const GemmParams& p, int64_t& id, int64_t& m0,
+                                          int64_t& n0) {
+  const int64_t nblocks = (tile_slots(p.tiles_m, p.tiles_n) + 7) / 8 * 8;
+  for (; id < nblocks; id += gridDim.x) {
+    bool live;
+    tile_of_id(p, id, m0, n0, live);
+    if (live) return true;
+  }
+  return false;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 4 x 4 transpose of bf16 values over the lanes of a quad: lane k holds row k
+// as (p0 = {x0, x1}, p1 = {x2, x3}); afterwards it holds column k, row j's
+// element in position j. Two lane-pair exchanges (DPP quad permutations).
+__device__ __forceinline__ void quad_transpose(uint32_t& p0, uint32_t& p1, int quad) {
+  constexpr int kXor1 = 0xB1, kXor2 = 0x4E;   // quad_perm (1,0,3,2) and (2,3,0,1)
+  const uint32_t r0 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(p0), kXor1, 0xF, 0xF, false));
+  const uint32_t r1 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(p1), kXor1, 0xF, 0xF, false));
+  // even lane: (own low, partner low); odd lane: (partner high, own high)
+  const bool odd = quad & 1;
+  const uint32_t a0 = odd ? ((r0 >> 16) | (p0 & 0xffff0000u)) : ((p0 & 0xffffu) | (r0 << 16));
+  const uint32_t a1 = odd ? ((r1 >> 16) | (p1 & 0xffff0000u)) : ((p1 & 0xffffu) | (r1 << 16));
+  // lanes 0, 1 keep a0 and take a0 of lanes 2, 3; lanes 2, 3 take a1 of lanes 0, 1 and keep a1
+  const bool upper = quad & 2;
+  const uint32_t send = upper ? a0 : a1;
+  const uint32_t recv = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(send), kXor2, 0xF, 0xF, false));
+  p0 = upper ? recv : a0;
+  p1 = upper ? a1 : recv;
 }
 
 // Gradient tiles of one column chunk: G = dL/dz for all rows and the chunk's
-// vocabulary columns, written row-major and transposed.
+// vocabulary columns, written row-major and transposed. Persistent over the
+// tiles (next_tile); the logits are formed transposed, C^T = W_chunk X^T, so a
+// lane holds four rows (m0 + wn * 128 + ni * 32 + lane % 32) and, per row,
+// runs of four adjacent columns (wm * 64 + mi * 32 + 8 g + 4 (lane / 32) +
+// 0..3): each run is one 8-byte store into G, and a 4 x 4 transpose over the
+// quad of lanes holding four adjacent rows turns it into one 8-byte store into
+// G^T. The next tile's first stage is in flight while a tile's gradient is
+// formed and stored.
 template <bool KMASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void lm_grad_kernel(
     GemmParams p) {
+  static_assert(kWaves == 8 && kMI == 2, "gradient layout: 8 waves of 64 x 128");
   __shared__ __align__(16) Stages s;
-  float (*cs)[kCRow] = reinterpret_cast<float (*)[kCRow]>(&s);
-  int64_t m0, n0;
-  bool live_tile;
-  tile_of_block(p, m0, n0, live_tile);
-  if (!live_tile) return;
-  f32x16 acc[kMI][kNI];
-  tile_product<KMASK>(p, s, m0, n0, acc);
-  const int row = threadIdx.x / kTPR, part = threadIdx.x % kTPR;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    band_to_lds(cs, acc, b);
-    __syncthreads();
-    // rows: dL/dz in place in the band, then row-major bf16 stores
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, quad = lane & 3;
+  GemmParams q = p;   // weight rows of the chunk on the matrix-core rows
+  q.a = p.b;
+  q.b = p.a;
+  int64_t id = blockIdx.x, m0, n0;
+  if (!next_tile(p, id, m0, n0)) return;
+  issue_stage0<KMASK>(q, s, n0, m0);
+  const int vrow = wm * 64 + 4 * (lane >> 5);   // + mi * 32 + 8 g + 0..3
+  while (true) {
+    f32x16 acc[kMI][kNI];
+    tile_product<KMASK, true>(q, s, n0, m0, acc);
+    int64_t idn = id + gridDim.x, m0n = 0, n0n = 0;
+    const bool more = next_tile(p, idn, m0n, n0n);
+    if (!more) {
+      m0n = m0;   // the last tile's stage is issued again (unused): an unconditional
+      n0n = n0;   // issue keeps the waits below for the row factors only
+    }
+    // the rows' factors, loaded before the next tile's stage so that waiting
+    // for them leaves its copies in flight
+    float kl[kNI], cnt[kNI], gtv[kNI], fill[kNI];
+    int64_t tl[kNI];
+    bool live[kNI];
     {
-      const int64_t gr = m0 + b * kBand + row;
-      float cnt = 0.f, gtv = 0.f, kl = 0.f, fill = 0.f;
-      int64_t t = -1;
-      bool live = false;
-      if (gr < p.zero_rows) {
-        const float* rs = p.row_state + kRowState * gr;
-        const float kind = rs[5];
-        if (kind == 0.f) {
-          const float zw = p.grad_scale * rs[4];
-          kl = rs[0];
-          cnt = (zw + zw * rs[3]) * fexp2(-rs[6]);   // rs[6]: rounding residue of rs[0]
-          gtv = -zw * rs[1] + zw * rs[3] * rs[2];
-          t = p.targets[gr];
-          live = true;
-        } else {
-          fill = (kind == 1.f) ? 0.f : __builtin_nanf("");
-        }
+      // all loads first (rows past zero_rows read the last row and are not used)
+      f32x4 sa[kNI], sb[kNI];
+      int64_t tg[kNI];
+#pragma unroll
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t gr = m0 + wn * 128 + ni * 32 + (lane & 31);
+        const int64_t grc = gr < p.zero_rows ? gr : p.zero_rows - 1;
+        const f32x4* rs = reinterpret_cast<const f32x4*>(p.row_state + kRowState * grc);
+        sa[ni] = rs[0];
+        sb[ni] = rs[1];
+        tg[ni] = p.targets[grc];
       }
-      const int64_t c0 = n0 + part * kCPT;
-      float* crow = &cs[row][part * kCPT];
-      uint16_t* dst = gr < p.M ? p.g + gr * p.ld_g + c0 : nullptr;
 #pragma unroll
-      for (int j0 = 0; j0 < kCPT; j0 += 8) {
-        float gv[8];
+      for (int ni = 0; ni < kNI; ++ni) {
+        const int64_t gr = m0 + wn * 128 + ni * 32 + (lane & 31);
+        const bool in = gr < p.zero_rows;
+        const float kind = sb[ni][1];   // rs[5]
+        const float zw = p.grad_scale * sb[ni][0];   // rs[4]
+        live[ni] = in && kind == 0.f;
+        kl[ni] = sa[ni][0];
+        cnt[ni] = (zw + zw * sa[ni][3]) * fexp2(-sb[ni][2]);   // rs[6]: rounding residue of rs[0]
+        gtv[ni] = -zw * sa[ni][1] + zw * sa[ni][3] * sa[ni][2];
+        tl[ni] = tg[ni] - p.v0 - (n0 + vrow);   // target's offset from the lane's first column
+        fill[ni] = (!in || kind == 1.f) ? 0.f : __builtin_nanf("");
+      }
+    }
+    issue_stage0<KMASK>(q, s, n0n, m0n);
+    bool hit = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int j = j0 + e;
-          const int64_t col = c0 + j;
-          if (col >= p.N) {
-            gv[e] = 0.f;
-          } else if (!live) {
-            gv[e] = fill;
-          } else if (col + p.v0 == t) {
-            gv[e] = gtv;
-          } else {
-            gv[e] = cnt * fexp2(__builtin_fmaf(crow[j], kL2E, -kl));
+    for (int ni = 0; ni < kNI; ++ni) hit |= live[ni] && tl[ni] >= 0 && tl[ni] < 64;
+    const bool masked = __builtin_amdgcn_ballot_w64(hit) != 0 || n0 + kBN > p.N;
+    const int64_t cend = p.N - (n0 + vrow);   // columns at or past this offset are outside the chunk
+#pragma unroll
+    for (int ni = 0; ni < kNI; ++ni) {
+      const int64_t row = m0 + wn * 128 + ni * 32 + (lane & 31);
+#pragma unroll
+      for (int mi = 0; mi < kMI; ++mi)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          float gv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = mi * 32 + 8 * g4 + e;
+            float x = cnt[ni] * fexp2(__builtin_fmaf(acc[mi][ni][4 * g4 + e], kL2E, -kl[ni]));
+            if (masked) x = (c == tl[ni]) ? gtv[ni] : x;
+            x = live[ni] ? x : fill[ni];
+            if (masked) x = (c < cend) ? x : 0.f;
+            gv[e] = x;
           }
+          // rounded to bf16 in pairs (v_cvt_pk_bf16_f32, RNE)
+          uint32_t p0 = pack_bf16x2(gv[0], gv[1]), p1 = pack_bf16x2(gv[2], gv[3]);
+          const int64_t col = n0 + vrow + mi * 32 + 8 * g4;
+          const u32x2 rowv = {p0, p1};
+          *reinterpret_cast<u32x2*>(p.g + row * p.ld_g + col) = rowv;
+          quad_transpose(p0, p1, quad);
+          const u32x2 colv = {p0, p1};
+          *reinterpret_cast<u32x2*>(p.gt + (col + quad) * p.ld_gt + (row - quad)) = colv;
         }
-        // round to bf16 in pairs (v_cvt_pk_bf16_f32, RNE); the band keeps the
-        // rounded values for the transposed stores
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          w[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
-          crow[j0 + 2 * e] = __uint_as_float(w[e] << 16);
-          crow[j0 + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-        }
-        if (dst) {
-          const u32x4 v = {w[0], w[1], w[2], w[3]};
-          *reinterpret_cast<u32x4*>(dst + j0) = v;
-        }
-      }
     }
-    __syncthreads();
-    // columns: transposed bf16 stores (rows of G^T); kThreads / 256 threads
-    // per column, each a run of band rows
-    {
-      constexpr int kRPT = kBand * 256 / kThreads;   // band rows per thread
-      const int col = threadIdx.x % 256, r0 = (threadIdx.x / 256) * kRPT;
-      uint16_t* dst = p.gt + (n0 + col) * p.ld_gt + m0 + b * kBand + r0;
-#pragma unroll
-      for (int j = r0; j < r0 + kRPT; j += 8) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lo = __float_as_uint(cs[j + 2 * e][col]) >> 16;
-          const uint32_t hi = __float_as_uint(cs[j + 2 * e + 1][col]) >> 16;
-          w[e] = lo | (hi << 16);
-        }
-        const u32x4 v = {w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<u32x4*>(dst + (j - r0)) = v;
-      }
-    }
-    __syncthreads();
+    if (!more) break;
+    id = idn;
+    m0 = m0n;
+    n0 = n0n;
   }
+  // the unused stage has landed before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // Plain product C = A B^T (fp32, optionally accumulated into C).
@@ -679,6 +743,29 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 // slots exit).
 int64_t tile_blocks(int64_t tiles_m, int64_t tiles_n) {
   return (tile_slots(tiles_m, tiles_n) + 7) / 8 * 8;
+}
+
+// Compute units of the current device (cached per device); -1 on error.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Workgroups of a persistent tile walk over `blocks` block ids: one per
+// compute unit (a workgroup's LDS stages fill a CU), a multiple of 8 so that
+// every id stays on the XCD it is dealt to.
+int64_t persistent_blocks(int64_t blocks) {
+  const int cus = device_cus();
+  if (cus <= 0) return -1;
+  return std::min<int64_t>(blocks, std::max(8, cus / 8 * 8));
 }
 
 ce_status launch(void (*kern)(GemmParams), int64_t blocks, const GemmParams& gp, hipStream_t st) {
@@ -855,7 +942,11 @@ ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* 
       gp.gt = gt;
       gp.ld_gt = L.t_pad;
       gp.zero_rows = T;
-      const ce_status s3 = launch_k<GradSel>(tile_blocks(L.tiles_m_all, tiles_c), gp, st);
+      const int64_t nb = tile_blocks(L.tiles_m_all, tiles_c);
+      if (nb > INT32_MAX) return CE_ERR_UNSUPPORTED;   // the tile walk counts block ids in 32 bits
+      const int64_t gb = persistent_blocks(nb);
+      if (gb < 0) return CE_ERR_HIP;
+      const ce_status s3 = launch_k<GradSel>(gb, gp, st);
       if (s3 != CE_OK) return s3;
     }
     if (dhidden) {
