@@ -10,7 +10,10 @@ held to the same bars as the hand-written parity cases (per-row loss,
 segment sums, every gradient element, ignored rows bit-exact). The same
 draws feed the forward-only call, the split form (random shard counts and
 alignments) and the distillation child (a teacher of the same dtype, random
-weight).
+weight). The loss behind the LM head gets draws of its own: row, vocabulary
+and hidden sizes that are ragged against its 256 x 256 x 64 tiles, column
+chunks, ignored and confident rows, a mask, the z-loss weight and the dX
+dtype, on "grid" inputs whose logits are exact in fp32.
 """
 
 from __future__ import annotations
@@ -24,6 +27,7 @@ import torch
 from parity_utils import run_oracle, to_np64
 from test_gpu_distill import compare as compare_distill
 from test_gpu_forward import compare_forward
+from test_gpu_lmhead import grid_inputs, run_and_compare
 from test_gpu_parity import _inp, compare_all
 from test_gpu_split import _split_case
 
@@ -133,3 +137,28 @@ def test_fuzz_distill(seed):
     compare_distill(zs, zt, t, mask=c["mask"], alpha=inp["z_alpha"], beta=beta, gamma=inp["grad_scale"],
                     grad_dtype=c["grad_dtype"], in_place=c["in_place"], what=f"fuzz distill {c['desc']}",
                     pad=c["pad"])
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_fuzz_lmhead(seed):
+    rng = np.random.default_rng(5000 + seed)
+    T = int(rng.integers(1, 600))
+    V = int(rng.integers(1, 2100))
+    H = 8 * int(rng.integers(1, 26))
+    chunk = int(rng.choice([0, 256, 512, 768]))
+    ignore = tuple(int(r) for r in np.flatnonzero(rng.random(T) < 0.15))
+    X, W, t = grid_inputs(T, V, H, seed=seed, ignore=ignore)
+    # confident rows: the target's weight row set to the row's hidden state
+    for r in np.flatnonzero(rng.random(T) < 0.1):
+        if int(t[r]) >= 0:
+            W[int(t[r])] = X[r]
+    mask = None
+    if rng.random() < 0.3:
+        mask = torch.as_tensor(rng.random(T) >= 0.2, device=DEV).to(torch.uint8)
+    z_alpha = float(rng.choice([0.0, 1e-3]))
+    dh_dtype = (torch.float32, torch.bfloat16)[int(rng.integers(2))]
+    desc = (f"seed={seed} T={T} V={V} H={H} chunk={chunk} ignored={len(ignore)} "
+            f"mask={mask is not None} alpha={z_alpha} dX={str(dh_dtype)[6:]}")
+    print(f"[fuzz lmhead] {desc}", flush=True)
+    run_and_compare(X, W, t, mask=mask, z_alpha=z_alpha, grad_scale=1.0 / T, chunk_cols=chunk,
+                    dhidden_dtype=dh_dtype, what=f"fuzz lmhead {desc}")
