@@ -60,11 +60,7 @@ constexpr int kRW = kBM / kWM;                // rows per wave
 constexpr int kMI = kRW / 32;                 // MFMA blocks per wave along M
 constexpr int kNI = 4;                        // ... along N (128 columns)
 constexpr int kLoadsPerStage = 2 * kBM * kCPR / kThreads;   // buffer loads per thread per stage
-constexpr int kTPR = kThreads / 64;           // epilogue threads per band row
-constexpr int kCPT = kBN / kTPR;              // band columns per epilogue thread
 constexpr int kChunks = kBM * kBK / 8;   // 16-byte chunks per operand stage (1024)
-constexpr int kBand = 64;         // epilogue rows per LDS band
-constexpr int kCRow = kBN + 4;    // padded fp32 row of the epilogue band
 constexpr int kRowState = 8;
 constexpr float kL2E = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -74,7 +70,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // a buffer offset past every op
 // sits at r * kCPR + (c ^ ((r / (16 / kCPR)) % kCPR)). A 128-bit LDS read is
 // served 16 lanes (256 bytes, all 64 banks) at a time, and the 16 rows that 16
 // consecutive lanes read then land on 16 distinct 16-byte bank groups.
-// Reused as the fp32 epilogue band.
+// The statistics kernel reuses it for its final merge of the wave rows.
 struct Stages {
   u32x4 a[kStages][kChunks];
   u32x4 b[kStages][kChunks];
@@ -82,7 +78,6 @@ struct Stages {
 __device__ __forceinline__ int swz(int row, int kc) {
   return row * kCPR + (kc ^ ((row / (16 / kCPR)) % kCPR));
 }
-static_assert(sizeof(float) * kBand * kCRow <= sizeof(Stages), "band fits in the stages");
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -263,31 +258,6 @@ __device__ __forceinline__ void tile_product(const GemmParams& p, Stages& s, int
     // stage kt + 1 must have landed: the stages after it may stay in flight
     wait_stages_left(std::min<int64_t>(kStages - 2, std::max<int64_t>(0, nk - 2 - kt)));
     __syncthreads();
-  }
-}
-
-// Rows [64 band, 64 band + 64) of the tile into the fp32 LDS band. Only the
-// waves that own those rows write (blocks mi0, mi0 + 1 of wave row wm).
-__device__ __forceinline__ void band_to_lds(float (*cs)[kCRow], const f32x16 (&acc)[kMI][kNI],
-                                            int band) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  if (wm != band * kBand / kRW) return;
-  const int mi0 = (band * kBand - wm * kRW) / 32;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int mi = 0; mi < kMI; ++mi) {
-      if (mi != mi0 + h) continue;
-#pragma unroll
-      for (int ni = 0; ni < kNI; ++ni)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int row = h * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-          const int col = wn * 128 + ni * 32 + (lane & 31);
-          cs[row][col] = acc[mi][ni][q];
-        }
-    }
   }
 }
 
@@ -571,25 +541,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 #pragma unroll
       for (int mi = 0; mi < kMI; ++mi)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float gv[4];
+        for (int g2 = 0; g2 < 4; g2 += 2) {
+          // two runs of four columns: 8 g4 + 4 (lane / 32) + 0..3, g4 = g2, g2 + 1
+          uint32_t pk[2][2];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = mi * 32 + 8 * g4 + e;
-            float x = cnt[ni] * fexp2(__builtin_fmaf(acc[mi][ni][4 * g4 + e], kL2E, -kl[ni]));
-            if (masked) x = (c == tl[ni]) ? gtv[ni] : x;
-            x = live[ni] ? x : fill[ni];
-            if (masked) x = (c < cend) ? x : 0.f;
-            gv[e] = x;
+          for (int h = 0; h < 2; ++h) {
+            const int g4 = g2 + h;
+            float gv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int c = mi * 32 + 8 * g4 + e;
+              float x = cnt[ni] * fexp2(__builtin_fmaf(acc[mi][ni][4 * g4 + e], kL2E, -kl[ni]));
+              if (masked) x = (c == tl[ni]) ? gtv[ni] : x;
+              x = live[ni] ? x : fill[ni];
+              if (masked) x = (c < cend) ? x : 0.f;
+              gv[e] = x;
+            }
+            // rounded to bf16 in pairs (v_cvt_pk_bf16_f32, RNE)
+            pk[h][0] = pack_bf16x2(gv[0], gv[1]);
+            pk[h][1] = pack_bf16x2(gv[2], gv[3]);
+            uint32_t t0 = pk[h][0], t1 = pk[h][1];
+            quad_transpose(t0, t1, quad);
+            const int64_t col = n0 + vrow + mi * 32 + 8 * g4;
+            const u32x2 colv = {t0, t1};
+            *reinterpret_cast<u32x2*>(p.gt + (col + quad) * p.ld_gt + (row - quad)) = colv;
           }
-          // rounded to bf16 in pairs (v_cvt_pk_bf16_f32, RNE)
-          uint32_t p0 = pack_bf16x2(gv[0], gv[1]), p1 = pack_bf16x2(gv[2], gv[3]);
-          const int64_t col = n0 + vrow + mi * 32 + 8 * g4;
-          const u32x2 rowv = {p0, p1};
-          *reinterpret_cast<u32x2*>(p.g + row * p.ld_g + col) = rowv;
-          quad_transpose(p0, p1, quad);
-          const u32x2 colv = {p0, p1};
-          *reinterpret_cast<u32x2*>(p.gt + (col + quad) * p.ld_gt + (row - quad)) = colv;
+          // G: lane l < 32 takes the upper half's first run (columns 8 g2 + 4..7)
+          // and gives it its second run (8 g2 + 8..11): then lane l stores
+          // columns 8 g2 + 0..7 and lane l + 32 columns 8 g2 + 8..15 of the
+          // same row, 16 bytes each
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+          const int64_t col = n0 + wm * 64 + mi * 32 + 8 * g2 + 8 * (lane >> 5);
+          const u32x4 rowv = {s0[0], s1[0], s0[1], s1[1]};
+          *reinterpret_cast<u32x4*>(p.g + row * p.ld_g + col) = rowv;
         }
     }
     if (!more) break;
