@@ -470,10 +470,11 @@ __device__ __forceinline__ void quad_transpose(uint32_t& p0, uint32_t& p1, int q
 // tiles (next_tile); the logits are formed transposed, C^T = W_chunk X^T, so a
 // lane holds four rows (m0 + wn * 128 + ni * 32 + lane % 32) and, per row,
 // runs of four adjacent columns (wm * 64 + mi * 32 + 8 g + 4 (lane / 32) +
-// 0..3): each run is one 8-byte store into G, and a 4 x 4 transpose over the
-// quad of lanes holding four adjacent rows turns it into one 8-byte store into
-// G^T. The next tile's first stage is in flight while a tile's gradient is
-// formed and stored.
+// 0..3): a 4 x 4 transpose over the quad of lanes holding four adjacent rows
+// turns each run into one 8-byte store into G^T, and lanes l and l + 32 trade
+// runs so that each stores eight adjacent columns of G (16 bytes). The next
+// tile's first stage is in flight while a tile's gradient is formed and
+// stored.
 template <bool KMASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void lm_grad_kernel(
     GemmParams p) {
