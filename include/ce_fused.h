@@ -431,8 +431,10 @@ size_t ce_lmhead_workspace_bytes(const ce_lmhead* p, int32_t backward);
  * Here L = sum_r s_r loss_r over valid rows. A valid row with a target outside
  * [0, V) gives a NaN loss, a NaN dX row and NaN in every dW element (its
  * gradient row enters every column sum). Outputs may not overlap the inputs
- * or the workspace (CE_ERR_ALIAS). Unaligned operands or H % 8 != 0 return
- * CE_ERR_UNSUPPORTED. The call is asynchronous and deterministic.
+ * or the workspace (CE_ERR_ALIAS). Unaligned operands, H % 8 != 0 or a
+ * product of more than 2^31 - 1 256 x 256 tiles return CE_ERR_UNSUPPORTED; a
+ * failed launch or device query returns CE_ERR_HIP. The call is asynchronous
+ * and deterministic.
  */
 ce_status ce_lmhead_fwd_bwd(const ce_lmhead* p, const void* hidden, const void* weight,
                             const int64_t* targets, const uint8_t* mask, float z_alpha,
