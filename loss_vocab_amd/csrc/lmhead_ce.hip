@@ -625,22 +625,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 }
 
 // out[c, r] = in[r, c] for r < R, c < C; out[c, r] = 0 for R <= r < Rp.
-// 64 x 64 tiles through LDS; grid (ceil(Rp/64), ceil(C/64)).
+// 64 x 64 tiles through LDS, moved as runs of eight elements (16 bytes) where
+// the run lies inside the rows; grid (Rp / 64, ceil(C / 64)). Rp, ld_in and
+// ld_out are multiples of 8 and both bases 16-byte aligned.
 __global__ __launch_bounds__(256) void lm_transpose_kernel(const uint16_t* __restrict__ in,
                                                            int64_t R, int64_t C, int64_t ld_in,
                                                            uint16_t* __restrict__ out, int64_t Rp,
                                                            int64_t ld_out) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __align__(16) uint16_t tile[64][72];   // 144-byte rows: every run 16-byte aligned
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64, c0 = static_cast<int64_t>(blockIdx.y) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < R && c < C) ? in[r * ld_in + c] : static_cast<uint16_t>(0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int row = q >> 3, cc = (q & 7) * 8;
+    const int64_t r = r0 + row, c = c0 + cc;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < R && c + 8 <= C) {
+      v = *reinterpret_cast<const u32x4*>(in + r * ld_in + c);
+    } else if (r < R) {
+      uint16_t e[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[k] = c + k < C ? in[r * ld_in + c + k] : static_cast<uint16_t>(0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = static_cast<uint32_t>(e[2 * k]) | (static_cast<uint32_t>(e[2 * k + 1]) << 16);
+    }
+    *reinterpret_cast<u32x4*>(&tile[row][cc]) = v;
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < Rp) out[c * ld_out + r] = tile[tx][i];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = threadIdx.x + 256 * i;
+    const int oc = q >> 3, rr = (q & 7) * 8;
+    const int64_t c = c0 + oc;
+    if (c >= C) continue;
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      v[k] = static_cast<uint32_t>(tile[rr + 2 * k][oc]) | (static_cast<uint32_t>(tile[rr + 2 * k + 1][oc]) << 16);
+    *reinterpret_cast<u32x4*>(out + c * ld_out + r0 + rr) = v;
   }
 }
 
