@@ -270,9 +270,12 @@ __device__ __forceinline__ void merge(float& mL, float& s, float m2, float s2) {
   mL = mn;
 }
 
-// Statistics: grid = tiles_m * n_ranges, range = block % n_ranges (so the
-// workgroups of one XCD walk one range and share its weight tiles); each
-// walks the vocabulary tiles of its range for 256 rows. The products are
+// Statistics: grid = tiles_m * n_ranges; each workgroup walks the vocabulary
+// tiles of one range for 256 rows. Row tiles in groups of 8 go with ranges in
+// fours: the 32 workgroups an XCD runs at once take 8 row tiles by 4 ranges,
+// so each weight slice of a K stage is shared through L2 by 8 of them and
+// each hidden slice by 4 (otherwise range = block % n_ranges, which gives the
+// same sharing for n_ranges a multiple of 32). The products are
 // formed transposed, C^T = W X^T, so that a lane holds few rows (4: row m0 +
 // wn * 128 + ni * 32 + lane % 32) and many vocabulary columns of each (32 per
 // tile: wm * 64 + mi * 32 + 8 (q / 4) + 4 (lane / 32) + q % 4), and keeps the
@@ -281,15 +284,32 @@ __device__ __forceinline__ void merge(float& mL, float& s, float m2, float s2) {
 // first stage is in flight while a tile's statistics are formed. A tile takes
 // the masked path only when a row's target lies among a wave's columns or the
 // tile passes the vocabulary's end.
+// The statistics grid in groups of 8 row tiles by 4 ranges (the 32
+// workgroups an XCD runs at once), a whole number of groups per XCD.
+__host__ __device__ inline bool grouped_ranges(int64_t tiles_m, int64_t n_ranges) {
+  return tiles_m % 8 == 0 && n_ranges % 4 == 0 && (tiles_m / 8) * (n_ranges / 4) % 8 == 0;
+}
+
 template <bool KMASK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void lm_stats_kernel(
     GemmParams p) {
   static_assert(kWaves == 8 && kMI == 2, "statistics layout: 8 waves of 64 x 128");
   __shared__ __align__(16) Stages s;
-  const int range = blockIdx.x % p.n_ranges;
-  const int mt = blockIdx.x / p.n_ranges;
-  const int64_t per = (p.tiles_n + p.n_ranges - 1) / p.n_ranges;
-  const int64_t nt0 = range * per, nt1 = std::min<int64_t>(p.tiles_n, nt0 + per);
+  int range, mt;
+  if (grouped_ranges(p.tiles_m, p.n_ranges)) {
+    // XCD x = block % 8 takes groups x, x + 8, ... of 8 row tiles by 4
+    // ranges, the 32 workgroups of a group together
+    const int x = blockIdx.x % 8, l = blockIdx.x / 8;
+    const int k = (l / 32) * 8 + x, q4 = p.n_ranges / 4;
+    mt = 8 * (k / q4) + l % 8;
+    range = 4 * (k % q4) + (l / 8) % 4;
+  } else {
+    range = blockIdx.x % p.n_ranges;
+    mt = blockIdx.x / p.n_ranges;
+  }
+  // ranges of tiles_n / n_ranges tiles, rounded down or up
+  const int64_t nt0 = range * static_cast<int64_t>(p.tiles_n) / p.n_ranges;
+  const int64_t nt1 = (range + 1) * static_cast<int64_t>(p.tiles_n) / p.n_ranges;
   const int64_t m0 = static_cast<int64_t>(mt) * kBM;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -709,12 +729,26 @@ LmLayout layout(const ce_lmhead* p, bool backward, bool dx32) {
   // an XCD runs at once (block % 8) then cover 32 / (n_ranges / 8) row tiles
   // of n_ranges / 8 ranges, sharing both operands' slices through L2 (with
   // one range per XCD they read 32 row tiles' slices; 32 ranges measured 9%
-  // faster at T = 16384).
+  // faster at T = 16384). Where the row tiles come in groups of 8, fewer and
+  // longer ranges in fours instead, each workgroup one whole range: at
+  // T = 16384, 4 ranges of 125 or 126 tiles, one workgroup per CU, against 32
+  // ranges of 16 tiles with a 5-tile last one (14.5 -> 13.7 ms).
   const int64_t tm = std::max<int64_t>(L.tiles_m_all, 1);
   const int64_t want = (2048 + tm - 1) / tm;
   int64_t nr = 1;
   while (nr < want && nr < L.tiles_n) nr *= 2;
   L.n_ranges = std::min<int64_t>(nr, L.tiles_n);
+  // With row tiles in groups of 8: ranges in fours, as few as give one
+  // workgroup per compute unit (256), each a whole range of balanced length
+  if (tm % 8 == 0) {
+    for (int64_t q4 = 1; 4 * q4 <= L.tiles_n; ++q4) {
+      if (!grouped_ranges(tm, 4 * q4)) continue;
+      if (tm * 4 * q4 >= 256 || 4 * (q4 + 1) > L.tiles_n) {
+        L.n_ranges = 4 * q4;
+        break;
+      }
+    }
+  }
   size_t off = 0;
   L.off_stats = off;
   off += align_up(static_cast<size_t>(L.n_ranges) * p->T * 3 * sizeof(float));

@@ -127,6 +127,16 @@ def test_grid_inputs(T, V, H, chunk):
                     what=f"T{T} V{V} H{H}")
 
 
+@pytest.mark.parametrize("T,V", [(2048, 8448), (4096, 5000)])
+def test_grouped_ranges_every_row(T, V):
+    """Row tiles in groups of 8 take the grouped statistics grid (8 row tiles
+    by 4 ranges per XCD, ranges of balanced length): every row's loss and lse,
+    and dX and dW, against the oracle."""
+    print(f"[lmhead] grouped ranges T={T} V={V}", flush=True)
+    X, W, t = grid_inputs(T, V, 64, seed=T + V, ignore=(0, T // 2))
+    run_and_compare(X, W, t, z_alpha=1e-3, grad_scale=1.0 / T, what=f"grouped T{T} V{V}")
+
+
 def test_strided_operands():
     """hidden and weight as column slices of wider buffers (row strides 80
     and 96 elements, still 16-byte aligned)."""
