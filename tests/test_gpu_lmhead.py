@@ -127,7 +127,7 @@ def test_grid_inputs(T, V, H, chunk):
                     what=f"T{T} V{V} H{H}")
 
 
-@pytest.mark.parametrize("T,V", [(2048, 8448), (4096, 5000)])
+@pytest.mark.parametrize("T,V", [(2048, 8448), (4096, 5000), (1950, 8300)])
 def test_grouped_ranges_every_row(T, V):
     """Row tiles in groups of 8 take the grouped statistics grid (8 row tiles
     by 4 ranges per XCD, ranges of balanced length): every row's loss and lse,
