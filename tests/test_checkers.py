@@ -186,3 +186,27 @@ def test_distill_fp32_grad_scaled_bar():
     g[1, i] += 3e-6 * 0.3 * max(1.0, abs(ref["grad"][1, i]) / 0.3)
     with pytest.raises(AssertionError):
         _run(zs, zt, t, ref, _f32(ref["loss"]), _f32(ref["kl"]), g)
+
+
+def test_entropy_bar():
+    """The entropy bar accepts fp32-sized errors where one non-target column
+    holds nearly all the mass (H small, p_nt ~ 1) and still rejects a 3e-5
+    relative error on a confident row, 1e-4 on an ordinary row and a term
+    lost outright."""
+    from oracle import row_entropy
+    from parity_utils import check_entropy
+    rng = np.random.default_rng(0)
+    z = rng.normal(0, 4, (6, 12))
+    t = np.array([1, 2, 3, 4, 5, 6])
+    z[0, 7] = z[0].max() + 9      # a non-target column dominates
+    z[1, 2] = z[1].max() + 30     # confident row
+    H, lse = row_entropy(z, t)
+    check_entropy(H, H, z, t, lse, "exact")
+    g = H.copy()
+    g[0] += 1e-7                  # the size of the fp32 partials' error
+    check_entropy(g, H, z, t, lse, "non-target-dominated row")
+    for r, f in ((1, 1 + 3e-5), (0, 1.5), (4, 1 + 1e-4)):
+        g = H.copy()
+        g[r] *= f
+        with pytest.raises(AssertionError):
+            check_entropy(g, H, z, t, lse, "planted")

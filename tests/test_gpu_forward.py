@@ -1,7 +1,16 @@
 """Forward-only entry (loss, full logsumexp, softmax entropy) vs the fp64 oracle.
 
-The entropy and the logsumexp are checked to the loss tolerance (relative
-1e-5); ignored rows are +0.0 bit for bit and out-of-range targets NaN. Cases:
+The logsumexp is checked to the loss tolerance (relative 1e-5), and so is the
+entropy, plus an absolute term derived from its fp32 inputs: the non-target
+part of H comes from the pass-1 partials (shift, sum S, sum U of e d), whose
+relative error is at most one 2^-24 rounding per step of a row's accumulation
+chain (fewer than 64 steps at the row lengths here: 2^-18). Carried through
+H_nt = ln2 2^(M - L2) ((L2 - M) S - U), that is at most
+2^-18 p_nt (1 + |lse - max_{j != t} z_j|) absolute; it matters only where
+one non-target column holds nearly all the mass (H small, p_nt ~ 1), and on
+confident rows (H ~ p_nt margin) it is about 2^-18 H, so they keep their
+relative accuracy. Ignored rows are +0.0 bit for bit and out-of-range
+targets NaN. Cases:
 the five workload recipes at oracle-sized shapes, vocabulary sizes across
 every kernel shape and the one-element path (unaligned strides), confident
 rows past the fp32 collapse point (where the entropy is ~1e-8 and must keep
@@ -18,7 +27,7 @@ import pytest
 import torch
 
 from oracle import ce_oracle, row_entropy
-from parity_utils import ROW_ALIGN, check_loss, padded_rows, to_np64
+from parity_utils import ROW_ALIGN, check_entropy, check_loss, padded_rows, to_np64
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -57,7 +66,7 @@ def compare_forward(z, t, *, mask=None, seg=None, S=0, alpha=0.0, what="", pad=F
     H, lse_ref = row_entropy(z64, t_np, mask=m_np)
     check_loss(_np(loss), ref["loss"], what + " loss")
     check_loss(_np(lse), lse_ref, what + " lse")
-    check_loss(_np(ent), H, what + " entropy")
+    check_entropy(_np(ent), H, z64, t_np, lse_ref, what + " entropy")
     inv = torch.as_tensor(~ref["valid"], device=z.device)
     for name, x in (("loss", loss), ("lse", lse), ("entropy", ent)):
         assert _bits_zero(x[inv]), f"{what}: ignored {name} not +0.0"

@@ -57,7 +57,8 @@ def compare_all(inp, *, grad_dtype=None, in_place=False, mask=None, want_grad=Tr
     if want_grad:
         sc = row_scales(logits.shape[0], inp["grad_scale"], _np(inp.get("segment_ids")),
                         inp.get("num_segments", 0), inp.get("segment_mean", False))
-        check_grad(to_np64(grad), ref["grad"], gdt, what + " grad", scale=sc)
+        check_grad(to_np64(grad), ref["grad"], gdt, what + " grad", scale=sc,
+                   targets=_np(inp["targets"]))
     if seg is not None:
         check_loss(_np(seg), ref["seg_nll"], what + " seg")
         empty = ref["seg_nll"] == 0
@@ -153,7 +154,7 @@ def test_row_stride_larger_than_V(dtype, pad):
     torch.cuda.synchronize()
     ref = run_oracle(to_np64(z), _np(t), z_alpha=1e-4, grad_scale=0.5)
     check_loss(_np(loss), ref["loss"])
-    check_grad(to_np64(gout), ref["grad"], torch.float32, scale=0.5)
+    check_grad(to_np64(gout), ref["grad"], torch.float32, scale=0.5, targets=_np(t))
     assert torch.all(gbig[:, V:] == 5.0), "padding columns of the gradient were written"
     # the padding of the logits is never part of the result
     big[:, V:] = float("nan")
@@ -603,7 +604,8 @@ def test_full_size(name):
     # the oracle ran with scale 1; apply each row's scale (exact in fp64 for
     # the power-of-two-free factors up to rounding far below the tolerance)
     g_ref = ref["grad"] * scale[:, None]
-    check_grad(to_np64(grad[ri]), g_ref, wl.grad_torch_dtype, f"{name} sampled grad", scale=scale)
+    check_grad(to_np64(grad[ri]), g_ref, wl.grad_torch_dtype, f"{name} sampled grad", scale=scale,
+               targets=t_all[rows])
     # every ignored row is +0.0, every valid loss finite
     inv = torch.as_tensor(t_all == -100, device=DEV)
     check_zero_rows(loss[inv], grad[inv])
